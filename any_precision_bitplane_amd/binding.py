@@ -1,0 +1,194 @@
+"""ctypes binding of libpagedweight (C ABI in include/pagedweight.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  Functions carry the C names.  Tensor arguments are torch tensors on
+the GPU (their data_ptr() is passed); `stream` is a torch.cuda.Stream, a raw
+hipStream_t integer, or None for torch's current stream.
+
+The library must have been built (python -m any_precision_bitplane_amd.build);
+loading fails loudly otherwise -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_int32, c_size_t, c_uint32, c_void_p
+from typing import Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpagedweight.so")
+
+PW_OK = 0
+PW_ERR_INVALID_ARG = -1
+PW_ERR_UNSUPPORTED_SHAPE = -2
+PW_ERR_BITWIDTH = -3
+PW_ERR_WORKSPACE = -4
+PW_ERR_ALIGNMENT = -5
+PW_ERR_HIP = -6
+PW_ERR_UNSUPPORTED = -7
+
+PW_DEV_BAD_EXPERT_ID = 0x1
+PW_DEV_BAD_BITWIDTH = 0x2
+
+PW_PATH_AUTO = 0
+PW_PATH_GEMV = 1
+PW_PATH_MFMA = 2
+
+PW_STAGE_ROUTE = 0
+PW_STAGE_GATE_UP = 1
+PW_STAGE_DOWN = 2
+PW_STAGE_COMBINE = 3
+PW_NUM_STAGES = 4
+
+
+class PwMoeShape(ctypes.Structure):
+    _fields_ = [("hidden", c_int32), ("inter", c_int32), ("num_experts", c_int32), ("top_k", c_int32)]
+
+
+class PwBlockDesc(ctypes.Structure):
+    _fields_ = [("planes", c_void_p), ("lut_all", c_void_p)]
+
+
+class PwMoeOptions(ctypes.Structure):
+    _fields_ = [("path", c_int32), ("mfma_min_tokens", c_int32),
+                ("stage_events", c_void_p * (PW_NUM_STAGES + 1))]
+
+
+class PwError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {pw_status_str(status)} ({status})")
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libpagedweight.so (once) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m any_precision_bitplane_amd.build`")
+    lib = ctypes.CDLL(path)
+    sig = {
+        "pw_abi_version": (c_int32, []),
+        "pw_status_str": (c_char_p, [c_int32]),
+        "pw_plane_words": (c_size_t, [c_int32, c_int32]),
+        "pw_lut_elems": (c_size_t, [c_int32]),
+        "pw_lut_offset": (c_size_t, [c_int32, c_int32]),
+        "pw_check_shape": (c_int32, [POINTER(PwMoeShape), c_int32]),
+        "pw_workspace_bytes": (c_size_t, [POINTER(PwMoeShape), c_int32]),
+        "pw_workspace_init": (c_int32, [c_void_p, c_size_t, c_void_p]),
+        "pw_moe_forward": (c_int32, [POINTER(PwMoeShape), c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_void_p, c_void_p, c_size_t, POINTER(PwMoeOptions), c_void_p]),
+        "pw_dequant_block": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
+        "pw_get_device_status": (c_int32, [c_void_p, POINTER(c_uint32), c_void_p]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def exported_symbols() -> Sequence[str]:
+    return ["pw_abi_version", "pw_status_str", "pw_plane_words", "pw_lut_elems", "pw_lut_offset",
+            "pw_check_shape", "pw_workspace_bytes", "pw_workspace_init", "pw_moe_forward",
+            "pw_dequant_block", "pw_get_device_status"]
+
+
+# ---------------------------------------------------------------------------
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, what: str):
+    if status != PW_OK:
+        raise PwError(status, what)
+
+
+def shape(H: int, I: int, E: int, k: int) -> PwMoeShape:
+    return PwMoeShape(H, I, E, k)
+
+
+def pw_abi_version() -> int:
+    return load().pw_abi_version()
+
+
+def pw_status_str(status: int) -> str:
+    return load().pw_status_str(status).decode()
+
+
+def pw_plane_words(N: int, K: int) -> int:
+    return load().pw_plane_words(N, K)
+
+
+def pw_lut_elems(N: int) -> int:
+    return load().pw_lut_elems(N)
+
+
+def pw_lut_offset(N: int, b: int) -> int:
+    return load().pw_lut_offset(N, b)
+
+
+def pw_check_shape(shp: PwMoeShape, T: int) -> int:
+    return load().pw_check_shape(ctypes.byref(shp), T)
+
+
+def pw_workspace_bytes(shp: PwMoeShape, T_max: int) -> int:
+    return load().pw_workspace_bytes(ctypes.byref(shp), T_max)
+
+
+def pw_workspace_init(workspace, stream=None) -> None:
+    _check(load().pw_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(stream)), "pw_workspace_init")
+
+
+def make_options(path: int = PW_PATH_AUTO, mfma_min_tokens: int = 0, events=None) -> PwMoeOptions:
+    o = PwMoeOptions()
+    o.path = path
+    o.mfma_min_tokens = mfma_min_tokens
+    if events is not None:
+        for i, ev in enumerate(events):
+            o.stage_events[i] = ev
+    return o
+
+
+def pw_moe_forward(shp: PwMoeShape, T: int, x, ids, w, blocks, q, y, workspace,
+                   opts: Optional[PwMoeOptions] = None, stream=None, check: bool = True) -> int:
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = load().pw_moe_forward(ctypes.byref(shp), T, _ptr(x), _ptr(ids), _ptr(w), _ptr(blocks), _ptr(q),
+                               _ptr(y), _ptr(workspace), ws_bytes,
+                               ctypes.byref(opts) if opts is not None else None, _stream(stream))
+    if check:
+        _check(st, "pw_moe_forward")
+    return st
+
+
+def pw_dequant_block(planes, lut_all, N: int, K: int, q: int, w_out, stream=None, check: bool = True) -> int:
+    st = load().pw_dequant_block(_ptr(planes), _ptr(lut_all), N, K, q, _ptr(w_out), _stream(stream))
+    if check:
+        _check(st, "pw_dequant_block")
+    return st
+
+
+def pw_get_device_status(workspace, stream=None) -> int:
+    flags = c_uint32(0)
+    _check(load().pw_get_device_status(_ptr(workspace), ctypes.byref(flags), _stream(stream)),
+           "pw_get_device_status")
+    return flags.value

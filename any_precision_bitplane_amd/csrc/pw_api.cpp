@@ -1,0 +1,161 @@
+// C-ABI host layer of libpagedweight: argument checks, workspace carving and
+// the launch sequence of the fused mixed-precision MoE layer
+// ("Technical summary: PagedWeight", Core components 3, fused kernel).
+//
+// A forward is at most five launches on the caller's stream and never
+// synchronizes: route, gate_up (GEMV and/or MFMA family), down (same), combine.
+// The committed bitwidths are read on the device, so the launch sequence does
+// not depend on them.
+#include <limits.h>
+#include <string.h>
+
+#include "pw_internal.h"
+
+using namespace pw;
+
+namespace {
+
+constexpr int kDefaultMfmaMinTokens = 32;
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+pw_status check_shape(const pw_moe_shape* s, int32_t T) {
+  if (!s || T < 0) return PW_ERR_INVALID_ARG;
+  if (s->hidden <= 0 || s->inter <= 0 || s->num_experts <= 0 || s->top_k <= 0) return PW_ERR_INVALID_ARG;
+  if (s->hidden % 32 || s->inter % 32) return PW_ERR_UNSUPPORTED_SHAPE;
+  if (s->num_experts > kMaxExperts || s->top_k > s->num_experts) return PW_ERR_UNSUPPORTED_SHAPE;
+  if ((int64_t)T * s->top_k > INT_MAX / 4) return PW_ERR_UNSUPPORTED_SHAPE;
+  return PW_OK;
+}
+
+pw_status hip_status(hipError_t e) { return e == hipSuccess ? PW_OK : PW_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t pw_abi_version(void) { return PW_ABI_VERSION; }
+
+const char* pw_status_str(pw_status s) {
+  switch (s) {
+    case PW_OK: return "ok";
+    case PW_ERR_INVALID_ARG: return "invalid argument";
+    case PW_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case PW_ERR_BITWIDTH: return "bitwidth outside 3..8";
+    case PW_ERR_WORKSPACE: return "workspace too small";
+    case PW_ERR_ALIGNMENT: return "misaligned pointer";
+    case PW_ERR_HIP: return "HIP runtime error";
+    case PW_ERR_UNSUPPORTED: return "unsupported option";
+    default: return "unknown status";
+  }
+}
+
+size_t pw_plane_words(int32_t N, int32_t K) {
+  if (N <= 0 || K <= 0 || K % 32) return 0;
+  return (size_t)8 * (size_t)N * (size_t)(K / 32);
+}
+
+size_t pw_lut_elems(int32_t N) { return N > 0 ? (size_t)504 * (size_t)N : 0; }
+
+size_t pw_lut_offset(int32_t N, int32_t b) {
+  if (N <= 0 || b < kMinBits || b > kMaxBits) return 0;
+  return (size_t)N * (size_t)((1 << b) - 8);
+}
+
+pw_status pw_check_shape(const pw_moe_shape* shape, int32_t T) { return check_shape(shape, T); }
+
+size_t pw_workspace_bytes(const pw_moe_shape* s, int32_t T_max) {
+  if (check_shape(s, T_max) != PW_OK) return 0;
+  return ws_layout(s->hidden, s->inter, s->num_experts, s->top_k, T_max).total;
+}
+
+pw_status pw_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace || workspace_bytes < kAlign) return PW_ERR_INVALID_ARG;
+  if (!aligned(workspace, kAlign)) return PW_ERR_ALIGNMENT;
+  return hip_status(launch_status_clear(reinterpret_cast<uint32_t*>(workspace), (hipStream_t)stream));
+}
+
+pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T, const uint16_t* x, const int32_t* ids,
+                         const float* w, const pw_block_desc* blocks, const uint8_t* q, uint16_t* y,
+                         void* workspace, size_t workspace_bytes, const pw_moe_options* opts, void* stream) {
+  pw_status st = check_shape(shape, T);
+  if (st != PW_OK) return st;
+  if (T == 0) return PW_OK;
+  if (!x || !ids || !w || !blocks || !q || !y || !workspace) return PW_ERR_INVALID_ARG;
+  const int path = opts ? opts->path : PW_PATH_AUTO;
+  if (path != PW_PATH_AUTO && path != PW_PATH_GEMV && path != PW_PATH_MFMA) return PW_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ids, 4) || !aligned(w, 4) || !aligned(blocks, 8) ||
+      !aligned(workspace, kAlign))
+    return PW_ERR_ALIGNMENT;
+
+  const int H = shape->hidden, I = shape->inter, E = shape->num_experts, k = shape->top_k;
+  const WsLayout L = ws_layout(H, I, E, k, T);
+  if (workspace_bytes < L.total) return PW_ERR_WORKSPACE;
+
+  int thresh;
+  if (path == PW_PATH_GEMV) thresh = INT_MAX;
+  else if (path == PW_PATH_MFMA) thresh = 0;
+  else thresh = (opts && opts->mfma_min_tokens > 0) ? opts->mfma_min_tokens : kDefaultMfmaMinTokens;
+  const int max_slots = T * k;               // upper bound of any expert's token count
+  const bool use_gemv = thresh > 1 || thresh == INT_MAX;
+  const bool use_mfma = thresh <= max_slots;
+
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  Route rt;
+  rt.status = reinterpret_cast<uint32_t*>(ws + L.status);
+  rt.num_active = reinterpret_cast<int32_t*>(ws + L.num_active);
+  rt.counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  rt.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  rt.active = reinterpret_cast<int32_t*>(ws + L.active);
+  rt.perm = reinterpret_cast<int32_t*>(ws + L.perm);
+  rt.inv = reinterpret_cast<int32_t*>(ws + L.inv);
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
+  float* o = reinterpret_cast<float*>(ws + L.o);
+
+  ExpertArgs gemv{H, I, E, k, T, blocks, q, rt, 0, thresh == 0 ? 0 : thresh};
+  ExpertArgs mfma{H, I, E, k, T, blocks, q, rt, thresh == 0 ? 1 : thresh, INT_MAX};
+
+  hipStream_t s = (hipStream_t)stream;
+  void* const* ev = (opts && opts->stage_events[0]) ? opts->stage_events : nullptr;
+  auto mark = [&](int i) -> hipError_t {
+    return ev ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess;
+  };
+
+  hipError_t e = mark(PW_STAGE_ROUTE);
+  if (e == hipSuccess) e = launch_route(ids, T, k, E, rt, s);
+  if (e == hipSuccess) e = mark(PW_STAGE_GATE_UP);
+  if (e == hipSuccess && use_gemv) e = launch_gemv_gate_up(gemv, x, h, s);
+  if (e == hipSuccess && use_mfma) e = launch_mfma_gate_up(mfma, x, h, s);
+  if (e == hipSuccess) e = mark(PW_STAGE_DOWN);
+  if (e == hipSuccess && use_gemv) e = launch_gemv_down(gemv, h, o, s);
+  if (e == hipSuccess && use_mfma) e = launch_mfma_down(mfma, h, o, s);
+  if (e == hipSuccess) e = mark(PW_STAGE_COMBINE);
+  if (e == hipSuccess) e = launch_combine(o, w, rt.inv, T, k, H, y, s);
+  if (e == hipSuccess) e = mark(PW_NUM_STAGES);
+  if (e == hipErrorNotSupported) return PW_ERR_UNSUPPORTED;
+  return hip_status(e);
+}
+
+pw_status pw_dequant_block(const uint32_t* planes, const uint16_t* lut_all, int32_t N, int32_t K, int32_t q,
+                           uint16_t* w_out, void* stream) {
+  if (!planes || !lut_all || !w_out || N <= 0 || K <= 0) return PW_ERR_INVALID_ARG;
+  if (K % 32) return PW_ERR_UNSUPPORTED_SHAPE;
+  if (q < kMinBits || q > kMaxBits) return PW_ERR_BITWIDTH;
+  if (!aligned(planes, 4) || !aligned(lut_all, 16) || !aligned(w_out, 16)) return PW_ERR_ALIGNMENT;
+  return hip_status(launch_dequant(planes, lut_all, N, K, q, w_out, (hipStream_t)stream));
+}
+
+pw_status pw_get_device_status(void* workspace, uint32_t* flags, void* stream) {
+  if (!workspace || !flags) return PW_ERR_INVALID_ARG;
+  if (!aligned(workspace, kAlign)) return PW_ERR_ALIGNMENT;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t v = 0;
+  if (hipStreamSynchronize(s) != hipSuccess) return PW_ERR_HIP;
+  if (hipMemcpy(&v, workspace, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return PW_ERR_HIP;
+  if (launch_status_clear(reinterpret_cast<uint32_t*>(workspace), s) != hipSuccess) return PW_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return PW_ERR_HIP;
+  *flags = v;
+  return PW_OK;
+}
+
+}  // extern "C"

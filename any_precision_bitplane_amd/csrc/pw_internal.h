@@ -1,0 +1,81 @@
+// Internal interfaces between the C-ABI host layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/pagedweight.h"
+
+namespace pw {
+
+constexpr int kMaxExperts = 256;
+constexpr int kMinBits = 3;   // committed bitwidths with a table: 3..8
+constexpr int kMaxBits = 8;
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Workspace layout (byte offsets from the workspace base).  The first 256
+// bytes are the header: status word, active-expert count.
+struct WsLayout {
+  size_t status = 0;        // uint32 status bits
+  size_t num_active = 4;    // int32 number of experts with at least one slot
+  size_t counts = 0;        // int32 [E]    slots per expert
+  size_t offsets = 0;       // int32 [E+1]  first sorted position per expert
+  size_t active = 0;        // int32 [E]    active expert ids, ascending
+  size_t perm = 0;          // int32 [T*k]  sorted position -> slot (t*k + j)
+  size_t inv = 0;           // int32 [T*k]  slot -> sorted position, -1 if dropped
+  size_t h = 0;             // fp16  [T*k][I] activations between the products
+  size_t o = 0;             // fp32  [T*k][H] expert outputs before the combine
+  size_t total = 0;
+};
+
+inline WsLayout ws_layout(int H, int I, int E, int k, int T) {
+  WsLayout L;
+  size_t off = kAlign;
+  const size_t slots = (size_t)T * (size_t)k;
+  L.counts = off;  off = align_up(off + sizeof(int32_t) * E, kAlign);
+  L.offsets = off; off = align_up(off + sizeof(int32_t) * (E + 1), kAlign);
+  L.active = off;  off = align_up(off + sizeof(int32_t) * E, kAlign);
+  L.perm = off;    off = align_up(off + sizeof(int32_t) * slots, kAlign);
+  L.inv = off;     off = align_up(off + sizeof(int32_t) * slots, kAlign);
+  L.h = off;       off = align_up(off + sizeof(uint16_t) * slots * I, kAlign);
+  L.o = off;       off = align_up(off + sizeof(float) * slots * H, kAlign);
+  L.total = off;
+  return L;
+}
+
+// Pointers into one workspace for one call.
+struct Route {
+  uint32_t* status;
+  int32_t* num_active;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* active;
+  int32_t* perm;
+  int32_t* inv;
+};
+
+struct ExpertArgs {
+  int H, I, E, k, T;
+  const pw_block_desc* blocks;
+  const uint8_t* q;
+  Route rt;
+  int min_tokens;   // process experts with min_tokens <= n_e < max_tokens
+  int max_tokens;
+};
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_route(const int32_t* ids, int T, int k, int E, const Route& rt, hipStream_t s);
+hipError_t launch_gemv_gate_up(const ExpertArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s);
+hipError_t launch_gemv_down(const ExpertArgs& a, const uint16_t* h, float* o, hipStream_t s);
+hipError_t launch_mfma_gate_up(const ExpertArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s);
+hipError_t launch_mfma_down(const ExpertArgs& a, const uint16_t* h, float* o, hipStream_t s);
+hipError_t launch_combine(const float* o, const float* w, const int32_t* inv, int T, int k, int H,
+                          uint16_t* y, hipStream_t s);
+hipError_t launch_dequant(const uint32_t* planes, const uint16_t* lut_all, int N, int K, int q,
+                          uint16_t* out, hipStream_t s);
+hipError_t launch_status_clear(uint32_t* status, hipStream_t s);
+
+}  // namespace pw

@@ -1,0 +1,122 @@
+// Weighted top-k combine and the block dequantization export.
+#include "pw_device.h"
+#include "pw_internal.h"
+
+namespace pw {
+
+// y[t][n] = fp16( sum_{j < k, ascending} w[t][j] * o[inv[t*k + j]][n] ).
+// The router weights are used as given; a slot the route step dropped (expert
+// id out of range) has inv = -1 and adds nothing.  Fixed j order and no
+// atomics, so the result is deterministic.
+constexpr int kCombineThreads = 256;
+
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ o,
+                                                                  const float* __restrict__ w,
+                                                                  const int32_t* __restrict__ inv, int k,
+                                                                  int H, uint16_t* __restrict__ y) {
+  const int t = blockIdx.y;
+  const int n = (blockIdx.x * kCombineThreads + threadIdx.x) * 4;
+  if (n >= H) return;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int pos = inv[t * k + j];
+    if (pos < 0) continue;
+    const float wj = w[t * k + j];
+    const floatx4 v = *reinterpret_cast<const floatx4*>(o + (size_t)pos * H + n);
+    a0 = __builtin_fmaf(wj, v[0], a0);
+    a1 = __builtin_fmaf(wj, v[1], a1);
+    a2 = __builtin_fmaf(wj, v[2], a2);
+    a3 = __builtin_fmaf(wj, v[3], a3);
+  }
+  const _Float16 h0 = (_Float16)a0, h1 = (_Float16)a1, h2 = (_Float16)a2, h3 = (_Float16)a3;
+  uint2 packed;
+  packed.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+  packed.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+  *reinterpret_cast<uint2*>(y + (size_t)t * H + n) = packed;
+}
+
+hipError_t launch_combine(const float* o, const float* w, const int32_t* inv, int T, int k, int H,
+                          uint16_t* y, hipStream_t s) {
+  const int per_block = kCombineThreads * 4;
+  dim3 grid((H + per_block - 1) / per_block, T);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombineThreads), 0, s, o, w, inv, k, H, y);
+  return hipGetLastError();
+}
+
+// Dequantize one block at bitwidth Q: out[n][c] = table_Q[n][code_Q(n, c)]
+// ("Technical summary: PagedWeight", Core components 1).  Same decode as the
+// GEMV kernels: a wave owns 8 rows, lanes own plane-word columns, the row
+// tables sit in LDS.
+constexpr int kDqThreads = 256;
+constexpr int kDqRowsPerWave = 8;
+
+template <int Q>
+__global__ __launch_bounds__(kDqThreads) void dequant_kernel(const uint32_t* __restrict__ planes,
+                                                            const uint16_t* __restrict__ lut_all, int N, int K,
+                                                            uint16_t* __restrict__ out) {
+  constexpr int TAB = (1 << Q) * 2;
+  constexpr int CH = TAB / 16;
+  __shared__ __align__(16) uint8_t lds[(kDqThreads / kWave) * kDqRowsPerWave * TAB];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int W = K >> 5;
+  const size_t pstride = (size_t)N * W;
+  const uint16_t* lut = lut_all + lut_offset(N, Q);
+  const int row0 = (blockIdx.x * (kDqThreads / kWave) + wave) * kDqRowsPerWave;
+  uint8_t* tabs = lds + wave * kDqRowsPerWave * TAB;
+
+#pragma unroll
+  for (int r = 0; r < kDqRowsPerWave; ++r) {
+    const int row = row0 + r;
+    for (int c = lane; c < CH; c += kWave) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (row < N) v = *reinterpret_cast<const uint4*>(lut + (size_t)row * (1 << Q) + c * 8);
+      *reinterpret_cast<uint4*>(tabs + r * TAB + c * 16) = v;
+    }
+  }
+  __syncthreads();
+
+  for (int s0 = 0; s0 < W; s0 += kWave) {
+    const int wc = s0 + lane;
+    if (wc >= W) continue;
+#pragma unroll
+    for (int r = 0; r < kDqRowsPerWave; ++r) {
+      const int row = row0 + r;
+      if (row >= N) continue;
+      uint32_t P[Q];
+#pragma unroll
+      for (int pp = 0; pp < Q; ++pp) P[pp] = planes[pp * pstride + (size_t)row * W + wc];
+      uint32_t R[8];
+      planes_to_fields<Q>(P, R);
+      const uint8_t* tab = tabs + r * TAB;
+      uint32_t packed[16];
+#pragma unroll
+      for (int j = 0; j < 32; j += 2) {
+        const half2_t w2 = lookup_pair<Q>(R, tab, j);
+        packed[j >> 1] = __builtin_bit_cast(uint32_t, w2);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(out + (size_t)row * K + (size_t)wc * 32);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        dst[v] = make_uint4(packed[4 * v], packed[4 * v + 1], packed[4 * v + 2], packed[4 * v + 3]);
+    }
+  }
+}
+
+hipError_t launch_dequant(const uint32_t* planes, const uint16_t* lut_all, int N, int K, int q, uint16_t* out,
+                          hipStream_t s) {
+  const int rows_per_block = (kDqThreads / kWave) * kDqRowsPerWave;
+  dim3 grid((N + rows_per_block - 1) / rows_per_block);
+  switch (q) {
+    case 3: hipLaunchKernelGGL(dequant_kernel<3>, grid, dim3(kDqThreads), 0, s, planes, lut_all, N, K, out); break;
+    case 4: hipLaunchKernelGGL(dequant_kernel<4>, grid, dim3(kDqThreads), 0, s, planes, lut_all, N, K, out); break;
+    case 5: hipLaunchKernelGGL(dequant_kernel<5>, grid, dim3(kDqThreads), 0, s, planes, lut_all, N, K, out); break;
+    case 6: hipLaunchKernelGGL(dequant_kernel<6>, grid, dim3(kDqThreads), 0, s, planes, lut_all, N, K, out); break;
+    case 7: hipLaunchKernelGGL(dequant_kernel<7>, grid, dim3(kDqThreads), 0, s, planes, lut_all, N, K, out); break;
+    case 8: hipLaunchKernelGGL(dequant_kernel<8>, grid, dim3(kDqThreads), 0, s, planes, lut_all, N, K, out); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pw

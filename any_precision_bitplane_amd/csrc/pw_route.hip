@@ -1,0 +1,126 @@
+// Token -> expert permutation: per-expert slot counts, exclusive offsets, the
+// list of routed ("active") experts and a stable scatter of every (t, j) slot
+// to an expert-sorted position.  The router's ids and weights are inputs of the
+// layer ("Technical summary: PagedWeight", Core components 2 speaks of the
+// routing mass as selection frequency and weight; the layer consumes both).
+//
+// One workgroup of 1024 threads handles any number of slots: counts with LDS
+// integer atomics (order-free, so deterministic), a serial scan over <= 256
+// experts, then the slots in chunks of 1024 in slot order.  Inside a chunk each
+// wave ranks its lanes per expert with ballots, and the per-wave counts are
+// scanned per expert, so a slot's position is
+//   offsets[e] + #{earlier slots routed to e}
+// exactly (a stable counting sort).
+#include "pw_device.h"
+#include "pw_internal.h"
+
+namespace pw {
+
+constexpr int kRouteThreads = 1024;
+constexpr int kRouteWaves = kRouteThreads / kWave;
+
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __restrict__ ids, int T, int k,
+                                                              int E, Route rt) {
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int off[kMaxExperts + 1];
+  __shared__ int base[kMaxExperts];
+  __shared__ int wcnt[kRouteWaves][kMaxExperts];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int S = T * k;
+
+  for (int e = tid; e < E; e += kRouteThreads) {
+    cnt[e] = 0;
+    base[e] = 0;
+  }
+  __syncthreads();
+
+  bool bad = false;
+  for (int s = tid; s < S; s += kRouteThreads) {
+    const int e = ids[s];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    else bad = true;
+  }
+  if (bad) raise_status(rt.status, PW_DEV_BAD_EXPERT_ID);
+  __syncthreads();
+
+  if (tid == 0) {
+    int acc = 0, na = 0;
+    for (int e = 0; e < E; ++e) {
+      off[e] = acc;
+      acc += cnt[e];
+      if (cnt[e] > 0) rt.active[na++] = e;
+    }
+    off[E] = acc;
+    *rt.num_active = na;
+    rt.offsets[E] = acc;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kRouteThreads) {
+    rt.counts[e] = cnt[e];
+    rt.offsets[e] = off[e];
+  }
+
+  for (int c0 = 0; c0 < S; c0 += kRouteThreads) {
+    for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) wcnt[i / E][i % E] = 0;
+    __syncthreads();
+
+    const int s = c0 + tid;
+    int e = -1;
+    if (s < S) {
+      e = ids[s];
+      if (e < 0 || e >= E) e = -1;
+    }
+    int rank = 0;
+    unsigned long long todo = __ballot(e >= 0);
+    while (todo) {
+      const int leader = __ffsll(todo) - 1;
+      const int le = __shfl(e, leader, kWave);
+      const unsigned long long m = __ballot(e == le);
+      if (e == le) {
+        rank = __popcll(m & ((1ull << lane) - 1ull));
+        if (lane == leader) wcnt[wave][le] = __popcll(m);
+      }
+      todo &= ~m;
+    }
+    __syncthreads();
+
+    for (int x = tid; x < E; x += kRouteThreads) {
+      int run = base[x];
+      for (int w = 0; w < kRouteWaves; ++w) {
+        const int c = wcnt[w][x];
+        wcnt[w][x] = run;
+        run += c;
+      }
+      base[x] = run;
+    }
+    __syncthreads();
+
+    if (s < S) {
+      if (e >= 0) {
+        const int pos = off[e] + wcnt[wave][e] + rank;
+        rt.perm[pos] = s;
+        rt.inv[s] = pos;
+      } else {
+        rt.inv[s] = -1;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_route(const int32_t* ids, int T, int k, int E, const Route& rt, hipStream_t s) {
+  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, s, ids, T, k, E, rt);
+  return hipGetLastError();
+}
+
+__global__ void status_clear_kernel(uint32_t* status) { *status = 0u; }
+
+hipError_t launch_status_clear(uint32_t* status, hipStream_t s) {
+  hipLaunchKernelGGL(status_clear_kernel, dim3(1), dim3(1), 0, s, status);
+  return hipGetLastError();
+}
+
+}  // namespace pw

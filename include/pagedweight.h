@@ -1,0 +1,165 @@
+/*
+ * pagedweight.h -- C ABI of libpagedweight, a fused mixed-precision
+ * Mixture-of-Experts expert layer for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  "Technical summary: PagedWeight" (gist.science, paper
+ * 2607.16184), Core components 1 (Paged Weight representation): every expert
+ * linear block -- (layer, expert, gate_up | down) -- is stored as Any-Precision
+ * overlaid bit planes with per-row lookup tables, and a Weight Page Table holds
+ * the committed bitwidth q_i of each block.  Core components 3 (second bullet,
+ * fused mixed-precision kernel): one fused operation reads the planes and the
+ * tables directly and computes each block at its own q_i.  The layer is a routed
+ * SwiGLU FFN:
+ *     gate, up = rows [0, I) and [I, 2I) of  W_gate_up(e) x_t      (W: [2I][H])
+ *     h        = SiLU(gate) * up,  SiLU(z) = z / (1 + exp(-z))
+ *     o        = W_down(e) h                                       (W: [H][I])
+ *     y_t      = sum_{j < k} w[t][j] * o_{ids[t][j]}(x_t)
+ * with W[n][c] = LUT_{q}[n][code_q(n, c)] and code_q the value of the first q
+ * planes (plane 0 = most significant bit).
+ *
+ * Storage format of one block with N rows and K columns (K % 32 == 0):
+ *   planes : uint32 [8][N][K/32], plane-major.  Bit j (LSB = 0) of word
+ *            [p][n][c] is plane p of weight (n, 32c + j).  Only planes 0..q-1
+ *            are read, so a block committed at q needs only that prefix to be
+ *            resident (a shorter allocation is fine).
+ *   lut_all: fp16 bits [504 * N], the per-row tables for b = 3..8 laid one
+ *            after another; the table of bitwidth b starts at element
+ *            N * (2^b - 8) and is [N][2^b].  Only the table of q is read.
+ *
+ * Conventions of every entry point.
+ *   - Pointers are DEVICE pointers unless the comment says host.  The caller
+ *     owns every buffer; the library allocates nothing and keeps no state
+ *     besides read-only kernel objects.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls enqueue work and return; results are ready when the stream reaches
+ *     that point.  Inputs (including the q table) must not change before that:
+ *     a q write ordered on the stream after a forward never affects it, which
+ *     is the "commit only at a safe boundary" rule (Core components 3, first
+ *     bullet).
+ *   - Host-detectable errors return a negative pw_status before anything is
+ *     enqueued.  Device-only errors (expert id outside [0, E), committed
+ *     bitwidth outside 3..8) make the offending slot / block contribute zero and
+ *     set a bit in the workspace status word, read by pw_get_device_status.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef PAGEDWEIGHT_H
+#define PAGEDWEIGHT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PW_ABI_VERSION 1
+
+typedef int32_t pw_status;
+#define PW_OK                     0
+#define PW_ERR_INVALID_ARG       -1  /* null pointer, negative size, bad enum  */
+#define PW_ERR_UNSUPPORTED_SHAPE -2  /* H, I not multiples of 32, E > 256, k > E */
+#define PW_ERR_BITWIDTH          -3  /* host-side bitwidth outside 3..8        */
+#define PW_ERR_WORKSPACE         -4  /* workspace too small                    */
+#define PW_ERR_ALIGNMENT         -5  /* pointer not 16-byte aligned            */
+#define PW_ERR_HIP               -6  /* a HIP runtime call failed              */
+#define PW_ERR_UNSUPPORTED       -7  /* option not available in this build     */
+
+/* device status bits (pw_get_device_status) */
+#define PW_DEV_BAD_EXPERT_ID  0x1u   /* some ids[t][j] outside [0, E)          */
+#define PW_DEV_BAD_BITWIDTH   0x2u   /* some routed block has q outside 3..8   */
+
+/* Layer shape: H = hidden size, I = expert intermediate size, E = number of
+ * routed experts (1..256), k = experts per token (1..E). */
+typedef struct {
+  int32_t hidden;
+  int32_t inter;
+  int32_t num_experts;
+  int32_t top_k;
+} pw_moe_shape;
+
+/* One Weight Page Table entry: where one block's planes and tables live.
+ * The table is device memory [E][2] (index 2e + m, m = 0 gate_up, 1 down),
+ * both pointers 16-byte aligned.  Moving a block means rewriting its entry. */
+typedef struct {
+  const uint32_t* planes;
+  const uint16_t* lut_all;
+} pw_block_desc;
+
+/* Kernel family for the expert products. */
+#define PW_PATH_AUTO 0   /* per expert: MFMA when its token count >= mfma_min_tokens */
+#define PW_PATH_GEMV 1   /* every expert on the bit-plane GEMV kernels            */
+#define PW_PATH_MFMA 2   /* every expert on the dequant-to-LDS MFMA kernels       */
+
+/* Stage boundaries at which optional events are recorded. */
+#define PW_STAGE_ROUTE   0
+#define PW_STAGE_GATE_UP 1
+#define PW_STAGE_DOWN    2
+#define PW_STAGE_COMBINE 3
+#define PW_NUM_STAGES    4
+
+typedef struct {
+  int32_t path;              /* PW_PATH_*                                     */
+  int32_t mfma_min_tokens;   /* AUTO threshold; <= 0 selects the default      */
+  /* Optional hipEvent_t handles (as void*).  If stage_events[0] is non-NULL,
+   * event s is recorded on `stream` right before stage s and event
+   * PW_NUM_STAGES after the last stage, so the caller can time each stage. */
+  void* stage_events[PW_NUM_STAGES + 1];
+} pw_moe_options;
+
+/* ABI version of the loaded library (PW_ABI_VERSION). */
+int32_t pw_abi_version(void);
+
+/* Static, never-NULL text for a status code. */
+const char* pw_status_str(pw_status status);
+
+/* Element counts of one block's storage (see the storage format above). */
+size_t pw_plane_words(int32_t N, int32_t K);   /* 8 * N * K / 32, 0 if invalid */
+size_t pw_lut_elems(int32_t N);                /* 504 * N                      */
+size_t pw_lut_offset(int32_t N, int32_t b);    /* N * (2^b - 8)                */
+
+/* Host-only shape check for a forward of T tokens (no device access). */
+pw_status pw_check_shape(const pw_moe_shape* shape /* host */, int32_t T);
+
+/* Workspace bytes a forward of up to T_max tokens needs (0 on a bad shape). */
+size_t pw_workspace_bytes(const pw_moe_shape* shape /* host */, int32_t T_max);
+
+/* Clear the workspace status word.  Call once on a fresh workspace before its
+ * first forward (the status word is otherwise sticky; see
+ * pw_get_device_status).  Enqueues one small kernel. */
+pw_status pw_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/* The fused mixed-precision MoE layer (Core components 3, fused kernel).
+ *   shape   host; T >= 0 tokens (T == 0 returns PW_OK and enqueues nothing)
+ *   x       fp16 [T][H]                         ids  int32 [T][k]
+ *   w       fp32 [T][k] routing weights, used as given (no renormalisation)
+ *   blocks  device pw_block_desc [E][2]         q    device uint8 [E][2]
+ *   y       fp16 [T][H], overwritten (round to nearest even from fp32)
+ *   workspace, workspace_bytes: device scratch of at least
+ *           pw_workspace_bytes(shape, T) bytes, 256-byte aligned; its first
+ *           bytes hold the status word.  Concurrent calls need distinct
+ *           workspaces.
+ *   opts    host, may be NULL (AUTO path, default threshold, no events).
+ * Accumulation is fp32; h is rounded to fp16 before the down product.
+ * Results are deterministic: the same inputs give the same bits. */
+pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T,
+                         const uint16_t* x, const int32_t* ids, const float* w,
+                         const pw_block_desc* blocks, const uint8_t* q,
+                         uint16_t* y, void* workspace, size_t workspace_bytes,
+                         const pw_moe_options* opts, void* stream);
+
+/* Dequantize one block at bitwidth q (host value, 3..8): w_out fp16 bits
+ * [N][K] = LUT_q[n][code_q(n, c)].  The same device decode the forward uses;
+ * bit-exact by definition (a table copy).  Core components 1. */
+pw_status pw_dequant_block(const uint32_t* planes, const uint16_t* lut_all,
+                           int32_t N, int32_t K, int32_t q,
+                           uint16_t* w_out, void* stream);
+
+/* Wait for `stream`, copy the workspace status word to *flags (host), then
+ * clear it.  Returns PW_ERR_HIP if the copy or the wait fails. */
+pw_status pw_get_device_status(void* workspace, uint32_t* flags /* host */, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDWEIGHT_H */

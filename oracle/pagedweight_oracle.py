@@ -119,17 +119,27 @@ def block_valid(b: int) -> bool:
     return MIN_BITS <= int(b) <= MAX_BITS
 
 
+def _dequant_cached(planes, lut_all, b, cache):
+    if cache is None:
+        return dequant_block(planes, lut_all, b)
+    key = (id(planes), id(lut_all), b)
+    if key not in cache:
+        cache[key] = (planes, lut_all, dequant_block(planes, lut_all, b))
+    return cache[key][2]
+
+
 def moe_forward(x: np.ndarray, ids: np.ndarray, w: np.ndarray,
                 planes: Sequence[Sequence[np.ndarray]], luts: Sequence[Sequence[np.ndarray]],
                 q: np.ndarray, H: int, I: int, E: int,
-                tokens: Sequence[int] | None = None) -> np.ndarray:
+                tokens: Sequence[int] | None = None, cache: dict | None = None) -> np.ndarray:
     """Routed top-k SwiGLU MoE layer with every block at its committed bitwidth.
 
     x fp16 [T][H]; ids int [T][k]; w fp32 [T][k]; planes[e][m], luts[e][m] in
     the input format; q uint8 [E][2].  Returns y fp64 [len(tokens)][H] for the
     requested tokens (all tokens by default).  Experts are visited in ascending
     id; each expert's blocks are dequantized once ([PW] Core components 3: each
-    block at its own bitwidth)."""
+    block at its own bitwidth).  ``cache`` (optional dict) keeps dequantized
+    blocks between calls, keyed by the storage arrays' identity and bitwidth."""
     T, k = ids.shape
     tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     y = np.zeros((len(tok), H), dtype=np.float64)
@@ -138,8 +148,8 @@ def moe_forward(x: np.ndarray, ids: np.ndarray, w: np.ndarray,
         rows, cols = np.nonzero(sel_ids == e)
         if not (block_valid(q[e][0]) and block_valid(q[e][1])):
             continue
-        Wgu = fp16_bits_to_f64(dequant_block(planes[e][0], luts[e][0], int(q[e][0])))
-        Wd = fp16_bits_to_f64(dequant_block(planes[e][1], luts[e][1], int(q[e][1])))
+        Wgu = fp16_bits_to_f64(_dequant_cached(planes[e][0], luts[e][0], int(q[e][0]), cache))
+        Wd = fp16_bits_to_f64(_dequant_cached(planes[e][1], luts[e][1], int(q[e][1]), cache))
         xe = x[tok[rows]].astype(np.float64)
         o = expert_ffn(xe, Wgu, Wd, I)
         for r, (ti, j) in enumerate(zip(rows, cols)):
@@ -147,7 +157,8 @@ def moe_forward(x: np.ndarray, ids: np.ndarray, w: np.ndarray,
     return y
 
 
-def moe_forward_layer(layer, tokens=None) -> np.ndarray:
+def moe_forward_layer(layer, tokens=None, cache=None, q=None, ids=None, w=None) -> np.ndarray:
     wl = layer.wl
-    return moe_forward(layer.x, layer.ids, layer.w, layer.planes, layer.luts, layer.q,
-                       wl.H, wl.I, wl.E, tokens=tokens)
+    return moe_forward(layer.x, layer.ids if ids is None else ids, layer.w if w is None else w,
+                       layer.planes, layer.luts, layer.q if q is None else q,
+                       wl.H, wl.I, wl.E, tokens=tokens, cache=cache)

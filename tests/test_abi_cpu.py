@@ -1,0 +1,115 @@
+"""The C-ABI library loads, exports every function its header declares, and its
+host-side checks reject bad arguments before touching a device.  No GPU needed:
+none of these calls reaches a kernel launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from any_precision_bitplane_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedweight.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pw_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libpagedweight.so is not built (python -m any_precision_bitplane_amd.build)")
+    return B.load()
+
+
+def test_every_declared_function_is_exported(lib):
+    declared = header_functions()
+    assert len(declared) >= 10
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(pw_\w+)", out))
+    for name in declared:
+        assert name in exported, name
+        assert hasattr(lib, name)
+    assert sorted(B.exported_symbols()) == declared
+
+
+def test_version_and_status_strings(lib):
+    assert B.pw_abi_version() == 1
+    for s in (B.PW_OK, B.PW_ERR_INVALID_ARG, B.PW_ERR_UNSUPPORTED_SHAPE, B.PW_ERR_BITWIDTH,
+              B.PW_ERR_WORKSPACE, B.PW_ERR_ALIGNMENT, B.PW_ERR_HIP, B.PW_ERR_UNSUPPORTED, 12345):
+        assert isinstance(B.pw_status_str(s), str) and B.pw_status_str(s)
+
+
+def test_storage_sizes(lib):
+    assert B.pw_plane_words(2816, 2048) == 8 * 2816 * 64
+    assert B.pw_plane_words(10, 33) == 0
+    assert B.pw_lut_elems(2048) == 504 * 2048
+    for b in range(3, 9):
+        assert B.pw_lut_offset(2048, b) == 2048 * (2 ** b - 8)
+    assert B.pw_lut_offset(2048, 2) == 0 and B.pw_lut_offset(2048, 9) == 0
+
+
+def test_shape_checks(lib):
+    ok = B.shape(2048, 1408, 60, 4)
+    assert B.pw_check_shape(ok, 4) == B.PW_OK
+    assert B.pw_check_shape(ok, 0) == B.PW_OK
+    assert B.pw_check_shape(ok, -1) == B.PW_ERR_INVALID_ARG
+    assert B.pw_check_shape(B.shape(2040, 1408, 60, 4), 4) == B.PW_ERR_UNSUPPORTED_SHAPE
+    assert B.pw_check_shape(B.shape(2048, 1400, 60, 4), 4) == B.PW_ERR_UNSUPPORTED_SHAPE
+    assert B.pw_check_shape(B.shape(2048, 1408, 4, 5), 4) == B.PW_ERR_UNSUPPORTED_SHAPE
+    assert B.pw_check_shape(B.shape(2048, 1408, 257, 4), 4) == B.PW_ERR_UNSUPPORTED_SHAPE
+    assert B.pw_check_shape(B.shape(0, 1408, 60, 4), 4) == B.PW_ERR_INVALID_ARG
+    assert B.pw_workspace_bytes(B.shape(2040, 1408, 60, 4), 4) == 0
+
+
+def test_workspace_size_grows_with_tokens(lib):
+    shp = B.shape(2048, 1408, 60, 4)
+    a, b = B.pw_workspace_bytes(shp, 4), B.pw_workspace_bytes(shp, 256)
+    assert 0 < a < b
+    # h (fp16, I wide) and o (fp32, H wide) per routed slot dominate
+    assert b >= 256 * 4 * (1408 * 2 + 2048 * 4)
+    assert a % 256 == 0 and b % 256 == 0
+
+
+def _fwd(lib, shp, T, x=1 << 20, ids=1 << 20, w=1 << 20, blocks=1 << 20, q=1 << 20, y=1 << 20,
+         ws=1 << 20, ws_bytes=1 << 40, opts=None):
+    return lib.pw_moe_forward(ctypes.byref(shp), T, x, ids, w, blocks, q, y, ws, ws_bytes,
+                              ctypes.byref(opts) if opts else None, None)
+
+
+def test_forward_rejects_bad_arguments_before_launch(lib):
+    shp = B.shape(256, 512, 8, 2)
+    assert _fwd(lib, shp, 0) == B.PW_OK                        # T = 0: nothing enqueued
+    assert _fwd(lib, shp, 4, x=None) == B.PW_ERR_INVALID_ARG
+    assert _fwd(lib, shp, 4, ids=None) == B.PW_ERR_INVALID_ARG
+    assert _fwd(lib, shp, 4, ws=None) == B.PW_ERR_INVALID_ARG
+    assert _fwd(lib, shp, 4, x=(1 << 20) + 2) == B.PW_ERR_ALIGNMENT
+    assert _fwd(lib, shp, 4, ws=(1 << 20) + 64) == B.PW_ERR_ALIGNMENT
+    assert _fwd(lib, shp, 4, ws_bytes=100) == B.PW_ERR_WORKSPACE
+    assert _fwd(lib, shp, 4, opts=B.make_options(path=7)) == B.PW_ERR_INVALID_ARG
+    assert _fwd(lib, B.shape(250, 512, 8, 2), 4) == B.PW_ERR_UNSUPPORTED_SHAPE
+    assert _fwd(lib, shp, -3) == B.PW_ERR_INVALID_ARG
+
+
+def test_dequant_rejects_bad_arguments_before_launch(lib):
+    f = lib.pw_dequant_block
+    p = 1 << 20
+    assert f(None, p, 8, 32, 4, p, None) == B.PW_ERR_INVALID_ARG
+    assert f(p, p, 8, 30, 4, p, None) == B.PW_ERR_UNSUPPORTED_SHAPE
+    assert f(p, p, 8, 32, 2, p, None) == B.PW_ERR_BITWIDTH
+    assert f(p, p, 8, 32, 9, p, None) == B.PW_ERR_BITWIDTH
+    assert f(p, p + 2, 8, 32, 4, p, None) == B.PW_ERR_ALIGNMENT
+    assert f(p, p, 0, 32, 4, p, None) == B.PW_ERR_INVALID_ARG
+
+
+def test_status_and_init_reject_bad_arguments(lib):
+    flags = ctypes.c_uint32(0)
+    assert lib.pw_get_device_status(None, ctypes.byref(flags), None) == B.PW_ERR_INVALID_ARG
+    assert lib.pw_get_device_status(1 << 20, None, None) == B.PW_ERR_INVALID_ARG
+    assert lib.pw_workspace_init(None, 1024, None) == B.PW_ERR_INVALID_ARG
+    assert lib.pw_workspace_init((1 << 20) + 16, 1024, None) == B.PW_ERR_ALIGNMENT

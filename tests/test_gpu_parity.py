@@ -1,0 +1,277 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Bars: dequantized weights bit-exact; layer output within relative L2 error
+1e-3 and max abs error 2e-2 of the oracle (fp32 accumulation, fp16 h and y).
+Every case prints what it runs before it launches anything.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle.pagedweight_oracle as orc
+from any_precision_bitplane_amd import binding as B
+from any_precision_bitplane_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 1e-3
+MAX_ABS = 2e-2
+
+_ORACLE_CACHE = {}
+_LAYERS = {}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as _t
+    if not _t.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    B.load()
+    return _t
+
+
+def layer_for(name, T=None, routed_only=True):
+    wl = synth.WORKLOADS[name] if T is None else synth.WORKLOADS[name].with_T(T)
+    key = (wl.name, routed_only)
+    if key not in _LAYERS:
+        _LAYERS[key] = synth.make_routed_layer(wl) if routed_only else synth.make_layer(wl)
+    return _LAYERS[key]
+
+
+def custom_layer(H, I, E, k, T, seed, qvals=None):
+    wl = synth.Workload(f"custom{H}x{I}x{E}x{k}x{T}", H=H, I=I, E=E, k=k, T=T, seed=seed)
+    L = synth.make_layer(wl)
+    if qvals is not None:
+        L.q[:] = np.asarray(qvals, np.uint8)
+    return L
+
+
+def oracle_y(L, tokens=None, q=None, ids=None, w=None):
+    return orc.moe_forward_layer(L, tokens=tokens, cache=_ORACLE_CACHE, q=q, ids=ids, w=w)
+
+
+def compare(got, ref, what):
+    got = np.asarray(got, dtype=np.float64)
+    err = got - ref
+    rel = np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-30)
+    mx = float(np.max(np.abs(err))) if err.size else 0.0
+    say(f"  {what}: rel_l2={rel:.3e} max_abs={mx:.3e}")
+    assert np.all(np.isfinite(got)), what
+    assert rel <= REL_L2, (what, rel)
+    assert mx <= MAX_ABS, (what, mx)
+
+
+def run_forward(torch, L, path=B.PW_PATH_AUTO, mfma_min_tokens=0, dev=None):
+    from any_precision_bitplane_amd.device import DeviceLayer
+    dev = dev or DeviceLayer(L)
+    dev.forward(B.make_options(path=path, mfma_min_tokens=mfma_min_tokens))
+    torch.cuda.synchronize()
+    return dev, dev.y.float().cpu().numpy()
+
+
+# ---------------------------------------------------------------------------
+# dequantization: bit-exact
+# ---------------------------------------------------------------------------
+def _dequant_check(torch, planes, lut, q, what):
+    N, K = planes.shape[1], planes.shape[2] * 32
+    say(f"dequant {what} N={N} K={K} q={q}")
+    p = torch.from_numpy(planes.view(np.int32)).cuda()
+    l = torch.from_numpy(lut.view(np.int16)).cuda()
+    out = torch.empty((N, K), dtype=torch.int16, device="cuda")
+    B.pw_dequant_block(p, l, N, K, q, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    ref = orc.dequant_block(planes, lut, q)
+    assert np.array_equal(got, ref), f"{what} q={q}: {np.count_nonzero(got != ref)} mismatches"
+
+
+def test_dequant_bit_exact_tiny_all_blocks(torch):
+    L = layer_for("tiny", routed_only=False)
+    for e in range(L.wl.E):
+        for m in (0, 1):
+            for q in range(3, 9):
+                _dequant_check(torch, L.planes[e][m], L.luts[e][m], q, f"tiny e{e} m{m}")
+
+
+def test_dequant_bit_exact_qwen_blocks(torch):
+    wl = synth.WORKLOADS["qwen_decode"]
+    for e in (0, 37):
+        for m in (0, 1):
+            N, K = wl.block_shape(m)
+            planes = synth.draw_planes(wl.seed, e, m, N, K)
+            lut = synth.draw_lut(wl.seed, e, m, N)
+            for q in range(3, 9):
+                _dequant_check(torch, planes, lut, q, f"qwen e{e} m{m}")
+
+
+def test_dequant_ragged_shapes(torch):
+    rng = np.random.default_rng(11)
+    for N, K in [(1, 32), (7, 96), (13, 2080), (33, 4128)]:
+        planes = rng.integers(0, 2 ** 32, (8, N, K // 32), dtype=np.uint32)
+        lut = synth.draw_lut(5, 0, 0, N)
+        for q in (3, 5, 8):
+            _dequant_check(torch, planes, lut, q, f"ragged")
+
+
+# ---------------------------------------------------------------------------
+# layer forward vs oracle
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("path", [B.PW_PATH_GEMV, B.PW_PATH_AUTO])
+def test_forward_tiny(torch, path):
+    L = layer_for("tiny")
+    say(f"forward tiny path={path}")
+    _, y = run_forward(torch, L, path)
+    compare(y, oracle_y(L), f"tiny path={path}")
+
+
+def test_forward_qwen_decode(torch):
+    L = layer_for("qwen_decode")
+    say("forward qwen_decode T=4")
+    _, y = run_forward(torch, L)
+    compare(y, oracle_y(L), "qwen_decode")
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_forward_mixtral_decode(torch, T):
+    L = layer_for("mixtral_decode", T=T)
+    say(f"forward mixtral_decode T={T}")
+    _, y = run_forward(torch, L, B.PW_PATH_GEMV)
+    compare(y, oracle_y(L), f"mixtral_decode T={T}")
+
+
+def test_forward_ragged_shapes(torch):
+    # gate_up K = 2080 (65 plane words: two slices, one-word tail); down K = 96
+    for (H, I, E, k, T, seed) in [(2080, 96, 5, 3, 7, 31), (32, 32, 3, 2, 5, 32), (96, 1056, 4, 4, 3, 33)]:
+        L = custom_layer(H, I, E, k, T, seed)
+        say(f"forward ragged H={H} I={I} E={E} k={k} T={T}")
+        _, y = run_forward(torch, L, B.PW_PATH_GEMV)
+        compare(y, oracle_y(L), f"ragged H={H} I={I}")
+
+
+def test_forward_many_tokens_per_expert_gemv(torch):
+    # experts with 3..40 tokens take several token groups on the GEMV path
+    L = custom_layer(256, 512, 4, 2, 40, 34)
+    say("forward gemv many tokens per expert")
+    _, y = run_forward(torch, L, B.PW_PATH_GEMV)
+    compare(y, oracle_y(L), "gemv many tokens")
+
+
+def test_forward_zero_tokens_is_noop(torch):
+    from any_precision_bitplane_amd.device import DeviceLayer
+    L = layer_for("tiny")
+    dev = DeviceLayer(L)
+    dev.y.fill_(7.0)
+    say("forward T=0")
+    st = B.pw_moe_forward(dev.shape, 0, dev.x, dev.ids, dev.w, dev.blocks[0], dev.q, dev.y, dev.ws)
+    torch.cuda.synchronize()
+    assert st == B.PW_OK
+    assert bool((dev.y == 7.0).all())
+
+
+# ---------------------------------------------------------------------------
+# invariants
+# ---------------------------------------------------------------------------
+def test_deterministic_and_relocation_invariant(torch):
+    """Same inputs give the same bits; moving the blocks to other addresses and
+    rewriting the page table gives the same bits too."""
+    from any_precision_bitplane_amd.device import DeviceLayer
+    L = layer_for("qwen_decode")
+    say("determinism + relocation qwen_decode")
+    dev = DeviceLayer(L, copies=2, experts=[int(e) for e in L.active_experts()])
+    dev.forward()
+    y0 = dev.y.clone()
+    dev.forward()
+    y1 = dev.y.clone()
+    dev.forward(copy=1)
+    y2 = dev.y.clone()
+    torch.cuda.synchronize()
+    assert dev.planes[1][int(L.active_experts()[0])][0].data_ptr() != dev.planes[0][int(L.active_experts()[0])][0].data_ptr()
+    assert torch.equal(y0, y1) and torch.equal(y0, y2)
+
+
+def test_commit_is_ordered_on_the_stream(torch):
+    """A q write enqueued after a forward does not affect it; the next forward
+    sees it (the page table is read on the device)."""
+    from any_precision_bitplane_amd.device import DeviceLayer
+    L = layer_for("qwen_decode")
+    say("stream-ordered commit qwen_decode")
+    dev = DeviceLayer(L)
+    q_new = L.q.copy()
+    q_new[:, :] = 3
+    out_a = torch.empty_like(dev.y)
+    out_b = torch.empty_like(dev.y)
+    dev.forward(y=out_a)
+    dev.set_q(q_new)
+    dev.forward(y=out_b)
+    torch.cuda.synchronize()
+    compare(out_a.float().cpu().numpy(), oracle_y(L), "before commit")
+    compare(out_b.float().cpu().numpy(), oracle_y(L, q=q_new), "after commit")
+    ref = DeviceLayer(L)
+    ref.forward()
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, ref.y)
+
+
+def test_block_bitwidth_only_affects_its_tokens(torch):
+    """Each block is computed at its own q: changing the q of experts a token
+    does not route to leaves that token's output bit-identical."""
+    from any_precision_bitplane_amd.device import DeviceLayer
+    L = layer_for("qwen_decode")
+    say("per-block bitwidth independence qwen_decode")
+    dev = DeviceLayer(L)
+    dev.forward()
+    base = dev.y.clone()
+    mine = set(int(e) for e in L.ids[0])
+    q2 = L.q.copy()
+    for e in range(L.wl.E):
+        if e not in mine:
+            q2[e] = 3 + (q2[e] - 3 + 2) % 6
+    dev.set_q(q2)
+    dev.forward()
+    torch.cuda.synchronize()
+    assert torch.equal(base[0], dev.y[0])
+
+
+def test_invalid_ids_and_bitwidths_flagged_and_zero(torch):
+    from any_precision_bitplane_amd.device import DeviceLayer
+    L = layer_for("tiny")
+    say("invalid ids / bitwidths")
+    ids = L.ids.copy()
+    ids[0, 1] = L.wl.E
+    ids[3, 0] = -5
+    dev = DeviceLayer(L)
+    dev.ids.copy_(torch.from_numpy(ids))
+    dev.forward()
+    torch.cuda.synchronize()
+    assert dev.status() & B.PW_DEV_BAD_EXPERT_ID
+    assert dev.status() == 0            # reading clears it
+    compare(dev.y.float().cpu().numpy(), oracle_y(L, ids=ids), "dropped slots")
+
+    q = L.q.copy()
+    bad_e = int(L.ids[5, 0])
+    q[bad_e, 1] = 11
+    dev2 = DeviceLayer(L)
+    dev2.set_q(q)
+    dev2.forward()
+    torch.cuda.synchronize()
+    assert dev2.status() & B.PW_DEV_BAD_BITWIDTH
+    compare(dev2.y.float().cpu().numpy(), oracle_y(L, q=q), "invalid bitwidth block")
+
+
+def test_duplicate_ids_are_summed(torch):
+    from any_precision_bitplane_amd.device import DeviceLayer
+    L = layer_for("tiny")
+    ids = L.ids.copy()
+    ids[:, 1] = ids[:, 0]
+    say("duplicate ids")
+    dev = DeviceLayer(L)
+    dev.ids.copy_(torch.from_numpy(ids))
+    dev.forward()
+    torch.cuda.synchronize()
+    compare(dev.y.float().cpu().numpy(), oracle_y(L, ids=ids), "duplicate ids")
