@@ -15,7 +15,7 @@ using namespace pw;
 
 namespace {
 
-constexpr int kDefaultMfmaMinTokens = 32;
+constexpr int kDefaultMfmaMinTokens = INT_MAX;   // MFMA family not built yet
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
