@@ -72,7 +72,7 @@ size_t pw_workspace_bytes(const pw_moe_shape* s, int32_t T_max) {
 pw_status pw_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
   if (!workspace || workspace_bytes < kAlign) return PW_ERR_INVALID_ARG;
   if (!aligned(workspace, kAlign)) return PW_ERR_ALIGNMENT;
-  return hip_status(launch_status_clear(reinterpret_cast<uint32_t*>(workspace), (hipStream_t)stream));
+  return hip_status(launch_fill_zero(workspace, workspace_bytes, (hipStream_t)stream));
 }
 
 pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T, const uint16_t* x, const int32_t* ids,
@@ -97,7 +97,7 @@ pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T, const uint16_t* x
   else if (path == PW_PATH_MFMA) thresh = 0;
   else thresh = (opts && opts->mfma_min_tokens > 0) ? opts->mfma_min_tokens : kDefaultMfmaMinTokens;
   const int max_slots = T * k;               // upper bound of any expert's token count
-  const bool use_gemv = thresh > 1 || thresh == INT_MAX;
+  const bool use_gemv = thresh > 0;
   const bool use_mfma = thresh <= max_slots;
 
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
@@ -112,8 +112,17 @@ pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T, const uint16_t* x
   uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
   float* o = reinterpret_cast<float*>(ws + L.o);
 
-  ExpertArgs gemv{H, I, E, k, T, blocks, q, rt, 0, thresh == 0 ? 0 : thresh};
+  const bool small = max_slots <= 64;
+  const bool inline_route = small && !use_mfma;
   ExpertArgs mfma{H, I, E, k, T, blocks, q, rt, thresh == 0 ? 1 : thresh, INT_MAX};
+  GemvLaunch g{};
+  g.H = H; g.I = I; g.E = E; g.k = k; g.T = T;
+  g.blocks = blocks; g.q = q; g.ids = ids; g.rt = rt;
+  g.inline_route = inline_route ? 1 : 0;
+  g.min_tokens = 0;
+  g.max_tokens = thresh == 0 ? 0 : thresh;
+  g.x = x; g.h = h; g.o = o;
+  g.kparts = down_kparts(H, I, E, k, T);
 
   hipStream_t s = (hipStream_t)stream;
   void* const* ev = (opts && opts->stage_events[0]) ? opts->stage_events : nullptr;
@@ -122,15 +131,15 @@ pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T, const uint16_t* x
   };
 
   hipError_t e = mark(PW_STAGE_ROUTE);
-  if (e == hipSuccess) e = launch_route(ids, T, k, E, rt, s);
+  if (e == hipSuccess && !inline_route) e = launch_route(ids, T, k, E, rt, s);
   if (e == hipSuccess) e = mark(PW_STAGE_GATE_UP);
-  if (e == hipSuccess && use_gemv) e = launch_gemv_gate_up(gemv, x, h, s);
+  if (e == hipSuccess && use_gemv) e = launch_gemv_gate_up(g, s);
   if (e == hipSuccess && use_mfma) e = launch_mfma_gate_up(mfma, x, h, s);
   if (e == hipSuccess) e = mark(PW_STAGE_DOWN);
-  if (e == hipSuccess && use_gemv) e = launch_gemv_down(gemv, h, o, s);
+  if (e == hipSuccess && use_gemv) e = launch_gemv_down(g, s);
   if (e == hipSuccess && use_mfma) e = launch_mfma_down(mfma, h, o, s);
   if (e == hipSuccess) e = mark(PW_STAGE_COMBINE);
-  if (e == hipSuccess) e = launch_combine(o, w, rt.inv, T, k, H, y, s);
+  if (e == hipSuccess) e = launch_combine(o, w, rt.inv, T, k, H, g.kparts, y, s);
   if (e == hipSuccess) e = mark(PW_NUM_STAGES);
   if (e == hipErrorNotSupported) return PW_ERR_UNSUPPORTED;
   return hip_status(e);

@@ -25,23 +25,61 @@ __host__ __device__ constexpr int lut_offset(int N, int b) { return N * ((1 << b
 // Bit-plane -> code fields.
 //
 // The q plane words of one row hold 32 weights.  We transpose the q x 32 bit
-// matrix inside each byte lane with three block-swap levels (4, 2, 1), the
-// classic recursive 8x8 bit transpose run on four byte lanes at once.  Input
-// register R[r] supplies field bit r; after the transpose, byte b of R[c] is
-// the field of weight 8b + c.
+// matrix inside each byte lane with three block-swap levels (the recursive 8x8
+// bit transpose, run on four byte lanes at once; the levels commute, so each
+// bitwidth uses the order that needs the fewest instructions given which input
+// registers are zero).  Input register R[r] supplies field bit r; after the
+// transpose, byte b of R[c] is the field of weight 8b + c.
 //
 // For q <= 7 plane p goes to field bit q - p, so the field is 2*code: the byte
 // offset of the entry in an fp16 table.  For q = 8 the field is the code itself
-// (2*code needs 9 bits) and the caller doubles it.
+// (2*code needs 9 bits) and the address step doubles it.
 // ---------------------------------------------------------------------------
+
+// v_bfi_b32: (a & m) | (b & ~m).  Written out because the compiler tends to
+// expand it into and/and/or.
+__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) {
+  uint32_t d;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(d) : "s"(m), "v"(a), "v"(b));
+  return d;
+}
+
 template <int S>
-__device__ __forceinline__ void swap_level(uint32_t (&R)[8], uint32_t hi) {
+__device__ __forceinline__ constexpr uint32_t level_mask() {
+  return S == 4 ? 0xF0F0F0F0u : S == 2 ? 0xCCCCCCCCu : 0xAAAAAAAAu;
+}
+
+// One swap level on rows r and r+S (r & S == 0), with compile-time knowledge of
+// which rows are still all-zero (bit r of Z).  Returns the new zero set.
+template <int S, unsigned Z>
+__device__ __forceinline__ constexpr unsigned level_zero_after() {
+  unsigned z = Z;
+  for (int r = 0; r < 8; ++r)
+    if ((r & S) == 0) {
+      const bool both = ((Z >> r) & 1u) && ((Z >> (r + S)) & 1u);
+      z = both ? (z | (1u << r) | (1u << (r + S))) : (z & ~(1u << r) & ~(1u << (r + S)));
+    }
+  return z;
+}
+
+template <int S, unsigned Z>
+__device__ __forceinline__ void swap_level(uint32_t (&R)[8]) {
+  constexpr uint32_t H = level_mask<S>();
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
-    if ((r & S) == 0) {
-      const uint32_t a = R[r], b = R[r + S];
-      R[r] = (a & ~hi) | ((b << S) & hi);
-      R[r + S] = (b & hi) | ((a >> S) & ~hi);
+    if ((r & S) != 0) continue;
+    const bool za = (Z >> r) & 1u, zb = (Z >> (r + S)) & 1u;
+    const uint32_t a = R[r], b = R[r + S];
+    if (za && zb) continue;
+    if (za) {
+      R[r] = (b << S) & H;
+      R[r + S] = b & H;
+    } else if (zb) {
+      R[r] = a & ~H;
+      R[r + S] = (a >> S) & ~H;
+    } else {
+      R[r] = bfi(H, b << S, a);
+      R[r + S] = bfi(H, b, a >> S);
     }
   }
 }
@@ -55,32 +93,111 @@ __device__ __forceinline__ void planes_to_fields(const uint32_t (&P)[Q], uint32_
     if constexpr (Q == 8) R[7 - p] = P[p];
     else R[Q - p] = P[p];
   }
-  swap_level<4>(R, 0xF0F0F0F0u);
-  swap_level<2>(R, 0xCCCCCCCCu);
-  swap_level<1>(R, 0xAAAAAAAAu);
+  constexpr unsigned Z0 = Q == 8 ? 0u : (0xFFu & ~(((1u << Q) - 1u) << 1));
+  // level orders with the fewest instructions for each zero pattern
+  constexpr int L0 = (Q == 3) ? 2 : (Q == 5) ? 1 : (Q == 4) ? 2 : 4;
+  constexpr int L1 = (Q == 3) ? 1 : (Q == 5) ? 4 : (Q == 4) ? 1 : 2;
+  constexpr int L2 = (Q == 3) ? 4 : (Q == 5) ? 2 : (Q == 4) ? 4 : 1;
+  constexpr unsigned Z1 = level_zero_after<L0, Z0>();
+  constexpr unsigned Z2 = level_zero_after<L1, Z1>();
+  swap_level<L0, Z0>(R);
+  swap_level<L1, Z1>(R);
+  swap_level<L2, Z2>(R);
 }
 
-// Byte offset into an fp16 table of the weight at position j (0..31) of the
-// word group, given the transposed fields.
-template <int Q>
-__device__ __forceinline__ uint32_t field_offset(const uint32_t (&R)[8], int j) {
-  const uint32_t f = (R[j & 7] >> (8 * (j >> 3))) & 0xFFu;
-  if constexpr (Q == 8) return f << 1;
-  else return f;
+// Byte B of r added to base (one SDWA instruction).
+template <int B>
+__device__ __forceinline__ uint32_t add_byte(uint32_t base, uint32_t r) {
+  uint32_t d;
+  if constexpr (B == 0)
+    asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0"
+        : "=v"(d) : "v"(base), "v"(r));
+  else if constexpr (B == 1)
+    asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1"
+        : "=v"(d) : "v"(base), "v"(r));
+  else if constexpr (B == 2)
+    asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2"
+        : "=v"(d) : "v"(base), "v"(r));
+  else
+    asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
+        : "=v"(d) : "v"(base), "v"(r));
+  return d;
 }
 
-__device__ __forceinline__ uint32_t lds_u16(const uint8_t* base, uint32_t byte_off) {
-  return *reinterpret_cast<const uint16_t*>(base + byte_off);
+// 2 * byte B of r (one SDWA instruction).
+template <int B>
+__device__ __forceinline__ uint32_t twice_byte(uint32_t r) {
+  uint32_t d;
+  if constexpr (B == 0)
+    asm("v_add_u32_sdwa %0, %1, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:BYTE_0"
+        : "=v"(d) : "v"(r));
+  else if constexpr (B == 1)
+    asm("v_add_u32_sdwa %0, %1, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:BYTE_1"
+        : "=v"(d) : "v"(r));
+  else if constexpr (B == 2)
+    asm("v_add_u32_sdwa %0, %1, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2 src1_sel:BYTE_2"
+        : "=v"(d) : "v"(r));
+  else
+    asm("v_add_u32_sdwa %0, %1, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3 src1_sel:BYTE_3"
+        : "=v"(d) : "v"(r));
+  return d;
 }
 
-// Weights j, j+1 (j even) of the 32-weight group, looked up in the row table
-// and packed as (w_j, w_j+1) fp16 pair.
-template <int Q>
-__device__ __forceinline__ half2_t lookup_pair(const uint32_t (&R)[8], const uint8_t* tab, int j) {
-  const uint32_t lo = lds_u16(tab, field_offset<Q>(R, j));
-  const uint32_t hi = lds_u16(tab, field_offset<Q>(R, j + 1));
+// LDS byte address of weight J's table entry: base + 2*code.
+template <int Q, int J>
+__device__ __forceinline__ uint32_t entry_addr(const uint32_t (&R)[8], uint32_t base) {
+  if constexpr (Q == 8) return base + twice_byte<(J >> 3)>(R[J & 7]);
+  else return add_byte<(J >> 3)>(base, R[J & 7]);
+}
+
+typedef const __attribute__((address_space(3))) uint16_t* lds_u16_ptr;
+typedef __attribute__((address_space(3))) uint8_t* lds_u8_ptr;
+
+__device__ __forceinline__ uint32_t lds_u16_at(uint32_t addr) { return *(lds_u16_ptr)(size_t)addr; }
+
+// 32-bit LDS address of a location inside a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(lds_u8_ptr)(const_cast<void*>(p));
+}
+
+// Weights J, J+1 (J even) of the group, looked up in the row table whose LDS
+// address is `base`, packed as an fp16 pair.
+template <int Q, int J>
+__device__ __forceinline__ half2_t lookup_pair(const uint32_t (&R)[8], uint32_t base) {
+  const uint32_t lo = lds_u16_at(entry_addr<Q, J>(R, base));
+  const uint32_t hi = lds_u16_at(entry_addr<Q, J + 1>(R, base));
   return __builtin_bit_cast(half2_t, lo | (hi << 16));
 }
+
+// Decode + dot of one row's 32-weight group against NT tokens' activations:
+// acc[t] += sum_j W[j] * x[t][j], one fp16 pair at a time (J = 0, 2, ..., 30).
+template <int Q, int NT, int J>
+struct GroupDot {
+  __device__ static __forceinline__ void run(const uint32_t (&R)[8], uint32_t base, const half2_t (&xr)[NT][16],
+                                             float* acc) {
+    const half2_t w2 = lookup_pair<Q, J>(R, base);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_fdot2(w2, xr[t][J >> 1], acc[t], false);
+    GroupDot<Q, NT, J + 2>::run(R, base, xr, acc);
+  }
+};
+template <int Q, int NT>
+struct GroupDot<Q, NT, 32> {
+  __device__ static __forceinline__ void run(const uint32_t (&)[8], uint32_t, const half2_t (&)[NT][16], float*) {}
+};
+
+// Decode of one row's 32-weight group into 16 fp16 pairs.
+template <int Q, int J>
+struct GroupDecode {
+  __device__ static __forceinline__ void run(const uint32_t (&R)[8], uint32_t base, uint32_t (&out)[16]) {
+    out[J >> 1] = __builtin_bit_cast(uint32_t, lookup_pair<Q, J>(R, base));
+    GroupDecode<Q, J + 2>::run(R, base, out);
+  }
+};
+template <int Q>
+struct GroupDecode<Q, 32> {
+  __device__ static __forceinline__ void run(const uint32_t (&)[8], uint32_t, uint32_t (&)[16]) {}
+};
 
 // Buffer resource over [base, base + bytes): loads past the end return 0, which
 // is how out-of-range rows and columns read as zero without a branch.
@@ -104,6 +221,20 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+
+// Values the kernels load from memory at a wave-uniform address are the same
+// in every lane, but the compiler cannot always prove it (it must use a vector
+// load when the memory may be written during the kernel).  These helpers say
+// so, which keeps descriptors in scalar registers and branches uniform.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
 
 // Workspace status word: set bits, never cleared by kernels of the forward.
 __device__ __forceinline__ void raise_status(uint32_t* status, uint32_t bits) {

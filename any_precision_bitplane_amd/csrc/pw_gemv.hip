@@ -2,221 +2,483 @@
 // expert has few tokens (decode).  "Technical summary: PagedWeight", Core
 // components 3 (fused mixed-precision kernel): the kernel reads the planes and
 // the tables directly and runs every block at its own committed bitwidth q,
-// which it reads from the device page table, so a commit never changes a launch
-// argument.
+// read from the device page table, so a commit never changes a launch argument.
 //
-// Work decomposition.  A workgroup is one wave and owns 8 rows of one routed
-// expert's block.  Its 64 lanes split a row's K/32 plane words (lane = word
-// column, slices of 64 words), so
-//   * each plane load of a row is one 256-byte coalesced wave access, and only
-//     planes 0..q-1 are read (buffer loads, plane offset in a scalar register);
-//   * a lane's 32 activations per token stay in registers for all 8 rows;
+// Work decomposition.  A workgroup is one wave; it owns a chunk of 16 rows of
+// one routed expert's block (and, for the down product of a small batch, one
+// part of the K range).  Its 64 lanes split a row's K/32 plane words (lane =
+// word column, slices of 64 words), so
+//   * each plane load is one 256-byte coalesced wave access and only planes
+//     0..q-1 are read (buffer loads; the plane offset is a scalar operand);
+//   * a lane's 32 activations per token stay in registers for a whole slice;
 //   * all lanes look up the same row's table, which keeps the LDS gather free
-//     of bank conflicts up to 64 table entries, and the row's table address is
-//     an instruction immediate.
-// The gate_up workgroup takes 4 matching gate and up rows (i and I + i), so
+//     of bank conflicts up to 64 entries, and the table address is an
+//     instruction immediate;
+//   * row groups are double-buffered: the planes of the next group are in
+//     flight while the current one is decoded.
+// gate_up chunks hold 8 gate rows and the matching 8 up rows (i and I + i), so
 // SwiGLU runs in the epilogue and h = SiLU(gate) * up leaves as fp16.
+//
+// Batches of at most 64 routed slots skip the separate route step: every
+// gate_up wave finds its expert and token slots with ballots over the slot
+// ids, and the first wave publishes the routing (counts, offsets, active list,
+// slot order) for the down and combine kernels that follow on the stream.
 #include "pw_device.h"
 #include "pw_internal.h"
 
 namespace pw {
 
-constexpr int kRows = 8;                                   // rows per workgroup (= wave)
+constexpr int kChunkRows = 16;
 constexpr int kMaxTabBytes = (1 << kMaxBits) * 2;          // 512 B per row table
 
-struct GemvParams {
-  ExpertArgs a;
-  const uint16_t* act;   // gate_up: x [T][H];  down: h [slots][I] (sorted positions)
-  void* out;             // gate_up: h fp16 [slots][I];  down: o fp32 [slots][H]
-  int tiles;             // row tiles per expert
+struct GemvArgs {
+  int H, I, E, k, T;
+  const pw_block_desc* blocks;
+  const uint8_t* q;
+  const int32_t* ids;       // router ids [T*k]          (inline routing)
+  Route rt;                 // route-kernel results      (routed mode)
+  int inline_route;         // 1: T*k <= 64 and every wave routes by itself
+  int min_tokens, max_tokens;
+  const uint16_t* act;      // gate_up: x [T][H];  down: h [slots][I]
+  uint16_t* hout;           // gate_up: h [slots][I]
+  float* oout;              // down: o [kparts][slots][H]
+  int chunks;               // row chunks per block
+  int kparts;               // parts of the K range (down)
 };
 
-// Row r (0..7) of tile `tile`; gate_up tiles hold gate rows i..i+3 then the
-// matching up rows I+i..I+i+3.
-template <bool GU>
-__device__ __forceinline__ int tile_row(int tile, int r, int I) {
-  if constexpr (GU) return (r < 4 ? 0 : I) + tile * 4 + (r & 3);
-  else return tile * kRows + r;
+// ---------------------------------------------------------------------------
+// Lane helpers
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // lane i <-> 7-i inside 8-lane halves
+constexpr int kDppRor8 = 0x128;         // lane i <- (i+8) mod 16 inside 16-lane rows
+
+// a in the lower 32 lanes, b in the upper: returns a + a' (lower) / b + b'
+// (upper), where ' is the partner lane l ^ 32.  v_permlane32_swap exchanges the
+// upper half of its first operand with the lower half of its second; the
+// instruction is written out because the compiler builtin returns the second
+// operand's new value incorrectly.  The s_nop pads cover the VALU-to-permlane
+// hazard.
+__device__ __forceinline__ float swap32_add(float a, float b) {
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return a + b;
+}
+// Same across 16-lane rows (odd rows of the first operand <-> even rows of the
+// second): lanes with bit 4 clear keep a's pair sum, set keep b's.
+__device__ __forceinline__ float swap16_add(float a, float b) {
+  asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return a + b;
 }
 
+// Split step inside 16-lane rows: lanes with (lane & bit) clear keep value
+// a's pair sum, the others b's; the partner lane comes from a DPP pattern that
+// pairs each lane with one lane of the opposite half.
+template <int CTRL>
+__device__ __forceinline__ float split_add(float a, float b, bool upper) {
+  const float mine = upper ? b : a;
+  const float give = upper ? a : b;
+  return mine + dpp_f<CTRL>(give);
+}
+
+// Reduce M per-lane values (M = 1..16, power of two) over the wave.  Afterwards
+// the total of value i sits in every lane l with l >> (6 - log2 M) == i.
+template <int M>
+__device__ __forceinline__ float multi_reduce(float (&v)[M]) {
+  const int lane = threadIdx.x;
+  float a[M > 1 ? M / 2 : 1];
+  if constexpr (M >= 2) {
+#pragma unroll
+    for (int i = 0; i < M / 2; ++i) a[i] = swap32_add(v[i], v[i + M / 2]);
+  } else {
+    a[0] = swap32_add(v[0], v[0]);
+  }
+  constexpr int M1 = M > 1 ? M / 2 : 1;
+  float b[M1 > 1 ? M1 / 2 : 1];
+  if constexpr (M1 >= 2) {
+#pragma unroll
+    for (int i = 0; i < M1 / 2; ++i) b[i] = swap16_add(a[i], a[i + M1 / 2]);
+  } else {
+    b[0] = swap16_add(a[0], a[0]);
+  }
+  constexpr int M2 = M1 > 1 ? M1 / 2 : 1;
+  float c[M2 > 1 ? M2 / 2 : 1];
+  if constexpr (M2 >= 2) {
+#pragma unroll
+    for (int i = 0; i < M2 / 2; ++i) c[i] = split_add<kDppRor8>(b[i], b[i + M2 / 2], (lane & 8) != 0);
+  } else {
+    c[0] = b[0] + dpp_f<kDppRor8>(b[0]);
+  }
+  constexpr int M3 = M2 > 1 ? M2 / 2 : 1;
+  float d;
+  if constexpr (M3 >= 2) {
+    static_assert(M3 == 2, "at most 16 values");
+    d = split_add<kDppHalfMirror>(c[0], c[1], (lane & 4) != 0);
+  } else {
+    d = c[0] + dpp_f<kDppHalfMirror>(c[0]);
+  }
+  d += dpp_f<kDppXor2>(d);
+  d += dpp_f<kDppXor1>(d);
+  return d;
+}
+
+__device__ __forceinline__ int wave_excl_scan(int v) {
+  const int lane = threadIdx.x;
+  int s = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(s, o, kWave);
+    if (lane >= o) s += t;
+  }
+  return s - v;
+}
+
+// ---------------------------------------------------------------------------
+// Which expert and which token slots a wave works on
+// ---------------------------------------------------------------------------
+struct Slots {
+  int e, n_e, off_e, num_active;
+  unsigned long long mask;   // inline routing: slots routed to e (bit = slot)
+};
+
+struct RouteLds {
+  int cnt[kMaxExperts];
+  int off[kMaxExperts];
+  int e_sel;
+};
+
+// Write the routing one wave computed in LDS to the workspace, in the same
+// form the route kernel produces (stable expert-sorted slot order).
+__device__ void publish_route(const GemvArgs& A, RouteLds& L, int id, bool valid, const int (&c)[4], int nzr,
+                              int run) {
+  const int lane = threadIdx.x;
+  const int S = A.T * A.k;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ex = 4 * lane + i;
+    if (ex < A.E) {
+      A.rt.counts[ex] = c[i];
+      A.rt.offsets[ex] = run;
+      if (c[i] > 0) A.rt.active[nzr++] = ex;
+    }
+    run += c[i];
+  }
+  if (lane == kWave - 1) {
+    A.rt.offsets[A.E] = run;
+    *A.rt.num_active = nzr;
+  }
+  int rank = 0;
+  unsigned long long todo = __ballot(valid);
+  while (todo) {
+    const int leader = __ffsll(todo) - 1;
+    const int le = __shfl(id, leader, kWave);
+    const unsigned long long m = __ballot(valid && id == le);
+    if (valid && id == le) rank = __popcll(m & ((1ull << lane) - 1ull));
+    todo &= ~m;
+  }
+  if (lane < S) {
+    const int pos = valid ? L.off[id] + rank : -1;
+    A.rt.inv[lane] = pos;
+    if (valid) A.rt.perm[pos] = lane;
+  }
+}
+
+// Inline routing over S = T*k <= 64 slots, one slot per lane.  Returns false
+// when fewer than a+1 experts are routed.
+__device__ bool find_expert_inline(const GemvArgs& A, int a, Slots& sl, RouteLds& L) {
+  const int lane = threadIdx.x;
+  const int S = A.T * A.k;
+  const int id = lane < S ? A.ids[lane] : -1;
+  const bool valid = id >= 0 && id < A.E;
+  if (blockIdx.x == 0 && __ballot(lane < S && !valid) != 0ull && lane == 0)
+    raise_status(A.rt.status, PW_DEV_BAD_EXPERT_ID);
+  for (int i = lane; i < A.E; i += kWave) L.cnt[i] = 0;
+  if (lane == 0) L.e_sel = -1;
+  __syncthreads();
+  if (valid) atomicAdd(&L.cnt[id], 1);
+  __syncthreads();
+  int c[4], tot = 0, nz = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ex = 4 * lane + i;
+    c[i] = ex < A.E ? L.cnt[ex] : 0;
+    tot += c[i];
+    nz += c[i] > 0 ? 1 : 0;
+  }
+  int run = wave_excl_scan(tot);
+  int nzr = wave_excl_scan(nz);
+  const int run_base = run, nzr_base = nzr;
+  const int n_act = uniform(__shfl(nzr + nz, kWave - 1, kWave));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ex = 4 * lane + i;
+    if (ex < A.E) L.off[ex] = run;
+    run += c[i];
+    if (c[i] > 0) {
+      if (nzr == a) L.e_sel = ex;
+      ++nzr;
+    }
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) publish_route(A, L, id, valid, c, nzr_base, run_base);
+  // Values read back from LDS are the same in every lane; saying so keeps the
+  // block's buffer descriptor in scalar registers.
+  sl.num_active = __builtin_amdgcn_readfirstlane(n_act);
+  if (a >= sl.num_active) return false;
+  const int e = __builtin_amdgcn_readfirstlane(L.e_sel);
+  sl.e = e;
+  sl.n_e = __builtin_amdgcn_readfirstlane(L.cnt[e]);
+  sl.off_e = __builtin_amdgcn_readfirstlane(L.off[e]);
+  sl.mask = __ballot(id == e);
+  return true;
+}
+
+__device__ bool find_expert_routed(const GemvArgs& A, int a, Slots& sl) {
+  const int n_act = uniform(*A.rt.num_active);
+  sl.num_active = n_act;
+  if (a >= n_act) return false;
+  const int e = uniform(A.rt.active[a]);
+  sl.e = e;
+  sl.n_e = uniform(A.rt.counts[e]);
+  sl.off_e = uniform(A.rt.offsets[e]);
+  sl.mask = 0ull;
+  return true;
+}
+
+// Slot (t*k + j) of the r-th token of the expert, in slot order.
+__device__ __forceinline__ int slot_of(const GemvArgs& A, const Slots& sl, int r) {
+  if (A.inline_route) {
+    unsigned long long m = sl.mask;
+    for (int i = 0; i < r; ++i) m &= m - 1ull;
+    return __ffsll(m) - 1;
+  }
+  return uniform(A.rt.perm[sl.off_e + r]);
+}
+
+// ---------------------------------------------------------------------------
+// One chunk of 16 rows at bitwidth Q for up to NT tokens at a time
+// ---------------------------------------------------------------------------
 template <bool GU>
-__device__ __forceinline__ bool row_valid(int tile, int r, int I, int H) {
-  if constexpr (GU) return tile * 4 + (r & 3) < I;
-  else return tile * kRows + r < H;
+__device__ __forceinline__ int chunk_row(int chunk, int r, int I) {
+  if constexpr (GU) return (r < 8 ? 0 : I) + chunk * 8 + (r & 7);
+  else return chunk * kChunkRows + r;
 }
 
 template <int Q, int NT, bool GU>
-__device__ __forceinline__ void gemv_body(const GemvParams& p, int e, int n_e, int tile, uint8_t* lds) {
+__device__ void chunk_body(const GemvArgs& A, const Slots& sl, int chunk, int kpart, uint8_t* tabs) {
+  constexpr int G = 4;                         // rows per pipeline group
+  constexpr int NGR = kChunkRows / G;          // groups per slice
+  constexpr int TAB = (1 << Q) * 2;            // bytes per row table
+  constexpr int M = G * NT;                    // values reduced per group
+  constexpr int MSH = 6 - (M == 1 ? 0 : M == 2 ? 1 : M == 4 ? 2 : M == 8 ? 3 : 4);
   const int lane = threadIdx.x;
-  const int H = p.a.H, I = p.a.I, k = p.a.k;
+  const int H = A.H, I = A.I;
   const int N = GU ? 2 * I : H;
   const int K = GU ? H : I;
   const int W = K >> 5;
-  const pw_block_desc d = p.a.blocks[2 * e + (GU ? 0 : 1)];
-  const uint32_t pstride = (uint32_t)N * (uint32_t)W * 4u;          // bytes per plane
-  const __amdgpu_buffer_rsrc_t prs = make_rsrc(d.planes, pstride * Q);
-  const uint16_t* __restrict__ lut = d.lut_all + lut_offset(N, Q);
-  const int off_e = p.a.rt.offsets[e];
-  const int* __restrict__ perm = p.a.rt.perm;
+  const pw_block_desc d = A.blocks[2 * sl.e + (GU ? 0 : 1)];
+  const uint32_t pstride = (uint32_t)N * (uint32_t)W * 4u;
+  const __amdgpu_buffer_rsrc_t prs = make_rsrc(uniform_ptr(d.planes), pstride * (uint32_t)Q);
+  const uint16_t* __restrict__ lut = uniform_ptr(d.lut_all) + lut_offset(N, Q);
 
-  // Stage the 8 row tables (2^Q fp16 each) into LDS.
-  constexpr int TAB = (1 << Q) * 2;
-  constexpr int CH = TAB / 16;            // 16-byte chunks per table
+  // Row tables of the chunk -> LDS (gate_up: two spans of 8 rows; down: one of 16).
+  {
+    constexpr int SPAN_ROWS = GU ? 8 : 16;
+    constexpr int SPAN_CH = SPAN_ROWS * TAB / 16;
 #pragma unroll
-  for (int r = 0; r < kRows; ++r) {
-    const bool rv = row_valid<GU>(tile, r, I, H);
-    for (int c = lane; c < CH; c += kWave) {
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (rv) v = *reinterpret_cast<const uint4*>(lut + (size_t)tile_row<GU>(tile, r, I) * (1 << Q) + c * 8);
-      *reinterpret_cast<uint4*>(lds + r * TAB + c * 16) = v;
+    for (int sp = 0; sp < (GU ? 2 : 1); ++sp) {
+      const uint16_t* src = lut + (size_t)chunk_row<GU>(chunk, sp * SPAN_ROWS, I) * (1 << Q);
+      uint8_t* dst = tabs + sp * SPAN_ROWS * TAB;
+#pragma unroll
+      for (int c0 = 0; c0 < SPAN_CH; c0 += kWave) {
+        const int c = c0 + lane;
+        if (c < SPAN_CH) *reinterpret_cast<uint4*>(dst + c * 16) = *reinterpret_cast<const uint4*>(src + c * 8);
+      }
     }
   }
   __syncthreads();
 
-  for (int t0 = 0; t0 < n_e; t0 += NT) {
-    const int nt = min(NT, n_e - t0);
-    float acc[kRows][NT];
-#pragma unroll
-    for (int r = 0; r < kRows; ++r)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc[r][t] = 0.0f;
+  const uint32_t tab_base = lds_addr(tabs);
+  const int nsl = (W + kWave - 1) / kWave;
+  const int spp = (nsl + A.kparts - 1) / A.kparts;
+  const int s_begin = kpart * spp;
+  const int s_end = min(nsl, s_begin + spp);
+  const int nsteps = max(0, s_end - s_begin) * NGR;
+  const int slots = A.T * A.k;
 
-    for (int s0 = 0; s0 < W; s0 += kWave) {
-      const int wc = s0 + lane;
-      const bool cv = wc < W;
-
-      // First Q plane words of the 8 rows (zero outside the block).
-      uint32_t P[kRows][Q];
+  for (int t0 = 0; t0 < sl.n_e; t0 += NT) {
+    const int nt = min(NT, sl.n_e - t0);
+    const uint16_t* xsrc[NT];
 #pragma unroll
-      for (int r = 0; r < kRows; ++r) {
-        const bool ok = cv && row_valid<GU>(tile, r, I, H);
-        const uint32_t voff = ok ? ((uint32_t)tile_row<GU>(tile, r, I) * (uint32_t)W + (uint32_t)wc) * 4u
-                                 : kOutOfRange;
-#pragma unroll
-        for (int pp = 0; pp < Q; ++pp) P[r][pp] = buf_load_u32(prs, voff, pp * pstride);
-      }
-
-      // Activations of this word column (32 values per token).
-      half2_t xr[NT][16];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const uint16_t* src = nullptr;
-        if (t < nt && cv) {
-          const int pos = off_e + t0 + t;
-          src = GU ? p.act + (size_t)(perm[pos] / k) * H : p.act + (size_t)pos * I;
-        }
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          uint4 u = make_uint4(0u, 0u, 0u, 0u);
-          if (src) u = *reinterpret_cast<const uint4*>(src + wc * 32 + v * 8);
-          xr[t][4 * v + 0] = __builtin_bit_cast(half2_t, u.x);
-          xr[t][4 * v + 1] = __builtin_bit_cast(half2_t, u.y);
-          xr[t][4 * v + 2] = __builtin_bit_cast(half2_t, u.z);
-          xr[t][4 * v + 3] = __builtin_bit_cast(half2_t, u.w);
-        }
-      }
-
-#pragma unroll
-      for (int r = 0; r < kRows; ++r) {
-        uint32_t R[8];
-        planes_to_fields<Q>(P[r], R);
-        const uint8_t* tab = lds + r * TAB;
-#pragma unroll
-        for (int j = 0; j < 32; j += 2) {
-          const half2_t w2 = lookup_pair<Q>(R, tab, j);
-#pragma unroll
-          for (int t = 0; t < NT; ++t) acc[r][t] = __builtin_amdgcn_fdot2(w2, xr[t][j >> 1], acc[r][t], false);
-        }
+    for (int t = 0; t < NT; ++t) {
+      xsrc[t] = nullptr;
+      if (t < nt) {
+        if constexpr (GU) xsrc[t] = A.act + (size_t)(slot_of(A, sl, t0 + t) / A.k) * H;
+        else xsrc[t] = A.act + (size_t)(sl.off_e + t0 + t) * I;
       }
     }
 
-#pragma unroll
-    for (int r = 0; r < kRows; ++r)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc[r][t] = wave_sum(acc[r][t]);
+    float tot = 0.0f;                // lane (t * 16 + r): total of chunk row r, token t
+    uint32_t Pa[G][Q], Pb[G][Q];
+    half2_t xr[NT][16];
+    int xslice = -1;
 
-    if constexpr (GU) {
-      uint16_t* hout = reinterpret_cast<uint16_t*>(p.out);
+    auto load_group = [&](uint32_t (&P)[G][Q], int st) {
+      const int slice = s_begin + st / NGR;
+      const int g = st % NGR;
+      const int wc = slice * kWave + lane;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < G; ++r) {
+        const uint32_t voff =
+            wc < W ? ((uint32_t)chunk_row<GU>(chunk, g * G + r, I) * (uint32_t)W + (uint32_t)wc) * 4u : kOutOfRange;
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-          if (lane == r * NT + t && t < nt && row_valid<GU>(tile, r, I, H)) {
-            const float h = silu_f32(acc[r][t]) * acc[r + 4][t];
-            const _Float16 hh = (_Float16)h;
-            hout[(size_t)(off_e + t0 + t) * I + tile_row<GU>(tile, r, I)] = __builtin_bit_cast(uint16_t, hh);
+        for (int p = 0; p < Q; ++p) P[r][p] = buf_load_u32(prs, voff, (uint32_t)p * pstride);
+      }
+    };
+
+    auto compute_group = [&](uint32_t (&P)[G][Q], int st) {
+      const int slice = s_begin + st / NGR;
+      const int g = st % NGR;
+      if (slice != xslice) {
+        xslice = slice;
+        const int wc = slice * kWave + lane;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            uint4 u = make_uint4(0u, 0u, 0u, 0u);
+            if (xsrc[t] != nullptr && wc < W) u = *reinterpret_cast<const uint4*>(xsrc[t] + wc * 32 + v * 8);
+            xr[t][4 * v + 0] = __builtin_bit_cast(half2_t, u.x);
+            xr[t][4 * v + 1] = __builtin_bit_cast(half2_t, u.y);
+            xr[t][4 * v + 2] = __builtin_bit_cast(half2_t, u.z);
+            xr[t][4 * v + 3] = __builtin_bit_cast(half2_t, u.w);
           }
+        }
+      }
+      float acc[M];
+#pragma unroll
+      for (int i = 0; i < M; ++i) acc[i] = 0.0f;
+#pragma unroll
+      for (int r = 0; r < G; ++r) {
+        // one row at a time: keeps the scheduler from interleaving the decode
+        // of several rows, which would cost registers and occupancy
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t R[8];
+        planes_to_fields<Q>(P[r], R);
+        GroupDot<Q, NT, 0>::run(R, tab_base + (uint32_t)((g * G + r) * TAB), xr, &acc[r * NT]);
+      }
+      const float red = multi_reduce<M>(acc);
+      // lane L = t * 16 + row takes value (row - g*G) * NT + t from lane vi << MSH
+      const int t_l = lane >> 4;
+      const int r_l = (lane & 15) - g * G;
+      const int vi = (r_l >= 0 && r_l < G) ? r_l * NT + t_l : 0;
+      const float v = __shfl(red, vi << MSH, kWave);
+      if (t_l < NT && r_l >= 0 && r_l < G) tot += v;
+    };
+
+    if (nsteps > 0) load_group(Pa, 0);
+    for (int st = 0; st < nsteps; st += 2) {
+      if (st + 1 < nsteps) load_group(Pb, st + 1);
+      compute_group(Pa, st);
+      if (st + 2 < nsteps) load_group(Pa, st + 2);
+      if (st + 1 < nsteps) compute_group(Pb, st + 1);
+    }
+
+    const int t_l = lane >> 4;
+    const int r_l = lane & 15;
+    if constexpr (GU) {
+      // up row r + 8 sits 8 lanes above gate row r inside the same 16-lane row
+      const float u = dpp_f<kDppRor8>(tot);
+      if (lane < 32 && r_l < 8 && t_l < nt) {
+        const float h = silu_f32(tot) * u;
+        const _Float16 hh = (_Float16)h;
+        A.hout[(size_t)(sl.off_e + t0 + t_l) * I + chunk * 8 + r_l] = __builtin_bit_cast(uint16_t, hh);
+      }
     } else {
-      float* oout = reinterpret_cast<float*>(p.out);
-#pragma unroll
-      for (int r = 0; r < kRows; ++r)
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-          if (lane == r * NT + t && t < nt && row_valid<GU>(tile, r, I, H))
-            oout[(size_t)(off_e + t0 + t) * H + tile_row<GU>(tile, r, I)] = acc[r][t];
+      if (lane < 32 && t_l < nt)
+        A.oout[((size_t)kpart * slots + sl.off_e + t0 + t_l) * H + chunk * kChunkRows + r_l] = tot;
     }
   }
 }
 
 // Rows of a block whose committed bitwidth is invalid read as zero.
 template <bool GU>
-__device__ void gemv_zero_rows(const GemvParams& p, int e, int n_e, int tile) {
+__device__ void chunk_zero(const GemvArgs& A, const Slots& sl, int chunk, int kpart) {
   const int lane = threadIdx.x;
-  const int H = p.a.H, I = p.a.I;
-  const int off_e = p.a.rt.offsets[e];
-  for (int t = lane; t < n_e; t += kWave) {
-#pragma unroll
-    for (int r = 0; r < (GU ? 4 : kRows); ++r) {
-      if (!row_valid<GU>(tile, r, I, H)) continue;
-      const int row = tile_row<GU>(tile, r, I);
-      if constexpr (GU) reinterpret_cast<uint16_t*>(p.out)[(size_t)(off_e + t) * I + row] = 0;
-      else reinterpret_cast<float*>(p.out)[(size_t)(off_e + t) * H + row] = 0.0f;
-    }
+  const int slots = A.T * A.k;
+  for (int i = lane; i < sl.n_e * (GU ? 8 : kChunkRows); i += kWave) {
+    const int t = i / (GU ? 8 : kChunkRows), r = i % (GU ? 8 : kChunkRows);
+    if constexpr (GU) A.hout[(size_t)(sl.off_e + t) * A.I + chunk * 8 + r] = 0;
+    else A.oout[((size_t)kpart * slots + sl.off_e + t) * A.H + chunk * kChunkRows + r] = 0.0f;
   }
-  if (lane == 0 && tile == 0) raise_status(p.a.rt.status, PW_DEV_BAD_BITWIDTH);
+  if (lane == 0 && chunk == 0 && kpart == 0) raise_status(A.rt.status, PW_DEV_BAD_BITWIDTH);
 }
 
 template <int Q, bool GU>
-__device__ __forceinline__ void gemv_by_tokens(const GemvParams& p, int e, int n_e, int tile, uint8_t* lds) {
-  if (n_e == 1) gemv_body<Q, 1, GU>(p, e, n_e, tile, lds);
-  else gemv_body<Q, 2, GU>(p, e, n_e, tile, lds);
+__device__ __forceinline__ void chunk_by_tokens(const GemvArgs& A, const Slots& sl, int chunk, int kpart,
+                                                uint8_t* tabs) {
+  if (sl.n_e == 1) chunk_body<Q, 1, GU>(A, sl, chunk, kpart, tabs);
+  else chunk_body<Q, 2, GU>(A, sl, chunk, kpart, tabs);
 }
 
 template <bool GU>
-__global__ __launch_bounds__(kWave) void gemv_kernel(GemvParams p) {
-  __shared__ __align__(16) uint8_t lds[kRows * kMaxTabBytes];
-  const int a = blockIdx.x / p.tiles;
-  const int tile = blockIdx.x % p.tiles;
-  if (a >= *p.a.rt.num_active) return;
-  const int e = p.a.rt.active[a];
-  const int n_e = p.a.rt.counts[e];
-  if (n_e < p.a.min_tokens || n_e >= p.a.max_tokens) return;
-  switch (p.a.q[2 * e + (GU ? 0 : 1)]) {
-    case 3: gemv_by_tokens<3, GU>(p, e, n_e, tile, lds); break;
-    case 4: gemv_by_tokens<4, GU>(p, e, n_e, tile, lds); break;
-    case 5: gemv_by_tokens<5, GU>(p, e, n_e, tile, lds); break;
-    case 6: gemv_by_tokens<6, GU>(p, e, n_e, tile, lds); break;
-    case 7: gemv_by_tokens<7, GU>(p, e, n_e, tile, lds); break;
-    case 8: gemv_by_tokens<8, GU>(p, e, n_e, tile, lds); break;
-    default: gemv_zero_rows<GU>(p, e, n_e, tile); break;
+__global__ __launch_bounds__(kWave) void gemv_kernel(GemvArgs A) {
+  __shared__ __align__(16) uint8_t tabs[kChunkRows * kMaxTabBytes];
+  __shared__ RouteLds L;
+  const int per_expert = A.chunks * A.kparts;
+  const int a = blockIdx.x / per_expert;
+  const int rem = blockIdx.x % per_expert;
+  const int chunk = rem / A.kparts;
+  const int kpart = rem % A.kparts;
+  Slots sl;
+  const bool have = A.inline_route ? find_expert_inline(A, a, sl, L) : find_expert_routed(A, a, sl);
+  if (!have) return;
+  if (sl.n_e < A.min_tokens || sl.n_e >= A.max_tokens) return;
+
+  switch (uniform(A.q[2 * sl.e + (GU ? 0 : 1)])) {
+    case 3: chunk_by_tokens<3, GU>(A, sl, chunk, kpart, tabs); break;
+    case 4: chunk_by_tokens<4, GU>(A, sl, chunk, kpart, tabs); break;
+    case 5: chunk_by_tokens<5, GU>(A, sl, chunk, kpart, tabs); break;
+    case 6: chunk_by_tokens<6, GU>(A, sl, chunk, kpart, tabs); break;
+    case 7: chunk_by_tokens<7, GU>(A, sl, chunk, kpart, tabs); break;
+    case 8: chunk_by_tokens<8, GU>(A, sl, chunk, kpart, tabs); break;
+    default: chunk_zero<GU>(A, sl, chunk, kpart); break;
   }
+
 }
 
-static int active_bound(const ExpertArgs& a) { return a.E < a.T * a.k ? a.E : a.T * a.k; }
+static int active_bound(int E, int T, int k) { return E < T * k ? E : T * k; }
 
-hipError_t launch_gemv_gate_up(const ExpertArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s) {
-  GemvParams p{a, x, h, (a.I + 3) / 4};
-  const int grid = active_bound(a) * p.tiles;
+hipError_t launch_gemv_gate_up(const GemvLaunch& g, hipStream_t s) {
+  GemvArgs A{};
+  A.H = g.H; A.I = g.I; A.E = g.E; A.k = g.k; A.T = g.T;
+  A.blocks = g.blocks; A.q = g.q; A.ids = g.ids; A.rt = g.rt;
+  A.inline_route = g.inline_route; A.min_tokens = g.min_tokens; A.max_tokens = g.max_tokens;
+  A.act = g.x; A.hout = g.h; A.oout = nullptr;
+  A.chunks = g.I / 8;
+  A.kparts = 1;
+  const int grid = active_bound(g.E, g.T, g.k) * A.chunks;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(gemv_kernel<true>, dim3(grid), dim3(kWave), 0, s, p);
+  hipLaunchKernelGGL(gemv_kernel<true>, dim3(grid), dim3(kWave), 0, s, A);
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_down(const ExpertArgs& a, const uint16_t* h, float* o, hipStream_t s) {
-  GemvParams p{a, h, o, (a.H + kRows - 1) / kRows};
-  const int grid = active_bound(a) * p.tiles;
+hipError_t launch_gemv_down(const GemvLaunch& g, hipStream_t s) {
+  GemvArgs A{};
+  A.H = g.H; A.I = g.I; A.E = g.E; A.k = g.k; A.T = g.T;
+  A.blocks = g.blocks; A.q = g.q; A.ids = g.ids; A.rt = g.rt;
+  A.inline_route = 0;    // the gate_up kernel or the route kernel published the routing
+  A.min_tokens = g.min_tokens; A.max_tokens = g.max_tokens;
+  A.act = g.h; A.hout = nullptr; A.oout = g.o;
+  A.chunks = g.H / kChunkRows;
+  A.kparts = g.kparts;
+  const int grid = active_bound(g.E, g.T, g.k) * A.chunks * A.kparts;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(gemv_kernel<false>, dim3(grid), dim3(kWave), 0, s, p);
+  hipLaunchKernelGGL(gemv_kernel<false>, dim3(grid), dim3(kWave), 0, s, A);
   return hipGetLastError();
 }
 

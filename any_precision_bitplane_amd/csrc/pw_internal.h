@@ -16,6 +16,19 @@ constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Parts of the down product's K range given to separate waves when a small
+// batch would otherwise leave most of the chip idle.
+inline int down_kparts(int H, int I, int E, int k, int T) {
+  const int slots = T * k;
+  if (slots > 64 || slots <= 0) return 1;
+  const int bound = E < slots ? E : slots;
+  const int waves = bound * (H / 16);
+  const int nsl = (I / 32 + 63) / 64;
+  int kp = (2048 + waves - 1) / waves;
+  if (kp > nsl) kp = nsl;
+  return kp < 1 ? 1 : kp;
+}
+
 // Workspace layout (byte offsets from the workspace base).  The first 256
 // bytes are the header: status word, active-expert count.
 struct WsLayout {
@@ -27,7 +40,7 @@ struct WsLayout {
   size_t perm = 0;          // int32 [T*k]  sorted position -> slot (t*k + j)
   size_t inv = 0;           // int32 [T*k]  slot -> sorted position, -1 if dropped
   size_t h = 0;             // fp16  [T*k][I] activations between the products
-  size_t o = 0;             // fp32  [T*k][H] expert outputs before the combine
+  size_t o = 0;             // fp32  [kparts][T*k][H] expert outputs before the combine
   size_t total = 0;
 };
 
@@ -35,13 +48,14 @@ inline WsLayout ws_layout(int H, int I, int E, int k, int T) {
   WsLayout L;
   size_t off = kAlign;
   const size_t slots = (size_t)T * (size_t)k;
+  const size_t kp = (size_t)down_kparts(H, I, E, k, T);
   L.counts = off;  off = align_up(off + sizeof(int32_t) * E, kAlign);
   L.offsets = off; off = align_up(off + sizeof(int32_t) * (E + 1), kAlign);
   L.active = off;  off = align_up(off + sizeof(int32_t) * E, kAlign);
   L.perm = off;    off = align_up(off + sizeof(int32_t) * slots, kAlign);
   L.inv = off;     off = align_up(off + sizeof(int32_t) * slots, kAlign);
   L.h = off;       off = align_up(off + sizeof(uint16_t) * slots * I, kAlign);
-  L.o = off;       off = align_up(off + sizeof(float) * slots * H, kAlign);
+  L.o = off;       off = align_up(off + sizeof(float) * kp * slots * H, kAlign);
   L.total = off;
   return L;
 }
@@ -66,16 +80,32 @@ struct ExpertArgs {
   int max_tokens;
 };
 
+// Everything the GEMV kernels need for one call.
+struct GemvLaunch {
+  int H, I, E, k, T;
+  const pw_block_desc* blocks;
+  const uint8_t* q;
+  const int32_t* ids;
+  Route rt;
+  int inline_route;          // T*k <= 64: no route kernel, gate_up waves route by themselves
+  int min_tokens, max_tokens;
+  const uint16_t* x;
+  uint16_t* h;
+  float* o;
+  int kparts;
+};
+
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_route(const int32_t* ids, int T, int k, int E, const Route& rt, hipStream_t s);
-hipError_t launch_gemv_gate_up(const ExpertArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s);
-hipError_t launch_gemv_down(const ExpertArgs& a, const uint16_t* h, float* o, hipStream_t s);
+hipError_t launch_gemv_gate_up(const GemvLaunch& g, hipStream_t s);
+hipError_t launch_gemv_down(const GemvLaunch& g, hipStream_t s);
 hipError_t launch_mfma_gate_up(const ExpertArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s);
 hipError_t launch_mfma_down(const ExpertArgs& a, const uint16_t* h, float* o, hipStream_t s);
-hipError_t launch_combine(const float* o, const float* w, const int32_t* inv, int T, int k, int H,
+hipError_t launch_combine(const float* o, const float* w, const int32_t* inv, int T, int k, int H, int kparts,
                           uint16_t* y, hipStream_t s);
 hipError_t launch_dequant(const uint32_t* planes, const uint16_t* lut_all, int N, int K, int q,
                           uint16_t* out, hipStream_t s);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_status_clear(uint32_t* status, hipStream_t s);
 
 }  // namespace pw

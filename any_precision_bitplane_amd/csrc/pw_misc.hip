@@ -4,7 +4,8 @@
 
 namespace pw {
 
-// y[t][n] = fp16( sum_{j < k, ascending} w[t][j] * o[inv[t*k + j]][n] ).
+// y[t][n] = fp16( sum_{j < k, ascending} w[t][j] * o[inv[t*k + j]][n] ), where
+// o is the sum of its K parts (the down product may split K across waves).
 // The router weights are used as given; a slot the route step dropped (expert
 // id out of range) has inv = -1 and adds nothing.  Fixed j order and no
 // atomics, so the result is deterministic.
@@ -12,8 +13,9 @@ constexpr int kCombineThreads = 256;
 
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ o,
                                                                   const float* __restrict__ w,
-                                                                  const int32_t* __restrict__ inv, int k,
-                                                                  int H, uint16_t* __restrict__ y) {
+                                                                  const int32_t* __restrict__ inv, int k, int H,
+                                                                  int kparts, size_t part_stride,
+                                                                  uint16_t* __restrict__ y) {
   const int t = blockIdx.y;
   const int n = (blockIdx.x * kCombineThreads + threadIdx.x) * 4;
   if (n >= H) return;
@@ -22,7 +24,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
     const int pos = inv[t * k + j];
     if (pos < 0) continue;
     const float wj = w[t * k + j];
-    const floatx4 v = *reinterpret_cast<const floatx4*>(o + (size_t)pos * H + n);
+    floatx4 v = *reinterpret_cast<const floatx4*>(o + (size_t)pos * H + n);
+    for (int kp = 1; kp < kparts; ++kp)
+      v += *reinterpret_cast<const floatx4*>(o + kp * part_stride + (size_t)pos * H + n);
     a0 = __builtin_fmaf(wj, v[0], a0);
     a1 = __builtin_fmaf(wj, v[1], a1);
     a2 = __builtin_fmaf(wj, v[2], a2);
@@ -35,11 +39,12 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
   *reinterpret_cast<uint2*>(y + (size_t)t * H + n) = packed;
 }
 
-hipError_t launch_combine(const float* o, const float* w, const int32_t* inv, int T, int k, int H,
+hipError_t launch_combine(const float* o, const float* w, const int32_t* inv, int T, int k, int H, int kparts,
                           uint16_t* y, hipStream_t s) {
   const int per_block = kCombineThreads * 4;
   dim3 grid((H + per_block - 1) / per_block, T);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombineThreads), 0, s, o, w, inv, k, H, y);
+  const size_t part_stride = (size_t)T * k * H;
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombineThreads), 0, s, o, w, inv, k, H, kparts, part_stride, y);
   return hipGetLastError();
 }
 
@@ -88,13 +93,8 @@ __global__ __launch_bounds__(kDqThreads) void dequant_kernel(const uint32_t* __r
       for (int pp = 0; pp < Q; ++pp) P[pp] = planes[pp * pstride + (size_t)row * W + wc];
       uint32_t R[8];
       planes_to_fields<Q>(P, R);
-      const uint8_t* tab = tabs + r * TAB;
       uint32_t packed[16];
-#pragma unroll
-      for (int j = 0; j < 32; j += 2) {
-        const half2_t w2 = lookup_pair<Q>(R, tab, j);
-        packed[j >> 1] = __builtin_bit_cast(uint32_t, w2);
-      }
+      GroupDecode<Q, 0>::run(R, lds_addr(tabs + r * TAB), packed);
       uint4* dst = reinterpret_cast<uint4*>(out + (size_t)row * K + (size_t)wc * 32);
 #pragma unroll
       for (int v = 0; v < 4; ++v)
@@ -116,6 +116,29 @@ hipError_t launch_dequant(const uint32_t* planes, const uint16_t* lut_all, int N
     case 8: hipLaunchKernelGGL(dequant_kernel<8>, grid, dim3(kDqThreads), 0, s, planes, lut_all, N, K, out); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+}  // namespace pw
+
+namespace pw {
+
+// Zero [p, p + bytes): 16-byte stores for the aligned body, byte stores for the tail.
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint8_t* p, size_t n16, size_t bytes) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    reinterpret_cast<uint4*>(p)[i] = make_uint4(0u, 0u, 0u, 0u);
+  const size_t tail = n16 * 16;
+  for (size_t i = tail + (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < bytes; i += stride) p[i] = 0;
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<uint8_t*>(p), n16,
+                     bytes);
   return hipGetLastError();
 }
 
