@@ -15,7 +15,8 @@ using namespace pw;
 
 namespace {
 
-constexpr int kDefaultMfmaMinTokens = INT_MAX;   // MFMA family not built yet
+// AUTO: experts with at least this many routed tokens take the MFMA kernels.
+constexpr int kDefaultMfmaMinTokens = 16;
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -109,6 +110,8 @@ pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T, const uint16_t* x
   rt.active = reinterpret_cast<int32_t*>(ws + L.active);
   rt.perm = reinterpret_cast<int32_t*>(ws + L.perm);
   rt.inv = reinterpret_cast<int32_t*>(ws + L.inv);
+  rt.mtiles = reinterpret_cast<int32_t*>(ws + L.mtiles);
+  rt.num_mtiles = reinterpret_cast<int32_t*>(ws + L.num_mtiles);
   uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
   float* o = reinterpret_cast<float*>(ws + L.o);
 
@@ -131,7 +134,7 @@ pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T, const uint16_t* x
   };
 
   hipError_t e = mark(PW_STAGE_ROUTE);
-  if (e == hipSuccess && !inline_route) e = launch_route(ids, T, k, E, rt, s);
+  if (e == hipSuccess && !inline_route) e = launch_route(ids, T, k, E, use_mfma ? (thresh == 0 ? 1 : thresh) : INT_MAX, rt, s);
   if (e == hipSuccess) e = mark(PW_STAGE_GATE_UP);
   if (e == hipSuccess && use_gemv) e = launch_gemv_gate_up(g, s);
   if (e == hipSuccess && use_mfma) e = launch_mfma_gate_up(mfma, x, h, s);

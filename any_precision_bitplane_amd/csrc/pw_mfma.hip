@@ -1,15 +1,260 @@
 // Dequant-to-LDS MFMA kernels for experts with many tokens (prefill).
+// "Technical summary: PagedWeight", Core components 3 (fused mixed-precision
+// kernel): each block is read at its own committed bitwidth q from the device
+// page table; here the decoded weights feed the matrix cores instead of a
+// GEMV, because with hundreds of tokens per expert the product is a dense
+// contraction.
+//
+// Tile: 128 tokens x 128 weight rows, K step 64.  Per K step every thread of
+// the 4-wave workgroup decodes one 32-weight group (the first q plane words of
+// one row) through the row's table in LDS into an fp16 weight tile, and loads
+// 64 bytes of the gathered activation tile; then each wave multiplies a 64 x 64
+// sub-tile with v_mfma_f32_16x16x32_f16 (fp32 accumulation).  gate_up tiles take
+// 64 gate rows and the matching 64 up rows, and each wave holds matching gate
+// and up columns, so SwiGLU runs on the accumulators and h leaves as fp16.
+//
+// Work items are (token tile, row tile) pairs; token tiles come from the route
+// kernel's list.  Consecutive items on one XCD (workgroups are dealt to the 8
+// XCDs round-robin) sweep the row tiles of one token tile, so the activation
+// tile stays in that XCD's L2.
 #include "pw_device.h"
 #include "pw_internal.h"
 
 namespace pw {
 
-hipError_t launch_mfma_gate_up(const ExpertArgs&, const uint16_t*, uint16_t*, hipStream_t) {
-  return hipErrorNotSupported;
+constexpr int kMfmaThreads = 256;
+constexpr int kTM = kMfmaTileM;        // 128 tokens
+constexpr int kTN = 128;               // weight rows
+constexpr int kTK = 64;                // reduction step
+constexpr int kTileStride = kTK + 8;   // fp16 elements per LDS tile row (padding against bank conflicts)
+constexpr int kXcds = 8;
+
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+struct MfmaArgs {
+  int H, I, E, k, T;
+  const pw_block_desc* blocks;
+  const uint8_t* q;
+  Route rt;
+  const uint16_t* act;   // gate_up: x [T][H]; down: h [slots][I]
+  uint16_t* hout;        // gate_up output
+  float* oout;           // down output
+  int ntiles;            // row tiles per block
+  int grid;              // launched workgroups (multiple of 8)
+};
+
+// Row of the block held at tile-local row r (0..127).
+template <bool GU>
+__device__ __forceinline__ int mrow(int nt, int r, int I) {
+  if constexpr (GU) return (r < 64 ? 0 : I) + nt * 64 + (r & 63);
+  else return nt * kTN + r;
 }
 
-hipError_t launch_mfma_down(const ExpertArgs&, const uint16_t*, float*, hipStream_t) {
-  return hipErrorNotSupported;
+template <bool GU>
+__device__ __forceinline__ bool mrow_ok(int nt, int r, int I, int H) {
+  if constexpr (GU) return nt * 64 + (r & 63) < I;
+  else return nt * kTN + r < H;
+}
+
+template <int Q, bool GU>
+__device__ void mfma_tile(const MfmaArgs& A, int e, int n_e, int off_e, int m0, int nt, uint8_t* lds) {
+  constexpr int TAB = (1 << Q) * 2;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int H = A.H, I = A.I;
+  const int N = GU ? 2 * I : H;
+  const int K = GU ? H : I;
+  const int W = K >> 5;
+
+  uint8_t* tabs = lds;                                                      // kTN * TAB
+  _Float16* wt = reinterpret_cast<_Float16*>(lds + kTN * TAB);              // [kTN][kTileStride]
+  _Float16* xt = wt + kTN * kTileStride;                                    // [kTM][kTileStride]
+
+  const pw_block_desc d = A.blocks[2 * e + (GU ? 0 : 1)];
+  const uint32_t pstride = (uint32_t)N * (uint32_t)W * 4u;
+  const __amdgpu_buffer_rsrc_t prs = make_rsrc(uniform_ptr(d.planes), pstride * (uint32_t)Q);
+  const uint16_t* __restrict__ lut = uniform_ptr(d.lut_all) + lut_offset(N, Q);
+
+  // Row tables -> LDS (uint4 chunks; rows outside the block read as zero).
+  for (int c = tid; c < kTN * TAB / 16; c += kMfmaThreads) {
+    const int r = c / (TAB / 16), cc = c % (TAB / 16);
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (mrow_ok<GU>(nt, r, I, H))
+      v = *reinterpret_cast<const uint4*>(lut + (size_t)mrow<GU>(nt, r, I) * (1 << Q) + cc * 8);
+    *reinterpret_cast<uint4*>(tabs + c * 16) = v;
+  }
+
+  // This thread's decode job: row dr, word dw of the K step.
+  const int dr = tid >> 1, dw = tid & 1;
+  const bool dr_ok = mrow_ok<GU>(nt, dr, I, H);
+  const uint32_t drow = (uint32_t)mrow<GU>(nt, dr, I);
+  const uint32_t tab_base = lds_addr(tabs) + (uint32_t)(dr * TAB);
+
+  // This thread's activation job: token row xr, 16-element quarter xq of the K step.
+  const int xr = tid >> 1, xq = (tid & 1) * 32;
+  const uint16_t* xsrc = nullptr;
+  if (xr < n_e - m0) {
+    const int pos = off_e + m0 + xr;
+    xsrc = GU ? A.act + (size_t)(A.rt.perm[pos] / A.k) * H : A.act + (size_t)pos * I;
+  }
+
+  // Wave sub-tile: tokens [64 wm, +64); rows: gate_up -> gate [32 wn, +32) and
+  // up [64 + 32 wn, +32); down -> [64 wn, +64).
+  const int wm = wave >> 1, wn = wave & 1;
+  int ncol[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ncol[j] = GU ? ((j < 2 ? 0 : 64) + 32 * wn + 16 * (j & 1)) : (64 * wn + 16 * j);
+
+  float4v acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  __syncthreads();
+
+  for (int k0 = 0; k0 < K; k0 += kTK) {
+    // 1. decode 32 weights of row dr into the weight tile
+    {
+      const int wc = (k0 >> 5) + dw;
+      const uint32_t voff = (dr_ok && wc < W) ? (drow * (uint32_t)W + (uint32_t)wc) * 4u : kOutOfRange;
+      uint32_t P[Q];
+#pragma unroll
+      for (int p = 0; p < Q; ++p) P[p] = buf_load_u32(prs, voff, (uint32_t)p * pstride);
+      uint4 xv[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        xv[v] = make_uint4(0u, 0u, 0u, 0u);
+        if (xsrc != nullptr && k0 + xq + 8 * v < K) xv[v] = *reinterpret_cast<const uint4*>(xsrc + k0 + xq + 8 * v);
+      }
+      uint32_t R[8];
+      planes_to_fields<Q>(P, R);
+      uint32_t packed[16];
+      GroupDecode<Q, 0>::run(R, tab_base, packed);
+      uint4* dst = reinterpret_cast<uint4*>(wt + dr * kTileStride + dw * 32);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        dst[v] = make_uint4(packed[4 * v], packed[4 * v + 1], packed[4 * v + 2], packed[4 * v + 3]);
+      uint4* xdst = reinterpret_cast<uint4*>(xt + xr * kTileStride + xq);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) xdst[v] = xv[v];
+    }
+    __syncthreads();
+
+    // 2. matrix cores: 4 x 4 tiles of 16 x 16, two K halves of 32
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      half8v af[4], bf[4];
+      const int kk = kh * 32 + 8 * (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const half8v*>(xt + (64 * wm + 16 * i + (lane & 15)) * kTileStride + kk);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bf[j] = *reinterpret_cast<const half8v*>(wt + (ncol[j] + (lane & 15)) * kTileStride + kk);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  // Epilogue.  acc[i][j] element v: token 64 wm + 16 i + 4 (lane >> 4) + v,
+  // tile column ncol[j] + (lane & 15).
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = 64 * wm + 16 * i + 4 * (lane >> 4) + v;
+      if (m >= n_e - m0) continue;
+      const size_t pos = (size_t)(off_e + m0 + m);
+      if constexpr (GU) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int r = ncol[j] + (lane & 15);          // gate row (tile-local < 64)
+          if (!mrow_ok<GU>(nt, r, I, H)) continue;
+          const float g = acc[i][j][v], u = acc[i][j + 2][v];
+          const _Float16 hh = (_Float16)(silu_f32(g) * u);
+          A.hout[pos * I + nt * 64 + r] = __builtin_bit_cast(uint16_t, hh);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = ncol[j] + (lane & 15);
+          if (!mrow_ok<GU>(nt, r, I, H)) continue;
+          A.oout[pos * H + nt * kTN + r] = acc[i][j][v];
+        }
+      }
+    }
+  }
+}
+
+template <bool GU>
+__device__ void mfma_zero_tile(const MfmaArgs& A, int n_e, int off_e, int m0, int nt) {
+  for (int i = threadIdx.x; i < kTM * kTN; i += kMfmaThreads) {
+    const int m = i / kTN, r = i % kTN;
+    if (m >= n_e - m0) continue;
+    const size_t pos = (size_t)(off_e + m0 + m);
+    if constexpr (GU) {
+      if (r < 64 && mrow_ok<GU>(nt, r, A.I, A.H)) A.hout[pos * A.I + nt * 64 + r] = 0;
+    } else {
+      if (mrow_ok<GU>(nt, r, A.I, A.H)) A.oout[pos * A.H + nt * kTN + r] = 0.0f;
+    }
+  }
+  if (threadIdx.x == 0 && nt == 0 && m0 == 0) raise_status(A.rt.status, PW_DEV_BAD_BITWIDTH);
+}
+
+constexpr int kMfmaLds = kTN * (1 << kMaxBits) * 2 + (kTN + kTM) * kTileStride * 2;
+
+template <bool GU>
+__global__ __launch_bounds__(kMfmaThreads) void mfma_kernel(MfmaArgs A) {
+  __shared__ __align__(16) uint8_t lds[kMfmaLds];
+  // deal items so that one XCD works through consecutive items
+  const int per_xcd = A.grid / kXcds;
+  const int item = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  const int mi = item / A.ntiles;
+  const int nt = item % A.ntiles;
+  if (mi >= uniform(*A.rt.num_mtiles)) return;
+  const int e = uniform(A.rt.mtiles[2 * mi]);
+  const int m0 = uniform(A.rt.mtiles[2 * mi + 1]);
+  const int n_e = uniform(A.rt.counts[e]);
+  const int off_e = uniform(A.rt.offsets[e]);
+  switch (uniform(A.q[2 * e + (GU ? 0 : 1)])) {
+    case 3: mfma_tile<3, GU>(A, e, n_e, off_e, m0, nt, lds); break;
+    case 4: mfma_tile<4, GU>(A, e, n_e, off_e, m0, nt, lds); break;
+    case 5: mfma_tile<5, GU>(A, e, n_e, off_e, m0, nt, lds); break;
+    case 6: mfma_tile<6, GU>(A, e, n_e, off_e, m0, nt, lds); break;
+    case 7: mfma_tile<7, GU>(A, e, n_e, off_e, m0, nt, lds); break;
+    case 8: mfma_tile<8, GU>(A, e, n_e, off_e, m0, nt, lds); break;
+    default: mfma_zero_tile<GU>(A, n_e, off_e, m0, nt); break;
+  }
+}
+
+template <bool GU>
+static hipError_t launch_mfma(const ExpertArgs& a, const uint16_t* act, uint16_t* h, float* o, hipStream_t s) {
+  MfmaArgs A{};
+  A.H = a.H; A.I = a.I; A.E = a.E; A.k = a.k; A.T = a.T;
+  A.blocks = a.blocks; A.q = a.q; A.rt = a.rt;
+  A.act = act; A.hout = h; A.oout = o;
+  A.ntiles = GU ? (a.I + 63) / 64 : (a.H + kTN - 1) / kTN;
+  const long long items = (long long)mtile_bound(a.E, a.T, a.k) * A.ntiles;
+  const long long grid = (items + kXcds - 1) / kXcds * kXcds;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  A.grid = (int)grid;
+  hipLaunchKernelGGL(mfma_kernel<GU>, dim3((unsigned)grid), dim3(kMfmaThreads), 0, s, A);
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma_gate_up(const ExpertArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s) {
+  return launch_mfma<true>(a, x, h, nullptr, s);
+}
+
+hipError_t launch_mfma_down(const ExpertArgs& a, const uint16_t* h, float* o, hipStream_t s) {
+  return launch_mfma<false>(a, h, nullptr, o, s);
 }
 
 }  // namespace pw

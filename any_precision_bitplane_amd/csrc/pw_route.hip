@@ -20,7 +20,7 @@ constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / kWave;
 
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __restrict__ ids, int T, int k,
-                                                              int E, Route rt) {
+                                                              int E, int mfma_min_tokens, Route rt) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int off[kMaxExperts + 1];
   __shared__ int base[kMaxExperts];
@@ -56,6 +56,17 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
     off[E] = acc;
     *rt.num_active = na;
     rt.offsets[E] = acc;
+    // token tiles of the experts that take the MFMA kernels, in expert order
+    int nm = 0;
+    for (int e = 0; e < E; ++e) {
+      if (cnt[e] < mfma_min_tokens || cnt[e] == 0) continue;
+      for (int m0 = 0; m0 < cnt[e]; m0 += kMfmaTileM) {
+        rt.mtiles[2 * nm] = e;
+        rt.mtiles[2 * nm + 1] = m0;
+        ++nm;
+      }
+    }
+    *rt.num_mtiles = nm;
   }
   __syncthreads();
   for (int e = tid; e < E; e += kRouteThreads) {
@@ -111,8 +122,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
   }
 }
 
-hipError_t launch_route(const int32_t* ids, int T, int k, int E, const Route& rt, hipStream_t s) {
-  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, s, ids, T, k, E, rt);
+hipError_t launch_route(const int32_t* ids, int T, int k, int E, int mfma_min_tokens, const Route& rt,
+                        hipStream_t s) {
+  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, s, ids, T, k, E, mfma_min_tokens, rt);
   return hipGetLastError();
 }
 

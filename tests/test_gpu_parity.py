@@ -275,3 +275,54 @@ def test_duplicate_ids_are_summed(torch):
     dev.forward()
     torch.cuda.synchronize()
     compare(dev.y.float().cpu().numpy(), oracle_y(L, ids=ids), "duplicate ids")
+
+
+# ---------------------------------------------------------------------------
+# MFMA (dequant-to-LDS) path and the per-expert path choice
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,T", [("tiny", None), ("qwen_decode", None), ("mixtral_decode", 64)])
+def test_forward_mfma_forced(torch, name, T):
+    L = layer_for(name, T=T)
+    say(f"forward {name} T={L.wl.T} path=MFMA")
+    _, y = run_forward(torch, L, B.PW_PATH_MFMA)
+    compare(y, oracle_y(L), f"{name} mfma")
+
+
+def test_forward_mfma_ragged_shapes(torch):
+    for (H, I, E, k, T, seed) in [(2080, 96, 5, 3, 70, 41), (96, 1056, 4, 4, 45, 42), (256, 512, 2, 1, 300, 43)]:
+        L = custom_layer(H, I, E, k, T, seed)
+        say(f"forward mfma ragged H={H} I={I} E={E} k={k} T={T}")
+        _, y = run_forward(torch, L, B.PW_PATH_MFMA)
+        compare(y, oracle_y(L), f"mfma ragged H={H} I={I}")
+
+
+def test_forward_qwen_batched_auto_mixes_paths(torch):
+    """Zipf routing: hot experts (many tokens, 8 bits) on the MFMA kernels, the
+    rest on the GEMV kernels, in one call."""
+    L = layer_for("qwen_batched")
+    counts = np.bincount(L.ids.reshape(-1), minlength=L.wl.E)
+    assert counts.max() >= 16 and counts[counts > 0].min() < 16
+    say("forward qwen_batched T=256 AUTO")
+    _, y = run_forward(torch, L, B.PW_PATH_AUTO, mfma_min_tokens=16)
+    ref = oracle_y(L)
+    compare(y, ref, "qwen_batched auto")
+    say("forward qwen_batched T=256 GEMV")
+    _, y2 = run_forward(torch, L, B.PW_PATH_GEMV)
+    compare(y2, ref, "qwen_batched gemv")
+
+
+def test_forward_mixtral_prefill_sampled(torch):
+    """Full-size prefill call (T=4096, skewed bitwidths, all experts on MFMA);
+    the oracle checks a sample of tokens one by one."""
+    L = layer_for("mixtral_prefill", routed_only=False)
+    say("forward mixtral_prefill T=4096 AUTO")
+    _, y = run_forward(torch, L, B.PW_PATH_AUTO)
+    assert np.all(np.isfinite(y))
+    # tokens whose two experts lie in a small subset keep the oracle's work bounded
+    rng = np.random.default_rng(5)
+    subset = {0, 1, 2}
+    cand = [t for t in range(L.wl.T) if set(int(e) for e in L.ids[t]) <= subset]
+    toks = sorted(rng.choice(cand, size=min(12, len(cand)), replace=False).tolist()) + [0, L.wl.T - 1]
+    toks = sorted(set(toks))
+    ref = oracle_y(L, tokens=toks)
+    compare(y[toks], ref, f"mixtral_prefill sampled tokens {toks}")
