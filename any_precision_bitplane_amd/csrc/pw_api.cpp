@@ -97,9 +97,13 @@ pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T, const uint16_t* x
   if (path == PW_PATH_GEMV) thresh = INT_MAX;
   else if (path == PW_PATH_MFMA) thresh = 0;
   else thresh = (opts && opts->mfma_min_tokens > 0) ? opts->mfma_min_tokens : kDefaultMfmaMinTokens;
-  const int max_slots = T * k;               // upper bound of any expert's token count
+  const int max_slots = T * k;
+  // An expert gets at most T tokens unless a token lists it twice; the MFMA
+  // family is launched only when some expert can reach the threshold that way.
+  // The GEMV family handles every expert the MFMA family does not.
+  const bool use_mfma = thresh <= T;
   const bool use_gemv = thresh > 0;
-  const bool use_mfma = thresh <= max_slots;
+  if (!use_mfma) thresh = INT_MAX;
 
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   Route rt;

@@ -55,6 +55,30 @@ class HipEvents:
         return float(out.value)
 
 
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary for this workload, if that summary was taken on the current kernel
+    source (its recorded source hash matches); otherwise None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_gemv_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for f in ("any_precision_bitplane_amd/csrc/pw_gemv.hip", "any_precision_bitplane_amd/csrc/pw_device.h"):
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    fields = {}
+    for line in open(path):
+        if line.startswith("source_sha256_16:"):
+            fields["sha"] = line.split(":", 1)[1].strip()
+        elif line.startswith(kernel + ":"):
+            for tok in line.split()[1:]:
+                k, v = tok.split("=")
+                fields[k] = float(v)
+    if fields.get("sha") != h.hexdigest()[:16] or "traffic_bytes_per_launch" not in fields:
+        return None
+    return fields["traffic_bytes_per_launch"]
+
+
 def cpu_baseline(layer, budget_s: float):
     """The oracle as it stands, on the host cores, over a bounded sample: whole
     layer calls on the same workload, repeated until the budget is spent."""
@@ -89,6 +113,8 @@ def main():
     ap.add_argument("--path", type=int, default=0, help="0 auto, 1 GEMV, 2 MFMA")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many bytes (counter calibration)")
     ap.add_argument("--uniform-q", type=int, default=0,
                     help="commit one bitwidth for every block (mixed-vs-uniform comparison)")
     args = ap.parse_args()
@@ -99,6 +125,16 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_bytes:
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(max(args.steps, 1)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes, "copies": max(args.steps, 1)}))
+        return
     from any_precision_bitplane_amd import binding as B
     from any_precision_bitplane_amd import roofline as RL
     from any_precision_bitplane_amd import synth
@@ -214,7 +250,7 @@ def main():
             "peak": RL.HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / RL.HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(dom, args.workload) if not (args.uniform_q or args.T) else None,
             "algorithmic_bytes_per_launch": dom_bytes,
             "avg_launch_ms": dom_ms,
         },
