@@ -16,7 +16,7 @@ constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-constexpr int kMfmaTileM = 128;   // tokens per MFMA tile
+constexpr int kMfmaTileM = 256;   // tokens per MFMA tile
 
 inline int mtile_bound(int E, int T, int k) {
   const int slots = T * k;

@@ -5,25 +5,30 @@
 // GEMV, because with hundreds of tokens per expert the product is a dense
 // contraction.
 //
-// Tile: 128 tokens x 128 weight rows, K step 64.  Per K step every thread of
-// the 4-wave workgroup decodes one 32-weight group (the first q plane words of
-// one row) through the row's table in LDS into an fp16 weight tile, and loads
-// 64 bytes of the gathered activation tile; then each wave multiplies a 64 x 64
-// sub-tile with v_mfma_f32_16x16x32_f16 (fp32 accumulation).  gate_up tiles take
-// 64 gate rows and the matching 64 up rows, and each wave holds matching gate
-// and up columns, so SwiGLU runs on the accumulators and h leaves as fp16.
+// Tile: 256 tokens x 128 weight rows per 8-wave workgroup, K step 64.
+//   * waves 0-3 decode: each thread turns one 32-weight group (the first q
+//     plane words of one row) into fp16 through the row's table in LDS and
+//     writes it to a double-buffered weight tile;
+//   * all waves stage the gathered activation tile (half a token row each);
+//   * every wave multiplies a 64 x 64 sub-tile with v_mfma_f32_16x16x32_f16
+//     (fp32 accumulation in AGPRs).
+// Plane words are prefetched into registers two K steps ahead and
+// activations one step ahead, and the decode of step k+1 is issued while the
+// matrix cores work on step k.  gate_up tiles take 64 gate rows and the matching 64 up rows; each
+// wave holds matching gate and up columns, so SwiGLU runs on the accumulators
+// and h leaves as fp16.
 //
 // Work items are (token tile, row tile) pairs; token tiles come from the route
 // kernel's list.  Consecutive items on one XCD (workgroups are dealt to the 8
 // XCDs round-robin) sweep the row tiles of one token tile, so the activation
-// tile stays in that XCD's L2.
+// rows stay in that XCD's L2.
 #include "pw_device.h"
 #include "pw_internal.h"
 
 namespace pw {
 
-constexpr int kMfmaThreads = 256;
-constexpr int kTM = kMfmaTileM;        // 128 tokens
+constexpr int kMfmaThreads = 512;
+constexpr int kTM = kMfmaTileM;        // 256 tokens
 constexpr int kTN = 128;               // weight rows
 constexpr int kTK = 64;                // reduction step
 constexpr int kTileStride = kTK + 8;   // fp16 elements per LDS tile row (padding against bank conflicts)
@@ -57,6 +62,11 @@ __device__ __forceinline__ bool mrow_ok(int nt, int r, int I, int H) {
   else return nt * kTN + r < H;
 }
 
+constexpr int kLdsTabs = kTN * (1 << kMaxBits) * 2;              // 64 KB
+constexpr int kLdsW = kTN * kTileStride * 2;                     // one weight tile
+constexpr int kLdsX = kTM * kTileStride * 2;                     // activation tile
+constexpr int kMfmaLds = kLdsTabs + 2 * kLdsW + kLdsX;
+
 template <int Q, bool GU>
 __device__ void mfma_tile(const MfmaArgs& A, int e, int n_e, int off_e, int m0, int nt, uint8_t* lds) {
   constexpr int TAB = (1 << Q) * 2;
@@ -67,10 +77,13 @@ __device__ void mfma_tile(const MfmaArgs& A, int e, int n_e, int off_e, int m0, 
   const int N = GU ? 2 * I : H;
   const int K = GU ? H : I;
   const int W = K >> 5;
+  const int nk = (K + kTK - 1) / kTK;
+  const bool decoder = wave < 4;
 
-  uint8_t* tabs = lds;                                                      // kTN * TAB
-  _Float16* wt = reinterpret_cast<_Float16*>(lds + kTN * TAB);              // [kTN][kTileStride]
-  _Float16* xt = wt + kTN * kTileStride;                                    // [kTM][kTileStride]
+  uint8_t* tabs = lds;
+  _Float16* wt0 = reinterpret_cast<_Float16*>(lds + kLdsTabs);
+  _Float16* wt1 = wt0 + kTN * kTileStride;
+  _Float16* xt = wt1 + kTN * kTileStride;
 
   const pw_block_desc d = A.blocks[2 * e + (GU ? 0 : 1)];
   const uint32_t pstride = (uint32_t)N * (uint32_t)W * 4u;
@@ -86,23 +99,59 @@ __device__ void mfma_tile(const MfmaArgs& A, int e, int n_e, int off_e, int m0, 
     *reinterpret_cast<uint4*>(tabs + c * 16) = v;
   }
 
-  // This thread's decode job: row dr, word dw of the K step.
-  const int dr = tid >> 1, dw = tid & 1;
+  // Decode job (waves 0-3): row dr, word dw of each K step.
+  const int dr = (tid & 255) >> 1, dw = tid & 1;
   const bool dr_ok = mrow_ok<GU>(nt, dr, I, H);
   const uint32_t drow = (uint32_t)mrow<GU>(nt, dr, I);
   const uint32_t tab_base = lds_addr(tabs) + (uint32_t)(dr * TAB);
-
-  // This thread's activation job: token row xr, 16-element quarter xq of the K step.
-  const int xr = tid >> 1, xq = (tid & 1) * 32;
+  // Activation job (all waves): token row xr, columns [32 xh, +32) of each K step.
+  const int xr = tid >> 1, xh = tid & 1;
   const uint16_t* xsrc = nullptr;
   if (xr < n_e - m0) {
     const int pos = off_e + m0 + xr;
     xsrc = GU ? A.act + (size_t)(A.rt.perm[pos] / A.k) * H : A.act + (size_t)pos * I;
   }
 
+  uint32_t Pa[Q], Pb[Q];
+  uint4 X[4];
+
+  // plane words of a K step (decoders), two steps ahead
+  auto prefetch_planes = [&](uint32_t (&P)[Q], int step) {
+    if (step >= nk || !decoder) return;
+    const int wc = ((step * kTK) >> 5) + dw;
+    const uint32_t voff = (dr_ok && wc < W) ? (drow * (uint32_t)W + (uint32_t)wc) * 4u : kOutOfRange;
+#pragma unroll
+    for (int p = 0; p < Q; ++p) P[p] = buf_load_u32(prs, voff, (uint32_t)p * pstride);
+  };
+  // activations of a K step (everyone), one step ahead (they hit L2)
+  auto prefetch_x = [&](int step) {
+    if (step >= nk) return;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int c = step * kTK + 32 * xh + 8 * v;
+      X[v] = make_uint4(0u, 0u, 0u, 0u);
+      if (xsrc != nullptr && c < K) X[v] = *reinterpret_cast<const uint4*>(xsrc + c);
+    }
+  };
+  auto decode = [&](uint32_t (&P)[Q], _Float16* wt) {
+    uint32_t R[8];
+    planes_to_fields<Q>(P, R);
+    uint32_t packed[16];
+    GroupDecode<Q, 0>::run(R, tab_base, packed);
+    uint4* dst = reinterpret_cast<uint4*>(wt + dr * kTileStride + dw * 32);
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      dst[v] = make_uint4(packed[4 * v], packed[4 * v + 1], packed[4 * v + 2], packed[4 * v + 3]);
+  };
+  auto stage_x = [&]() {
+    uint4* dst = reinterpret_cast<uint4*>(xt + xr * kTileStride + 32 * xh);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) dst[v] = X[v];
+  };
+
   // Wave sub-tile: tokens [64 wm, +64); rows: gate_up -> gate [32 wn, +32) and
   // up [64 + 32 wn, +32); down -> [64 wn, +64).
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave & 3, wn = wave >> 2;
   int ncol[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) ncol[j] = GU ? ((j < 2 ? 0 : 64) + 32 * wn + 16 * (j & 1)) : (64 * wn + 16 * j);
@@ -113,39 +162,10 @@ __device__ void mfma_tile(const MfmaArgs& A, int e, int n_e, int off_e, int m0, 
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
 
-  __syncthreads();
-
-  for (int k0 = 0; k0 < K; k0 += kTK) {
-    // 1. decode 32 weights of row dr into the weight tile
-    {
-      const int wc = (k0 >> 5) + dw;
-      const uint32_t voff = (dr_ok && wc < W) ? (drow * (uint32_t)W + (uint32_t)wc) * 4u : kOutOfRange;
-      uint32_t P[Q];
-#pragma unroll
-      for (int p = 0; p < Q; ++p) P[p] = buf_load_u32(prs, voff, (uint32_t)p * pstride);
-      uint4 xv[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        xv[v] = make_uint4(0u, 0u, 0u, 0u);
-        if (xsrc != nullptr && k0 + xq + 8 * v < K) xv[v] = *reinterpret_cast<const uint4*>(xsrc + k0 + xq + 8 * v);
-      }
-      uint32_t R[8];
-      planes_to_fields<Q>(P, R);
-      uint32_t packed[16];
-      GroupDecode<Q, 0>::run(R, tab_base, packed);
-      uint4* dst = reinterpret_cast<uint4*>(wt + dr * kTileStride + dw * 32);
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        dst[v] = make_uint4(packed[4 * v], packed[4 * v + 1], packed[4 * v + 2], packed[4 * v + 3]);
-      uint4* xdst = reinterpret_cast<uint4*>(xt + xr * kTileStride + xq);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) xdst[v] = xv[v];
-    }
-    __syncthreads();
-
-    // 2. matrix cores: 4 x 4 tiles of 16 x 16, two K halves of 32
+  auto mma = [&](const _Float16* wt) {
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
+      __builtin_amdgcn_sched_barrier(0);   // keep the two K halves' fragments from being live together
       half8v af[4], bf[4];
       const int kk = kh * 32 + 8 * (lane >> 4);
 #pragma unroll
@@ -158,6 +178,47 @@ __device__ void mfma_tile(const MfmaArgs& A, int e, int n_e, int off_e, int m0, 
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // Prologue: planes of steps 0 and 1 and activations of step 0 in flight;
+  // stage step 0; activations of step 1 in flight.
+  prefetch_planes(Pa, 0);
+  prefetch_planes(Pb, 1);
+  prefetch_x(0);
+  __syncthreads();                        // tables in LDS
+  if (decoder) decode(Pa, wt0);
+  stage_x();
+  prefetch_planes(Pa, 2);
+  prefetch_x(1);
+  __syncthreads();
+
+  // Step k: matrix cores on (xt, wt[k&1]); meanwhile decode step k+1 into the
+  // other weight buffer; then stage the activations of step k+1.
+  for (int k = 0; k < nk; k += 2) {
+    // even step k: weights in wt0; planes of step k+1 in Pb
+    mma(wt0);
+    if (k + 1 < nk && decoder) {
+      decode(Pb, wt1);
+      prefetch_planes(Pb, k + 3);
+    }
+    __syncthreads();
+    if (k + 1 < nk) {
+      stage_x();
+      prefetch_x(k + 2);
+    }
+    __syncthreads();
+    if (k + 1 >= nk) break;
+    // odd step k+1: weights in wt1; planes of step k+2 in Pa
+    mma(wt1);
+    if (k + 2 < nk && decoder) {
+      decode(Pa, wt0);
+      prefetch_planes(Pa, k + 4);
+    }
+    __syncthreads();
+    if (k + 2 < nk) {
+      stage_x();
+      prefetch_x(k + 3);
     }
     __syncthreads();
   }
@@ -206,8 +267,6 @@ __device__ void mfma_zero_tile(const MfmaArgs& A, int n_e, int off_e, int m0, in
   }
   if (threadIdx.x == 0 && nt == 0 && m0 == 0) raise_status(A.rt.status, PW_DEV_BAD_BITWIDTH);
 }
-
-constexpr int kMfmaLds = kTN * (1 << kMaxBits) * 2 + (kTN + kTM) * kTileStride * 2;
 
 template <bool GU>
 __global__ __launch_bounds__(kMfmaThreads) void mfma_kernel(MfmaArgs A) {
