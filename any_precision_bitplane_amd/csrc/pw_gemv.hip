@@ -62,16 +62,19 @@ constexpr int kDppRor8 = 0x128;         // lane i <- (i+8) mod 16 inside 16-lane
 // (upper), where ' is the partner lane l ^ 32.  v_permlane32_swap exchanges the
 // upper half of its first operand with the lower half of its second; the
 // instruction is written out because the compiler builtin returns the second
-// operand's new value incorrectly.  The s_nop pads cover the VALU-to-permlane
-// hazard.
+// operand's new value incorrectly.  The compiler's hazard tracking does not
+// look inside inline assembly, so the pads are written out: a dot-product
+// result read by another VALU op needs three wait states (the accumulators
+// arrive here straight from v_dot2), an ordinary VALU result two; s_nop 3
+// gives four.  The trailing pad covers the permlane result feeding a VALU op.
 __device__ __forceinline__ float swap32_add(float a, float b) {
-  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  asm("s_nop 3\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
   return a + b;
 }
 // Same across 16-lane rows (odd rows of the first operand <-> even rows of the
 // second): lanes with bit 4 clear keep a's pair sum, set keep b's.
 __device__ __forceinline__ float swap16_add(float a, float b) {
-  asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  asm("s_nop 3\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
   return a + b;
 }
 

@@ -68,7 +68,7 @@ constexpr int kLdsX = kTM * kTileStride * 2;                     // activation t
 constexpr int kMfmaLds = kLdsTabs + 2 * kLdsW + kLdsX;
 
 template <int Q, bool GU>
-__device__ void mfma_tile(const MfmaArgs& A, int e, int n_e, int off_e, int m0, int nt, uint8_t* lds) {
+__device__ __forceinline__ void mfma_tile(const MfmaArgs& A, int e, int n_e, int off_e, int m0, int nt, uint8_t* lds) {
   constexpr int TAB = (1 << Q) * 2;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -254,7 +254,7 @@ __device__ void mfma_tile(const MfmaArgs& A, int e, int n_e, int off_e, int m0, 
 }
 
 template <bool GU>
-__device__ void mfma_zero_tile(const MfmaArgs& A, int n_e, int off_e, int m0, int nt) {
+__device__ __forceinline__ void mfma_zero_tile(const MfmaArgs& A, int n_e, int off_e, int m0, int nt) {
   for (int i = threadIdx.x; i < kTM * kTN; i += kMfmaThreads) {
     const int m = i / kTN, r = i % kTN;
     if (m >= n_e - m0) continue;

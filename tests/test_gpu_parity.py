@@ -154,6 +154,20 @@ def test_forward_ragged_shapes(torch):
         compare(y, oracle_y(L), f"ragged H={H} I={I}")
 
 
+@pytest.mark.parametrize("H,I,E,k,T,seed", [(2048, 704, 36, 6, 6, 35), (512, 256, 96, 8, 12, 36)])
+def test_forward_one_token_per_expert_every_bitwidth_pair(torch, H, I, E, k, T, seed):
+    # Every expert takes exactly one token, and the experts' (gate_up, down)
+    # bitwidths run over all 36 pairs of 3..8: the single-token decode at
+    # every Q, in both products.  S = T*k = 36 routes inside the gate_up
+    # kernel; S = 96 goes through the route kernel.
+    qvals = [(3 + e % 6, 3 + (e // 6) % 6) for e in range(E)]
+    L = custom_layer(H, I, E, k, T, seed, qvals=qvals)
+    L.ids[:] = np.arange(T * k, dtype=np.int32).reshape(T, k) % E
+    say(f"forward one token per expert H={H} I={I} E={E} k={k} T={T}")
+    _, y = run_forward(torch, L, B.PW_PATH_GEMV)
+    compare(y, oracle_y(L), f"one token per expert E={E}")
+
+
 def test_forward_many_tokens_per_expert_gemv(torch):
     # experts with 3..40 tokens take several token groups on the GEMV path
     L = custom_layer(256, 512, 4, 2, 40, 34)
