@@ -169,23 +169,6 @@ __device__ __forceinline__ half2_t lookup_pair(const uint32_t (&R)[8], uint32_t 
   return __builtin_bit_cast(half2_t, lo | (hi << 16));
 }
 
-// Decode + dot of one row's 32-weight group against NT tokens' activations:
-// acc[t] += sum_j W[j] * x[t][j], one fp16 pair at a time (J = 0, 2, ..., 30).
-template <int Q, int NT, int J>
-struct GroupDot {
-  __device__ static __forceinline__ void run(const uint32_t (&R)[8], uint32_t base, const half2_t (&xr)[NT][16],
-                                             float* acc) {
-    const half2_t w2 = lookup_pair<Q, J>(R, base);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_fdot2(w2, xr[t][J >> 1], acc[t], false);
-    GroupDot<Q, NT, J + 2>::run(R, base, xr, acc);
-  }
-};
-template <int Q, int NT>
-struct GroupDot<Q, NT, 32> {
-  __device__ static __forceinline__ void run(const uint32_t (&)[8], uint32_t, const half2_t (&)[NT][16], float*) {}
-};
-
 // Decode of one row's 32-weight group into 16 fp16 pairs.
 template <int Q, int J>
 struct GroupDecode {

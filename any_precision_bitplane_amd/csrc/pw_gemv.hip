@@ -12,8 +12,9 @@
 //     0..q-1 are read (buffer loads; the plane offset is a scalar operand);
 //   * a lane's 32 activations per token stay in registers for a whole slice;
 //   * all lanes look up the same row's table, which keeps the LDS gather free
-//     of bank conflicts up to 64 entries, and the table address is an
-//     instruction immediate;
+//     of bank conflicts up to 64 entries; the row tables sit at 256-byte
+//     strides, so an entry's address is one byte permute of the table base
+//     and the code field, and the lookups go out in batches;
 //   * row groups are double-buffered: the planes of the next group are in
 //     flight while the current one is decoded.
 // gate_up chunks hold 8 gate rows and the matching 8 up rows (i and I + i), so
@@ -138,6 +139,58 @@ __device__ __forceinline__ int wave_excl_scan(int v) {
     if (lane >= o) s += t;
   }
   return s - v;
+}
+
+// ---------------------------------------------------------------------------
+// Table lookups of one row
+//
+// The GEMV kernels keep each row table at a 256-byte (q <= 7) or 512-byte
+// (q = 8) stride in LDS.  For q <= 7 the field byte is 2*code, so an entry's
+// address is the table base with its low byte replaced by the field: one
+// v_perm_b32.  For q = 8 the field is the code and the address is
+// base + 2*code.
+// ---------------------------------------------------------------------------
+template <int Q>
+constexpr int kTabStride = Q == 8 ? 512 : 256;
+
+template <int Q>
+__device__ __forceinline__ uint32_t row_entry(const uint32_t (&R)[8], uint32_t base, int j) {
+  const uint32_t f = R[j & 7];
+  const int b = j >> 3;
+  if constexpr (Q == 8) return base + (((f >> (8 * b)) & 0xFFu) << 1);
+  else return __builtin_amdgcn_perm(base, f, 0x07060500u | (uint32_t)b);
+}
+
+// acc[t] += sum_j W[j] * x[t][j] over the row's 32 weights.  The 32 lookups
+// go out in batches of eight, two batches ahead of the arithmetic that
+// consumes them, so the wave waits on LDS about once per batch.
+template <int Q, int NT>
+__device__ __forceinline__ void row_dot(const uint32_t (&R)[8], uint32_t base, const half2_t (&xr)[NT][16],
+                                        float* acc) {
+  constexpr int kBatch = 8;
+  constexpr int kAddrOps = Q == 8 ? 2 : 1;
+  constexpr int kUseOps = (kBatch / 2) * (1 + NT);
+  uint32_t v[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) v[j] = lds_u16_at(row_entry<Q>(R, base, j));
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    const half2_t w2 = __builtin_bit_cast(half2_t, v[2 * p] | (v[2 * p + 1] << 16));
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_fdot2(w2, xr[t][p], acc[t], false);
+  }
+  constexpr int kValu = 0x002, kDsRead = 0x100;
+  __builtin_amdgcn_sched_group_barrier(kValu, kBatch * kAddrOps, 0);
+  __builtin_amdgcn_sched_group_barrier(kDsRead, kBatch, 0);
+  __builtin_amdgcn_sched_group_barrier(kValu, kBatch * kAddrOps, 0);
+  __builtin_amdgcn_sched_group_barrier(kDsRead, kBatch, 0);
+#pragma unroll
+  for (int i = 2; i < 32 / kBatch; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kValu, kUseOps, 0);
+    __builtin_amdgcn_sched_group_barrier(kValu, kBatch * kAddrOps, 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, kBatch, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kValu, 2 * kUseOps, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -276,6 +329,7 @@ __device__ void chunk_body(const GemvArgs& A, const Slots& sl, int chunk, int kp
   constexpr int G = 4;                         // rows per pipeline group
   constexpr int NGR = kChunkRows / G;          // groups per slice
   constexpr int TAB = (1 << Q) * 2;            // bytes per row table
+  constexpr int TSTRIDE = kTabStride<Q>;       // LDS bytes between row tables
   constexpr int M = G * NT;                    // values reduced per group
   constexpr int MSH = 6 - (M == 1 ? 0 : M == 2 ? 1 : M == 4 ? 2 : M == 8 ? 3 : 4);
   const int lane = threadIdx.x;
@@ -295,11 +349,14 @@ __device__ void chunk_body(const GemvArgs& A, const Slots& sl, int chunk, int kp
 #pragma unroll
     for (int sp = 0; sp < (GU ? 2 : 1); ++sp) {
       const uint16_t* src = lut + (size_t)chunk_row<GU>(chunk, sp * SPAN_ROWS, I) * (1 << Q);
-      uint8_t* dst = tabs + sp * SPAN_ROWS * TAB;
+      uint8_t* dst = tabs + sp * SPAN_ROWS * TSTRIDE;
+      constexpr int CPR = TAB / 16;            // 16-byte pieces per row table
 #pragma unroll
       for (int c0 = 0; c0 < SPAN_CH; c0 += kWave) {
         const int c = c0 + lane;
-        if (c < SPAN_CH) *reinterpret_cast<uint4*>(dst + c * 16) = *reinterpret_cast<const uint4*>(src + c * 8);
+        if (c < SPAN_CH)
+          *reinterpret_cast<uint4*>(dst + (c / CPR) * TSTRIDE + (c % CPR) * 16) =
+              *reinterpret_cast<const uint4*>(src + c * 8);
       }
     }
   }
@@ -372,7 +429,7 @@ __device__ void chunk_body(const GemvArgs& A, const Slots& sl, int chunk, int kp
         __builtin_amdgcn_sched_barrier(0);
         uint32_t R[8];
         planes_to_fields<Q>(P[r], R);
-        GroupDot<Q, NT, 0>::run(R, tab_base + (uint32_t)((g * G + r) * TAB), xr, &acc[r * NT]);
+        row_dot<Q, NT>(R, tab_base + (uint32_t)((g * G + r) * TSTRIDE), xr, &acc[r * NT]);
       }
       const float red = multi_reduce<M>(acc);
       // lane L = t * 16 + row takes value (row - g*G) * NT + t from lane vi << MSH
@@ -430,7 +487,7 @@ __device__ __forceinline__ void chunk_by_tokens(const GemvArgs& A, const Slots& 
 
 template <bool GU>
 __global__ __launch_bounds__(kWave) void gemv_kernel(GemvArgs A) {
-  __shared__ __align__(16) uint8_t tabs[kChunkRows * kMaxTabBytes];
+  __shared__ __align__(512) uint8_t tabs[kChunkRows * kMaxTabBytes];   // row tables at kTabStride<Q>
   __shared__ RouteLds L;
   const int per_expert = A.chunks * A.kparts;
   const int a = blockIdx.x / per_expert;
