@@ -4,10 +4,14 @@
 // the tables directly and runs every block at its own committed bitwidth q,
 // read from the device page table, so a commit never changes a launch argument.
 //
-// Work decomposition.  A workgroup is one wave; it owns a chunk of 16 rows of
-// one routed expert's block (and, for the down product of a small batch, one
-// part of the K range).  Its 64 lanes split a row's K/32 plane words (lane =
-// word column, slices of 64 words), so
+// Work decomposition.  A workgroup is one wave.  The grid is about as many
+// waves as stay resident together; once a wave knows how many experts are
+// routed, the grid splits evenly over the (expert, K part) segments and each
+// wave takes an even share of its segment's rows, at most one chunk (8 gate_up
+// row pairs with their up rows, or 16 down rows), so the waves carry about the
+// same work however many experts are routed.  The down product of a small
+// batch also splits K.  A wave's 64 lanes split a row's K/32 plane words
+// (lane = word column, slices of 64 words), so
 //   * each plane load is one 256-byte coalesced wave access and only planes
 //     0..q-1 are read (buffer loads; the plane offset is a scalar operand);
 //   * a lane's 32 activations per token stay in registers for a whole slice;
@@ -43,7 +47,6 @@ struct GemvArgs {
   const uint16_t* act;      // gate_up: x [T][H];  down: h [slots][I]
   uint16_t* hout;           // gate_up: h [slots][I]
   float* oout;              // down: o [kparts][slots][H]
-  int chunks;               // row chunks per block
   int kparts;               // parts of the K range (down)
 };
 
@@ -209,7 +212,7 @@ struct RouteLds {
 
 // Write the routing one wave computed in LDS to the workspace, in the same
 // form the route kernel produces (stable expert-sorted slot order).
-__device__ void publish_route(const GemvArgs& A, RouteLds& L, int id, bool valid, const int (&c)[4], int nzr,
+__device__ __forceinline__ void publish_route(const GemvArgs& A, RouteLds& L, int id, bool valid, const int (&c)[4], int nzr,
                               int run) {
   const int lane = threadIdx.x;
   const int S = A.T * A.k;
@@ -243,9 +246,28 @@ __device__ void publish_route(const GemvArgs& A, RouteLds& L, int id, bool valid
   }
 }
 
+// The grid splits evenly over the (routed expert, K part) segments; a wave's
+// segment index (>= n_act * kparts: no work).
+// Waves per segment: an even split of the grid, but no more than keeps a
+// wave's share at kTargetPairs gate_up pairs / kTargetRows down rows (a wave's
+// fixed costs, the routing and the table staging, need some rows to spread over).
+constexpr int kTargetPairs = 8;
+constexpr int kTargetRows = 8;
+template <bool GU>
+__device__ __forceinline__ int waves_per_segment(const GemvArgs& A, int n_act) {
+  const int rows = GU ? A.I : A.H;
+  const int target = GU ? kTargetPairs : kTargetRows;
+  return max(1, min((int)gridDim.x / (n_act * A.kparts), (rows + target - 1) / target));
+}
+
+template <bool GU>
+__device__ __forceinline__ int wave_segment(const GemvArgs& A, int n_act) {
+  return (int)blockIdx.x / waves_per_segment<GU>(A, n_act);
+}
+
 // Inline routing over S = T*k <= 64 slots, one slot per lane.  Returns false
 // when fewer than a+1 experts are routed.
-__device__ bool find_expert_inline(const GemvArgs& A, int a, Slots& sl, RouteLds& L) {
+__device__ __forceinline__ bool find_expert_inline(const GemvArgs& A, int& a, Slots& sl, RouteLds& L) {
   const int lane = threadIdx.x;
   const int S = A.T * A.k;
   const int id = lane < S ? A.ids[lane] : -1;
@@ -269,6 +291,7 @@ __device__ bool find_expert_inline(const GemvArgs& A, int a, Slots& sl, RouteLds
   int nzr = wave_excl_scan(nz);
   const int run_base = run, nzr_base = nzr;
   const int n_act = uniform(__shfl(nzr + nz, kWave - 1, kWave));
+  a = n_act > 0 ? wave_segment<true>(A, n_act) / A.kparts : 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int ex = 4 * lane + i;
@@ -293,9 +316,11 @@ __device__ bool find_expert_inline(const GemvArgs& A, int a, Slots& sl, RouteLds
   return true;
 }
 
-__device__ bool find_expert_routed(const GemvArgs& A, int a, Slots& sl) {
+template <bool GU>
+__device__ __forceinline__ bool find_expert_routed(const GemvArgs& A, int& a, Slots& sl) {
   const int n_act = uniform(*A.rt.num_active);
   sl.num_active = n_act;
+  a = n_act > 0 ? wave_segment<GU>(A, n_act) / A.kparts : 0;
   if (a >= n_act) return false;
   const int e = uniform(A.rt.active[a]);
   sl.e = e;
@@ -318,14 +343,28 @@ __device__ __forceinline__ int slot_of(const GemvArgs& A, const Slots& sl, int r
 // ---------------------------------------------------------------------------
 // One chunk of 16 rows at bitwidth Q for up to NT tokens at a time
 // ---------------------------------------------------------------------------
+// A chunk: gate_up pairs [first, first + n) (n <= 8; chunk row r < 8 is gate
+// row first + r, chunk row 8 + r the matching up row), or down rows
+// [first, first + n) (n <= 16) of K part kpart.  Chunk rows past n are masked.
+// Rows of one row group are consecutive rows of the block, so each plane load
+// of a group reads one contiguous 1 KB run (K = 2048).
+struct Chunk {
+  int first, n, kpart;
+};
+
 template <bool GU>
-__device__ __forceinline__ int chunk_row(int chunk, int r, int I) {
-  if constexpr (GU) return (r < 8 ? 0 : I) + chunk * 8 + (r & 7);
-  else return chunk * kChunkRows + r;
+__device__ __forceinline__ int chunk_row(const Chunk& ch, int r, int I) {
+  if constexpr (GU) return (r < 8 ? 0 : I) + ch.first + (r & 7);
+  else return ch.first + r;
+}
+
+template <bool GU>
+__device__ __forceinline__ bool chunk_row_valid(const Chunk& ch, int r) {
+  return GU ? (r & 7) < ch.n : r < ch.n;
 }
 
 template <int Q, int NT, bool GU>
-__device__ void chunk_body(const GemvArgs& A, const Slots& sl, int chunk, int kpart, uint8_t* tabs) {
+__device__ __forceinline__ void chunk_body(const GemvArgs& A, const Slots& sl, const Chunk& ch, uint8_t* tabs) {
   constexpr int G = 4;                         // rows per pipeline group
   constexpr int NGR = kChunkRows / G;          // groups per slice
   constexpr int TAB = (1 << Q) * 2;            // bytes per row table
@@ -348,14 +387,15 @@ __device__ void chunk_body(const GemvArgs& A, const Slots& sl, int chunk, int kp
     constexpr int SPAN_CH = SPAN_ROWS * TAB / 16;
 #pragma unroll
     for (int sp = 0; sp < (GU ? 2 : 1); ++sp) {
-      const uint16_t* src = lut + (size_t)chunk_row<GU>(chunk, sp * SPAN_ROWS, I) * (1 << Q);
-      uint8_t* dst = tabs + sp * SPAN_ROWS * TSTRIDE;
+      const uint16_t* src = lut + (size_t)((GU && sp ? I : 0) + ch.first) * (1 << Q);
       constexpr int CPR = TAB / 16;            // 16-byte pieces per row table
 #pragma unroll
       for (int c0 = 0; c0 < SPAN_CH; c0 += kWave) {
         const int c = c0 + lane;
-        if (c < SPAN_CH)
-          *reinterpret_cast<uint4*>(dst + (c / CPR) * TSTRIDE + (c % CPR) * 16) =
+        const int j = c / CPR;                 // row inside the span
+        const int pos = sp * SPAN_ROWS + j;
+        if (c < SPAN_CH && j < ch.n)
+          *reinterpret_cast<uint4*>(tabs + pos * TSTRIDE + (c % CPR) * 16) =
               *reinterpret_cast<const uint4*>(src + c * 8);
       }
     }
@@ -365,10 +405,12 @@ __device__ void chunk_body(const GemvArgs& A, const Slots& sl, int chunk, int kp
   const uint32_t tab_base = lds_addr(tabs);
   const int nsl = (W + kWave - 1) / kWave;
   const int spp = (nsl + A.kparts - 1) / A.kparts;
-  const int s_begin = kpart * spp;
+  const int s_begin = ch.kpart * spp;
   const int s_end = min(nsl, s_begin + spp);
   const int nsteps = max(0, s_end - s_begin) * NGR;
   const int slots = A.T * A.k;
+  // a row group with no row inside the chunk is neither loaded nor computed
+  auto group_live = [&](int g) { return chunk_row_valid<GU>(ch, g * G); };   // its first row
 
   for (int t0 = 0; t0 < sl.n_e; t0 += NT) {
     const int nt = min(NT, sl.n_e - t0);
@@ -390,11 +432,13 @@ __device__ void chunk_body(const GemvArgs& A, const Slots& sl, int chunk, int kp
     auto load_group = [&](uint32_t (&P)[G][Q], int st) {
       const int slice = s_begin + st / NGR;
       const int g = st % NGR;
+      if (!group_live(g)) return;
       const int wc = slice * kWave + lane;
 #pragma unroll
       for (int r = 0; r < G; ++r) {
-        const uint32_t voff =
-            wc < W ? ((uint32_t)chunk_row<GU>(chunk, g * G + r, I) * (uint32_t)W + (uint32_t)wc) * 4u : kOutOfRange;
+        const uint32_t voff = (wc < W && chunk_row_valid<GU>(ch, g * G + r))
+                                  ? ((uint32_t)chunk_row<GU>(ch, g * G + r, I) * (uint32_t)W + (uint32_t)wc) * 4u
+                                  : kOutOfRange;
 #pragma unroll
         for (int p = 0; p < Q; ++p) P[r][p] = buf_load_u32(prs, voff, (uint32_t)p * pstride);
       }
@@ -403,6 +447,7 @@ __device__ void chunk_body(const GemvArgs& A, const Slots& sl, int chunk, int kp
     auto compute_group = [&](uint32_t (&P)[G][Q], int st) {
       const int slice = s_begin + st / NGR;
       const int g = st % NGR;
+      if (!group_live(g)) return;
       if (slice != xslice) {
         xslice = slice;
         const int wc = slice * kWave + lane;
@@ -453,92 +498,130 @@ __device__ void chunk_body(const GemvArgs& A, const Slots& sl, int chunk, int kp
     if constexpr (GU) {
       // up row r + 8 sits 8 lanes above gate row r inside the same 16-lane row
       const float u = dpp_f<kDppRor8>(tot);
-      if (lane < 32 && r_l < 8 && t_l < nt) {
+      const int pair = r_l;
+      if (lane < 32 && r_l < 8 && pair < ch.n && t_l < nt) {
         const float h = silu_f32(tot) * u;
         const _Float16 hh = (_Float16)h;
-        A.hout[(size_t)(sl.off_e + t0 + t_l) * I + chunk * 8 + r_l] = __builtin_bit_cast(uint16_t, hh);
+        A.hout[(size_t)(sl.off_e + t0 + t_l) * I + ch.first + pair] = __builtin_bit_cast(uint16_t, hh);
       }
     } else {
-      if (lane < 32 && t_l < nt)
-        A.oout[((size_t)kpart * slots + sl.off_e + t0 + t_l) * H + chunk * kChunkRows + r_l] = tot;
+      if (lane < 32 && t_l < nt && r_l < ch.n)
+        A.oout[((size_t)ch.kpart * slots + sl.off_e + t0 + t_l) * H + ch.first + r_l] = tot;
     }
   }
 }
 
 // Rows of a block whose committed bitwidth is invalid read as zero.
 template <bool GU>
-__device__ void chunk_zero(const GemvArgs& A, const Slots& sl, int chunk, int kpart) {
+__device__ __forceinline__ void chunk_zero(const GemvArgs& A, const Slots& sl, const Chunk& ch) {
   const int lane = threadIdx.x;
   const int slots = A.T * A.k;
-  for (int i = lane; i < sl.n_e * (GU ? 8 : kChunkRows); i += kWave) {
-    const int t = i / (GU ? 8 : kChunkRows), r = i % (GU ? 8 : kChunkRows);
-    if constexpr (GU) A.hout[(size_t)(sl.off_e + t) * A.I + chunk * 8 + r] = 0;
-    else A.oout[((size_t)kpart * slots + sl.off_e + t) * A.H + chunk * kChunkRows + r] = 0.0f;
+  for (int i = lane; i < sl.n_e * ch.n; i += kWave) {
+    const int t = i / ch.n, r = i % ch.n;
+    if constexpr (GU) A.hout[(size_t)(sl.off_e + t) * A.I + ch.first + r] = 0;
+    else A.oout[((size_t)ch.kpart * slots + sl.off_e + t) * A.H + ch.first + r] = 0.0f;
   }
-  if (lane == 0 && chunk == 0 && kpart == 0) raise_status(A.rt.status, PW_DEV_BAD_BITWIDTH);
+  if (lane == 0 && ch.first == 0 && ch.kpart == 0) raise_status(A.rt.status, PW_DEV_BAD_BITWIDTH);
 }
 
 template <int Q, bool GU>
-__device__ __forceinline__ void chunk_by_tokens(const GemvArgs& A, const Slots& sl, int chunk, int kpart,
-                                                uint8_t* tabs) {
-  if (sl.n_e == 1) chunk_body<Q, 1, GU>(A, sl, chunk, kpart, tabs);
-  else chunk_body<Q, 2, GU>(A, sl, chunk, kpart, tabs);
+__device__ __forceinline__ void chunk_by_tokens(const GemvArgs& A, const Slots& sl, const Chunk& ch, uint8_t* tabs) {
+  if (sl.n_e == 1) chunk_body<Q, 1, GU>(A, sl, ch, tabs);
+  else chunk_body<Q, 2, GU>(A, sl, ch, tabs);
 }
 
+// The grid is at least as many one-wave workgroups as stay resident together,
+// and enough that every wave's share fits one chunk.  Once the number of
+// routed experts n is known, each (expert, K part) segment gets
+// floor(grid / (n * kparts)) consecutive waves, and each of them an even share
+// of the segment's rows (gate_up row pairs, down rows): at most 8 pairs / 16
+// rows, so all waves carry about the same work whatever n is.
 template <bool GU>
 __global__ __launch_bounds__(kWave) void gemv_kernel(GemvArgs A) {
   __shared__ __align__(512) uint8_t tabs[kChunkRows * kMaxTabBytes];   // row tables at kTabStride<Q>
   __shared__ RouteLds L;
-  const int per_expert = A.chunks * A.kparts;
-  const int a = blockIdx.x / per_expert;
-  const int rem = blockIdx.x % per_expert;
-  const int chunk = rem / A.kparts;
-  const int kpart = rem % A.kparts;
   Slots sl;
-  const bool have = A.inline_route ? find_expert_inline(A, a, sl, L) : find_expert_routed(A, a, sl);
+  int a = 0;
+  const bool have = A.inline_route ? find_expert_inline(A, a, sl, L) : find_expert_routed<GU>(A, a, sl);
   if (!have) return;
   if (sl.n_e < A.min_tokens || sl.n_e >= A.max_tokens) return;
 
+  const int rows = GU ? A.I : A.H;
+  const int per = waves_per_segment<GU>(A, sl.num_active);
+  const int seg = (int)blockIdx.x / per;
+  const int c = (int)blockIdx.x - seg * per;
+  Chunk ch;
+  ch.kpart = seg - a * A.kparts;
+  ch.first = (int)(((long long)c * rows) / per);
+  ch.n = (int)(((long long)(c + 1) * rows) / per) - ch.first;
+  if (ch.n <= 0) return;
   switch (uniform(A.q[2 * sl.e + (GU ? 0 : 1)])) {
-    case 3: chunk_by_tokens<3, GU>(A, sl, chunk, kpart, tabs); break;
-    case 4: chunk_by_tokens<4, GU>(A, sl, chunk, kpart, tabs); break;
-    case 5: chunk_by_tokens<5, GU>(A, sl, chunk, kpart, tabs); break;
-    case 6: chunk_by_tokens<6, GU>(A, sl, chunk, kpart, tabs); break;
-    case 7: chunk_by_tokens<7, GU>(A, sl, chunk, kpart, tabs); break;
-    case 8: chunk_by_tokens<8, GU>(A, sl, chunk, kpart, tabs); break;
-    default: chunk_zero<GU>(A, sl, chunk, kpart); break;
+    case 3: chunk_by_tokens<3, GU>(A, sl, ch, tabs); break;
+    case 4: chunk_by_tokens<4, GU>(A, sl, ch, tabs); break;
+    case 5: chunk_by_tokens<5, GU>(A, sl, ch, tabs); break;
+    case 6: chunk_by_tokens<6, GU>(A, sl, ch, tabs); break;
+    case 7: chunk_by_tokens<7, GU>(A, sl, ch, tabs); break;
+    case 8: chunk_by_tokens<8, GU>(A, sl, ch, tabs); break;
+    default: chunk_zero<GU>(A, sl, ch); break;
   }
-
 }
 
-static int active_bound(int E, int T, int k) { return E < T * k ? E : T * k; }
+// Resident one-wave workgroups of a kernel (cached per device).
+template <bool GU>
+static int resident_waves() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1024;
+  if (cache[dev] == 0) {
+    int ncu = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0) ncu = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemv_kernel<GU>, kWave, 0) != hipSuccess || per_cu <= 0)
+      per_cu = 4;
+    cache[dev] = ncu * per_cu;
+  }
+  return cache[dev];
+}
 
-hipError_t launch_gemv_gate_up(const GemvLaunch& g, hipStream_t s) {
+static GemvArgs make_args(const GemvLaunch& g) {
   GemvArgs A{};
   A.H = g.H; A.I = g.I; A.E = g.E; A.k = g.k; A.T = g.T;
   A.blocks = g.blocks; A.q = g.q; A.ids = g.ids; A.rt = g.rt;
-  A.inline_route = g.inline_route; A.min_tokens = g.min_tokens; A.max_tokens = g.max_tokens;
+  A.min_tokens = g.min_tokens; A.max_tokens = g.max_tokens;
+  return A;
+}
+
+// Waves for a launch: the resident count, but at least enough that with every
+// expert routed each wave's share is one chunk (8 pairs / 16 rows), and no more
+// than the split can use (shares of kTargetPairs / kTargetRows).
+template <bool GU>
+static int gemv_grid(const GemvArgs& A) {
+  const long long bound = (long long)(A.E < A.T * A.k ? A.E : A.T * A.k) * A.kparts;
+  const int rows = GU ? A.I : A.H;
+  const int chunk = GU ? 8 : kChunkRows;
+  const int target = GU ? kTargetPairs : kTargetRows;
+  const long long need = bound * ((rows + chunk - 1) / chunk);
+  const long long cap = bound * ((rows + target - 1) / target);
+  long long g = resident_waves<GU>();
+  if (g < need) g = need;
+  if (g > cap) g = cap;
+  return (int)g;
+}
+
+hipError_t launch_gemv_gate_up(const GemvLaunch& g, hipStream_t s) {
+  GemvArgs A = make_args(g);
+  A.inline_route = g.inline_route;
   A.act = g.x; A.hout = g.h; A.oout = nullptr;
-  A.chunks = g.I / 8;
   A.kparts = 1;
-  const int grid = active_bound(g.E, g.T, g.k) * A.chunks;
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(gemv_kernel<true>, dim3(grid), dim3(kWave), 0, s, A);
+  hipLaunchKernelGGL(gemv_kernel<true>, dim3(gemv_grid<true>(A)), dim3(kWave), 0, s, A);
   return hipGetLastError();
 }
 
 hipError_t launch_gemv_down(const GemvLaunch& g, hipStream_t s) {
-  GemvArgs A{};
-  A.H = g.H; A.I = g.I; A.E = g.E; A.k = g.k; A.T = g.T;
-  A.blocks = g.blocks; A.q = g.q; A.ids = g.ids; A.rt = g.rt;
+  GemvArgs A = make_args(g);
   A.inline_route = 0;    // the gate_up kernel or the route kernel published the routing
-  A.min_tokens = g.min_tokens; A.max_tokens = g.max_tokens;
   A.act = g.h; A.hout = nullptr; A.oout = g.o;
-  A.chunks = g.H / kChunkRows;
   A.kparts = g.kparts;
-  const int grid = active_bound(g.E, g.T, g.k) * A.chunks * A.kparts;
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(gemv_kernel<false>, dim3(grid), dim3(kWave), 0, s, A);
+  hipLaunchKernelGGL(gemv_kernel<false>, dim3(gemv_grid<false>(A)), dim3(kWave), 0, s, A);
   return hipGetLastError();
 }
 
