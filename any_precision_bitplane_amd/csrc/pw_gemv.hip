@@ -381,26 +381,26 @@ __device__ __forceinline__ void chunk_body(const GemvArgs& A, const Slots& sl, c
   const __amdgpu_buffer_rsrc_t prs = make_rsrc(uniform_ptr(d.planes), pstride * (uint32_t)Q);
   const uint16_t* __restrict__ lut = uniform_ptr(d.lut_all) + lut_offset(N, Q);
 
-  // Row tables of the chunk -> LDS (gate_up: two spans of 8 rows; down: one of 16).
+  // Row tables of the chunk -> LDS with direct buffer-to-LDS loads (no
+  // registers, no LDS store instructions): load i fills LDS bytes
+  // [1024 i, 1024 i + 1024), lane l the 16 bytes at 1024 i + 16 l, taken from
+  // the table row and piece those bytes belong to (row tables sit TSTRIDE apart;
+  // the bytes past a row's table and the rows past the chunk read as zero).
+  // They land asynchronously; the wait before the first lookup covers them.
   {
-    constexpr int SPAN_ROWS = GU ? 8 : 16;
-    constexpr int SPAN_CH = SPAN_ROWS * TAB / 16;
+    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(lut, (uint32_t)N * (uint32_t)TAB);
+    constexpr int NI = kChunkRows * TSTRIDE / 1024;
 #pragma unroll
-    for (int sp = 0; sp < (GU ? 2 : 1); ++sp) {
-      const uint16_t* src = lut + (size_t)((GU && sp ? I : 0) + ch.first) * (1 << Q);
-      constexpr int CPR = TAB / 16;            // 16-byte pieces per row table
-#pragma unroll
-      for (int c0 = 0; c0 < SPAN_CH; c0 += kWave) {
-        const int c = c0 + lane;
-        const int j = c / CPR;                 // row inside the span
-        const int pos = sp * SPAN_ROWS + j;
-        if (c < SPAN_CH && j < ch.n)
-          *reinterpret_cast<uint4*>(tabs + pos * TSTRIDE + (c % CPR) * 16) =
-              *reinterpret_cast<const uint4*>(src + c * 8);
-      }
+    for (int i = 0; i < NI; ++i) {
+      const int dst = 1024 * i + 16 * lane;
+      const int pos = dst / TSTRIDE, col = dst % TSTRIDE;
+      const uint32_t voff = (col < TAB && chunk_row_valid<GU>(ch, pos))
+                                ? (uint32_t)chunk_row<GU>(ch, pos, I) * (uint32_t)TAB + (uint32_t)col
+                                : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (__attribute__((address_space(3))) void*)(tabs + 1024 * i), 16,
+                                               voff, 0, 0, 0);
     }
   }
-  __syncthreads();
 
   const uint32_t tab_base = lds_addr(tabs);
   const int nsl = (W + kWave - 1) / kWave;
@@ -444,26 +444,28 @@ __device__ __forceinline__ void chunk_body(const GemvArgs& A, const Slots& sl, c
       }
     };
 
+    auto load_x = [&](int slice) {
+      xslice = slice;
+      const int wc = slice * kWave + lane;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          uint4 u = make_uint4(0u, 0u, 0u, 0u);
+          if (xsrc[t] != nullptr && wc < W) u = *reinterpret_cast<const uint4*>(xsrc[t] + wc * 32 + v * 8);
+          xr[t][4 * v + 0] = __builtin_bit_cast(half2_t, u.x);
+          xr[t][4 * v + 1] = __builtin_bit_cast(half2_t, u.y);
+          xr[t][4 * v + 2] = __builtin_bit_cast(half2_t, u.z);
+          xr[t][4 * v + 3] = __builtin_bit_cast(half2_t, u.w);
+        }
+      }
+    };
+
     auto compute_group = [&](uint32_t (&P)[G][Q], int st) {
       const int slice = s_begin + st / NGR;
       const int g = st % NGR;
       if (!group_live(g)) return;
-      if (slice != xslice) {
-        xslice = slice;
-        const int wc = slice * kWave + lane;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            uint4 u = make_uint4(0u, 0u, 0u, 0u);
-            if (xsrc[t] != nullptr && wc < W) u = *reinterpret_cast<const uint4*>(xsrc[t] + wc * 32 + v * 8);
-            xr[t][4 * v + 0] = __builtin_bit_cast(half2_t, u.x);
-            xr[t][4 * v + 1] = __builtin_bit_cast(half2_t, u.y);
-            xr[t][4 * v + 2] = __builtin_bit_cast(half2_t, u.z);
-            xr[t][4 * v + 3] = __builtin_bit_cast(half2_t, u.w);
-          }
-        }
-      }
+      if (slice != xslice) load_x(slice);
       float acc[M];
 #pragma unroll
       for (int i = 0; i < M; ++i) acc[i] = 0.0f;
@@ -485,12 +487,17 @@ __device__ __forceinline__ void chunk_body(const GemvArgs& A, const Slots& sl, c
       if (t_l < NT && r_l >= 0 && r_l < G) tot += v;
     };
 
+    // the activations of the first slice, then the first two row groups
+    if (nsteps > 0) load_x(s_begin);
     if (nsteps > 0) load_group(Pa, 0);
+    if (nsteps > 1) load_group(Pb, 1);
+    // everything issued so far, the staged row tables included, has landed
+    if (t0 == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     for (int st = 0; st < nsteps; st += 2) {
-      if (st + 1 < nsteps) load_group(Pb, st + 1);
       compute_group(Pa, st);
       if (st + 2 < nsteps) load_group(Pa, st + 2);
       if (st + 1 < nsteps) compute_group(Pb, st + 1);
+      if (st + 3 < nsteps) load_group(Pb, st + 3);
     }
 
     const int t_l = lane >> 4;
