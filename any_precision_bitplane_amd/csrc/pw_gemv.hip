@@ -133,14 +133,21 @@ __device__ __forceinline__ float multi_reduce(float (&v)[M]) {
   return d;
 }
 
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Exclusive prefix sum over the wave with DPP: shifts inside 16-lane rows,
+// then the row totals carried by row_bcast:15 / row_bcast:31.
 __device__ __forceinline__ int wave_excl_scan(int v) {
-  const int lane = threadIdx.x;
   int s = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_up(s, o, kWave);
-    if (lane >= o) s += t;
-  }
+  s += dpp_i<0x111, 0xF>(s);   // row_shr:1
+  s += dpp_i<0x112, 0xF>(s);   // row_shr:2
+  s += dpp_i<0x114, 0xF>(s);   // row_shr:4
+  s += dpp_i<0x118, 0xF>(s);   // row_shr:8
+  s += dpp_i<0x142, 0xA>(s);   // row_bcast:15 into rows 1 and 3
+  s += dpp_i<0x143, 0xC>(s);   // row_bcast:31 into rows 2 and 3
   return s - v;
 }
 
@@ -202,6 +209,7 @@ __device__ __forceinline__ void row_dot(const uint32_t (&R)[8], uint32_t base, c
 struct Slots {
   int e, n_e, off_e, num_active;
   unsigned long long mask;   // inline routing: slots routed to e (bit = slot)
+  pw_block_desc d;           // page-table entry of this product's block of e
 };
 
 struct RouteLds {
@@ -376,7 +384,7 @@ __device__ __forceinline__ void chunk_body(const GemvArgs& A, const Slots& sl, c
   const int N = GU ? 2 * I : H;
   const int K = GU ? H : I;
   const int W = K >> 5;
-  const pw_block_desc d = A.blocks[2 * sl.e + (GU ? 0 : 1)];
+  const pw_block_desc d = sl.d;
   const uint32_t pstride = (uint32_t)N * (uint32_t)W * 4u;
   const __amdgpu_buffer_rsrc_t prs = make_rsrc(uniform_ptr(d.planes), pstride * (uint32_t)Q);
   const uint16_t* __restrict__ lut = uniform_ptr(d.lut_all) + lut_offset(N, Q);
@@ -562,7 +570,10 @@ __global__ __launch_bounds__(kWave) void gemv_kernel(GemvArgs A) {
   ch.first = (int)(((long long)c * rows) / per);
   ch.n = (int)(((long long)(c + 1) * rows) / per) - ch.first;
   if (ch.n <= 0) return;
-  switch (uniform(A.q[2 * sl.e + (GU ? 0 : 1)])) {
+  // bitwidth and page-table entry of the block, requested together
+  const int qv = uniform(A.q[2 * sl.e + (GU ? 0 : 1)]);
+  sl.d = A.blocks[2 * sl.e + (GU ? 0 : 1)];
+  switch (qv) {
     case 3: chunk_by_tokens<3, GU>(A, sl, ch, tabs); break;
     case 4: chunk_by_tokens<4, GU>(A, sl, ch, tabs); break;
     case 5: chunk_by_tokens<5, GU>(A, sl, ch, tabs); break;
