@@ -6,8 +6,9 @@
 // contraction.
 //
 // Tile: 256 tokens x 128 weight rows per 8-wave workgroup, K step 64.
-//   * waves 0-3 decode: each thread turns one 32-weight group (the first q
-//     plane words of one row) into fp16 through the row's table in LDS and
+//   * every wave decodes: a pair of threads turns one 32-weight group (the
+//     first q plane words of one row) into fp16 through the row's table in
+//     LDS, each thread half of it with its lookups issued together, and
 //     writes it to a double-buffered weight tile;
 //   * all waves stage the gathered activation tile (half a token row each);
 //   * every wave multiplies a 64 x 64 sub-tile with v_mfma_f32_16x16x32_f16
@@ -67,6 +68,25 @@ constexpr int kLdsW = kTN * kTileStride * 2;                     // one weight t
 constexpr int kLdsX = kTM * kTileStride * 2;                     // activation tile
 constexpr int kMfmaLds = kLdsTabs + 2 * kLdsW + kLdsX;
 
+// Sixteen weights of a group: fields of weights j (0..15) in byte j >> 3 of
+// F[j & 7]; all sixteen lookups are issued before any is packed.
+template <int Q>
+struct HalfGroupDecode {
+  __device__ static __forceinline__ void run(const uint32_t (&F)[8], uint32_t base, uint32_t (&out)[8]) {
+    uint32_t v[16];
+    lookups<0>(F, base, v);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) out[p] = v[2 * p] | (v[2 * p + 1] << 16);
+  }
+  template <int J>
+  __device__ static __forceinline__ void lookups(const uint32_t (&F)[8], uint32_t base, uint32_t (&v)[16]) {
+    if constexpr (J < 16) {
+      v[J] = lds_u16_at(entry_addr<Q, J>(F, base));
+      lookups<J + 1>(F, base, v);
+    }
+  }
+};
+
 template <int Q, bool GU>
 __device__ __forceinline__ void mfma_tile(const MfmaArgs& A, int e, int n_e, int off_e, int m0, int nt, uint8_t* lds) {
   constexpr int TAB = (1 << Q) * 2;
@@ -78,7 +98,6 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& A, int e, int n_e, int
   const int K = GU ? H : I;
   const int W = K >> 5;
   const int nk = (K + kTK - 1) / kTK;
-  const bool decoder = wave < 4;
 
   uint8_t* tabs = lds;
   _Float16* wt0 = reinterpret_cast<_Float16*>(lds + kLdsTabs);
@@ -99,8 +118,9 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& A, int e, int n_e, int
     *reinterpret_cast<uint4*>(tabs + c * 16) = v;
   }
 
-  // Decode job (waves 0-3): row dr, word dw of each K step.
-  const int dr = (tid & 255) >> 1, dw = tid & 1;
+  // Decode job: row dr, word dw of each K step, weights [16 dh, 16 dh + 16)
+  // of that word (the two threads of a pair load the same plane words).
+  const int dr = tid >> 2, dw = (tid >> 1) & 1, dh = tid & 1;
   const bool dr_ok = mrow_ok<GU>(nt, dr, I, H);
   const uint32_t drow = (uint32_t)mrow<GU>(nt, dr, I);
   const uint32_t tab_base = lds_addr(tabs) + (uint32_t)(dr * TAB);
@@ -115,9 +135,9 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& A, int e, int n_e, int
   uint32_t Pa[Q], Pb[Q];
   uint4 X[4];
 
-  // plane words of a K step (decoders), two steps ahead
+  // plane words of a K step, two steps ahead
   auto prefetch_planes = [&](uint32_t (&P)[Q], int step) {
-    if (step >= nk || !decoder) return;
+    if (step >= nk) return;
     const int wc = ((step * kTK) >> 5) + dw;
     const uint32_t voff = (dr_ok && wc < W) ? (drow * (uint32_t)W + (uint32_t)wc) * 4u : kOutOfRange;
 #pragma unroll
@@ -136,12 +156,16 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& A, int e, int n_e, int
   auto decode = [&](uint32_t (&P)[Q], _Float16* wt) {
     uint32_t R[8];
     planes_to_fields<Q>(P, R);
-    uint32_t packed[16];
-    GroupDecode<Q, 0>::run(R, tab_base, packed);
-    uint4* dst = reinterpret_cast<uint4*>(wt + dr * kTileStride + dw * 32);
+    // this thread's half: fields of weights 16 dh + j sit in bytes 2 dh, 2 dh + 1 of R[j & 7]
+    uint32_t F[8];
+    const uint32_t sel = dh ? 0x0c0c0302u : 0x0c0c0100u;
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-      dst[v] = make_uint4(packed[4 * v], packed[4 * v + 1], packed[4 * v + 2], packed[4 * v + 3]);
+    for (int i = 0; i < 8; ++i) F[i] = __builtin_amdgcn_perm(0u, R[i], sel);
+    uint32_t packed[8];
+    HalfGroupDecode<Q>::run(F, tab_base, packed);
+    uint4* dst = reinterpret_cast<uint4*>(wt + dr * kTileStride + dw * 32 + dh * 16);
+    dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
   };
   auto stage_x = [&]() {
     uint4* dst = reinterpret_cast<uint4*>(xt + xr * kTileStride + 32 * xh);
@@ -187,7 +211,7 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& A, int e, int n_e, int
   prefetch_planes(Pb, 1);
   prefetch_x(0);
   __syncthreads();                        // tables in LDS
-  if (decoder) decode(Pa, wt0);
+  decode(Pa, wt0);
   stage_x();
   prefetch_planes(Pa, 2);
   prefetch_x(1);
@@ -198,7 +222,7 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& A, int e, int n_e, int
   for (int k = 0; k < nk; k += 2) {
     // even step k: weights in wt0; planes of step k+1 in Pb
     mma(wt0);
-    if (k + 1 < nk && decoder) {
+    if (k + 1 < nk) {
       decode(Pb, wt1);
       prefetch_planes(Pb, k + 3);
     }
@@ -211,7 +235,7 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& A, int e, int n_e, int
     if (k + 1 >= nk) break;
     // odd step k+1: weights in wt1; planes of step k+2 in Pa
     mma(wt1);
-    if (k + 2 < nk && decoder) {
+    if (k + 2 < nk) {
       decode(Pa, wt0);
       prefetch_planes(Pa, k + 4);
     }
