@@ -16,7 +16,7 @@ using namespace pw;
 namespace {
 
 // AUTO: experts with at least this many routed tokens take the MFMA kernels.
-constexpr int kDefaultMfmaMinTokens = 16;
+constexpr int kDefaultMfmaMinTokens = 8;
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 

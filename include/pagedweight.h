@@ -99,7 +99,7 @@ typedef struct {
 
 typedef struct {
   int32_t path;              /* PW_PATH_*                                     */
-  int32_t mfma_min_tokens;   /* AUTO threshold; <= 0 selects the default      */
+  int32_t mfma_min_tokens;   /* AUTO threshold; <= 0 selects the default (8)  */
   /* Optional hipEvent_t handles (as void*).  If stage_events[0] is non-NULL,
    * event s is recorded on `stream` right before stage s and event
    * PW_NUM_STAGES after the last stage, so the caller can time each stage. */
