@@ -46,7 +46,7 @@ struct GemvArgs {
   int min_tokens, max_tokens;
   const uint16_t* act;      // gate_up: x [T][H];  down: h [slots][I]
   uint16_t* hout;           // gate_up: h [slots][I]
-  float* oout;              // down: o [kparts][slots][H]
+  float* oout;              // down: o [kparts][slots][H], rows by slot t*k + j
   int kparts;               // parts of the K range (down)
 };
 
@@ -433,6 +433,13 @@ __device__ __forceinline__ void chunk_body(const GemvArgs& A, const Slots& sl, c
     }
 
     float tot = 0.0f;                // lane (t * 16 + r): total of chunk row r, token t
+    // down: o rows are indexed by slot (t*k + j), so the combine needs no
+    // indirection; the lane's slot is requested here and used at the end
+    int oslot = 0;
+    if constexpr (!GU) {
+      const int tl = lane >> 4;
+      if (lane < 32 && t0 + tl < sl.n_e) oslot = A.rt.perm[sl.off_e + t0 + tl];
+    }
     uint32_t Pa[G][Q], Pb[G][Q];
     half2_t xr[NT][16];
     int xslice = -1;
@@ -521,7 +528,7 @@ __device__ __forceinline__ void chunk_body(const GemvArgs& A, const Slots& sl, c
       }
     } else {
       if (lane < 32 && t_l < nt && r_l < ch.n)
-        A.oout[((size_t)ch.kpart * slots + sl.off_e + t0 + t_l) * H + ch.first + r_l] = tot;
+        A.oout[((size_t)ch.kpart * slots + oslot) * H + ch.first + r_l] = tot;
     }
   }
 }
@@ -534,7 +541,7 @@ __device__ __forceinline__ void chunk_zero(const GemvArgs& A, const Slots& sl, c
   for (int i = lane; i < sl.n_e * ch.n; i += kWave) {
     const int t = i / ch.n, r = i % ch.n;
     if constexpr (GU) A.hout[(size_t)(sl.off_e + t) * A.I + ch.first + r] = 0;
-    else A.oout[((size_t)ch.kpart * slots + sl.off_e + t) * A.H + ch.first + r] = 0.0f;
+    else A.oout[((size_t)ch.kpart * slots + A.rt.perm[sl.off_e + t]) * A.H + ch.first + r] = 0.0f;
   }
   if (lane == 0 && ch.first == 0 && ch.kpart == 0) raise_status(A.rt.status, PW_DEV_BAD_BITWIDTH);
 }

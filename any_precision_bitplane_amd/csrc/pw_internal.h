@@ -49,7 +49,7 @@ struct WsLayout {
   size_t inv = 0;           // int32 [T*k]  slot -> sorted position, -1 if dropped
   size_t mtiles = 0;        // int32 [2 * mtile_bound] MFMA token tiles
   size_t h = 0;             // fp16  [T*k][I] activations between the products
-  size_t o = 0;             // fp32  [kparts][T*k][H] expert outputs before the combine
+  size_t o = 0;             // fp32  [kparts][T*k][H] expert outputs by slot (t*k + j), before the combine
   size_t total = 0;
 };
 

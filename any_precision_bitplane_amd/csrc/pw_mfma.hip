@@ -12,12 +12,14 @@
 //     writes it to a double-buffered weight tile;
 //   * all waves stage the gathered activation tile (half a token row each);
 //   * every wave multiplies a 64 x 64 sub-tile with v_mfma_f32_16x16x32_f16
-//     (fp32 accumulation in AGPRs).
+//     (fp32 accumulation).
 // Plane words are prefetched into registers two K steps ahead and
 // activations one step ahead, and the decode of step k+1 is issued while the
-// matrix cores work on step k.  gate_up tiles take 64 gate rows and the matching 64 up rows; each
-// wave holds matching gate and up columns, so SwiGLU runs on the accumulators
-// and h leaves as fp16.
+// matrix cores work on step k.  gate_up tiles take 64 gate rows and the
+// matching 64 up rows; each wave holds matching gate and up columns, so SwiGLU
+// runs on the accumulators and h leaves as fp16.  Token tiles less than half
+// full take a variant that feeds the matrix cores' activation operand from
+// registers loaded straight from memory (no LDS activation tile).
 //
 // Work items are (token tile, row tile) pairs; token tiles come from the route
 // kernel's list.  Consecutive items on one XCD (workgroups are dealt to the 8
@@ -266,11 +268,208 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& A, int e, int n_e, int
           A.hout[pos * I + nt * 64 + r] = __builtin_bit_cast(uint16_t, hh);
         }
       } else {
+        const size_t slot = (size_t)A.rt.perm[pos];   // o rows are indexed by slot
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int r = ncol[j] + (lane & 15);
           if (!mrow_ok<GU>(nt, r, I, H)) continue;
-          A.oout[pos * H + nt * kTN + r] = acc[i][j][v];
+          A.oout[slot * H + nt * kTN + r] = acc[i][j][v];
+        }
+      }
+    }
+  }
+}
+
+// Variant for token tiles less than half full (moderate batches): the
+// matrix-core A operand is loaded straight from the activation rows into
+// registers, one K step ahead, instead of being staged in LDS, so a step needs
+// one barrier instead of two and absent tokens cost no loads; waves whose
+// tokens are all absent skip the matrix-core work.  With full tiles the
+// LDS-staged kernel above hides the activation latency better (measured on
+// the Mixtral-shaped prefill layer: 9.1 ms staged, 10.2 ms direct); with 16
+// tokens per expert (Mixtral-shaped layer, T = 64) the call takes 1.43 ms
+// instead of 1.98, the batched Qwen-shaped call 0.68 ms instead of 0.81.  The
+// switch point (fewer than 128 tokens) was the fastest of 64/128/192/256 on
+// the prefill layer; the other two calls did not depend on it.
+constexpr int kDirectBelow = 128;
+template <int Q, bool GU>
+__device__ __forceinline__ void mfma_tile_direct(const MfmaArgs& A, int e, int n_e, int off_e, int m0, int nt, uint8_t* lds) {
+  constexpr int TAB = (1 << Q) * 2;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int H = A.H, I = A.I;
+  const int N = GU ? 2 * I : H;
+  const int K = GU ? H : I;
+  const int W = K >> 5;
+  const int nk = (K + kTK - 1) / kTK;
+
+  uint8_t* tabs = lds;
+  _Float16* wt0 = reinterpret_cast<_Float16*>(lds + kLdsTabs);
+  _Float16* wt1 = wt0 + kTN * kTileStride;   // (the activation tile's LDS is unused here)
+
+  const pw_block_desc d = A.blocks[2 * e + (GU ? 0 : 1)];
+  const uint32_t pstride = (uint32_t)N * (uint32_t)W * 4u;
+  const __amdgpu_buffer_rsrc_t prs = make_rsrc(uniform_ptr(d.planes), pstride * (uint32_t)Q);
+  const uint16_t* __restrict__ lut = uniform_ptr(d.lut_all) + lut_offset(N, Q);
+
+  // Row tables -> LDS (uint4 chunks; rows outside the block read as zero).
+  for (int c = tid; c < kTN * TAB / 16; c += kMfmaThreads) {
+    const int r = c / (TAB / 16), cc = c % (TAB / 16);
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (mrow_ok<GU>(nt, r, I, H))
+      v = *reinterpret_cast<const uint4*>(lut + (size_t)mrow<GU>(nt, r, I) * (1 << Q) + cc * 8);
+    *reinterpret_cast<uint4*>(tabs + c * 16) = v;
+  }
+
+  // Decode job: row dr, word dw of each K step, weights [16 dh, 16 dh + 16)
+  // of that word (the two threads of a pair load the same plane words).
+  const int dr = tid >> 2, dw = (tid >> 1) & 1, dh = tid & 1;
+  const bool dr_ok = mrow_ok<GU>(nt, dr, I, H);
+  const uint32_t drow = (uint32_t)mrow<GU>(nt, dr, I);
+  const uint32_t tab_base = lds_addr(tabs) + (uint32_t)(dr * TAB);
+  uint32_t Pa[Q], Pb[Q];
+
+  // plane words of a K step, two steps ahead
+  auto prefetch_planes = [&](uint32_t (&P)[Q], int step) {
+    if (step >= nk) return;
+    const int wc = ((step * kTK) >> 5) + dw;
+    const uint32_t voff = (dr_ok && wc < W) ? (drow * (uint32_t)W + (uint32_t)wc) * 4u : kOutOfRange;
+#pragma unroll
+    for (int p = 0; p < Q; ++p) P[p] = buf_load_u32(prs, voff, (uint32_t)p * pstride);
+  };
+  auto decode = [&](uint32_t (&P)[Q], _Float16* wt) {
+    uint32_t R[8];
+    planes_to_fields<Q>(P, R);
+    // this thread's half: fields of weights 16 dh + j sit in bytes 2 dh, 2 dh + 1 of R[j & 7]
+    uint32_t F[8];
+    const uint32_t sel = dh ? 0x0c0c0302u : 0x0c0c0100u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) F[i] = __builtin_amdgcn_perm(0u, R[i], sel);
+    uint32_t packed[8];
+    HalfGroupDecode<Q>::run(F, tab_base, packed);
+    uint4* dst = reinterpret_cast<uint4*>(wt + dr * kTileStride + dw * 32 + dh * 16);
+    dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+  };
+  // Wave sub-tile: tokens [64 wm, +64); rows: gate_up -> gate [32 wn, +32) and
+  // up [64 + 32 wn, +32); down -> [64 wn, +64).
+  const int wm = wave & 3, wn = wave >> 2;
+  // Matrix-core A operand straight from the activation rows (no LDS stage):
+  // for token block i the lane holds token 64 wm + 16 i + (lane & 15),
+  // columns 8 (lane >> 4) .. +8 of each 32-column half of a K step.
+  const uint32_t abytes = (uint32_t)((GU ? (size_t)A.T * H : (size_t)A.T * A.k * I) * 2u);
+  const __amdgpu_buffer_rsrc_t ars = make_rsrc(A.act, abytes);
+  uint32_t aoff[4];   // byte offset of the lane's token row (out of range: reads zero)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = 64 * wm + 16 * i + (lane & 15);
+    aoff[i] = kOutOfRange;
+    if (m < n_e - m0) {
+      const int pos = off_e + m0 + m;
+      aoff[i] = GU ? (uint32_t)(A.rt.perm[pos] / A.k) * (uint32_t)H * 2u : (uint32_t)pos * (uint32_t)I * 2u;
+    }
+  }
+  int ncol[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ncol[j] = GU ? ((j < 2 ? 0 : 64) + 32 * wn + 16 * (j & 1)) : (64 * wn + 16 * j);
+
+  float4v acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  uint4 Ar[2][4];
+  auto load_a = [&](uint4 (&Ar)[2][4], int step) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const int c = step * kTK + kh * 32 + 8 * (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t voff = c < K ? aoff[i] + 2u * (uint32_t)c : kOutOfRange;
+        Ar[kh][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ars, (int)voff, 0, 0));
+      }
+    }
+  };
+  // a wave whose 64 tokens all lie past the expert's last one has nothing to multiply
+  const bool wave_live = 64 * wm < n_e - m0;
+  auto mma = [&](const _Float16* wt, const uint4 (&Ar)[2][4]) {
+    if (!wave_live) return;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      __builtin_amdgcn_sched_barrier(0);   // keep the two K halves' fragments from being live together
+      half8v af[4], bf[4];
+      const int kk = kh * 32 + 8 * (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = __builtin_bit_cast(half8v, Ar[kh][i]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bf[j] = *reinterpret_cast<const half8v*>(wt + (ncol[j] + (lane & 15)) * kTileStride + kk);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // Prologue: planes of steps 0 and 1 and activations of step 0 in flight;
+  // decode step 0.
+  load_a(Ar, 0);
+  prefetch_planes(Pa, 0);
+  prefetch_planes(Pb, 1);
+  __syncthreads();                        // tables in LDS
+  decode(Pa, wt0);
+  prefetch_planes(Pa, 2);
+  __syncthreads();
+
+  // Step k: matrix cores on wt[k&1] with the activations in registers; then
+  // request the activations of step k+1 and decode step k+1 into the other
+  // weight buffer.  One barrier per step: after it the decoded tile is
+  // complete and nobody reads the buffer the next decode overwrites.
+  for (int k = 0; k < nk; k += 2) {
+    mma(wt0, Ar);
+    if (k + 1 < nk) {
+      load_a(Ar, k + 1);
+      decode(Pb, wt1);
+      prefetch_planes(Pb, k + 3);
+    }
+    __syncthreads();
+    if (k + 1 >= nk) break;
+    mma(wt1, Ar);
+    if (k + 2 < nk) {
+      load_a(Ar, k + 2);
+      decode(Pa, wt0);
+      prefetch_planes(Pa, k + 4);
+    }
+    __syncthreads();
+  }
+
+  // Epilogue.  acc[i][j] element v: token 64 wm + 16 i + 4 (lane >> 4) + v,
+  // tile column ncol[j] + (lane & 15).
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = 64 * wm + 16 * i + 4 * (lane >> 4) + v;
+      if (m >= n_e - m0) continue;
+      const size_t pos = (size_t)(off_e + m0 + m);
+      if constexpr (GU) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int r = ncol[j] + (lane & 15);          // gate row (tile-local < 64)
+          if (!mrow_ok<GU>(nt, r, I, H)) continue;
+          const float g = acc[i][j][v], u = acc[i][j + 2][v];
+          const _Float16 hh = (_Float16)(silu_f32(g) * u);
+          A.hout[pos * I + nt * 64 + r] = __builtin_bit_cast(uint16_t, hh);
+        }
+      } else {
+        const size_t slot = (size_t)A.rt.perm[pos];   // o rows are indexed by slot
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = ncol[j] + (lane & 15);
+          if (!mrow_ok<GU>(nt, r, I, H)) continue;
+          A.oout[slot * H + nt * kTN + r] = acc[i][j][v];
         }
       }
     }
@@ -286,7 +485,7 @@ __device__ __forceinline__ void mfma_zero_tile(const MfmaArgs& A, int n_e, int o
     if constexpr (GU) {
       if (r < 64 && mrow_ok<GU>(nt, r, A.I, A.H)) A.hout[pos * A.I + nt * 64 + r] = 0;
     } else {
-      if (mrow_ok<GU>(nt, r, A.I, A.H)) A.oout[pos * A.H + nt * kTN + r] = 0.0f;
+      if (mrow_ok<GU>(nt, r, A.I, A.H)) A.oout[(size_t)A.rt.perm[pos] * A.H + nt * kTN + r] = 0.0f;
     }
   }
   if (threadIdx.x == 0 && nt == 0 && m0 == 0) raise_status(A.rt.status, PW_DEV_BAD_BITWIDTH);
@@ -305,14 +504,27 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_kernel(MfmaArgs A) {
   const int m0 = uniform(A.rt.mtiles[2 * mi + 1]);
   const int n_e = uniform(A.rt.counts[e]);
   const int off_e = uniform(A.rt.offsets[e]);
-  switch (uniform(A.q[2 * e + (GU ? 0 : 1)])) {
-    case 3: mfma_tile<3, GU>(A, e, n_e, off_e, m0, nt, lds); break;
-    case 4: mfma_tile<4, GU>(A, e, n_e, off_e, m0, nt, lds); break;
-    case 5: mfma_tile<5, GU>(A, e, n_e, off_e, m0, nt, lds); break;
-    case 6: mfma_tile<6, GU>(A, e, n_e, off_e, m0, nt, lds); break;
-    case 7: mfma_tile<7, GU>(A, e, n_e, off_e, m0, nt, lds); break;
-    case 8: mfma_tile<8, GU>(A, e, n_e, off_e, m0, nt, lds); break;
-    default: mfma_zero_tile<GU>(A, n_e, off_e, m0, nt); break;
+  const int qv = uniform(A.q[2 * e + (GU ? 0 : 1)]);
+  if (qv < kMinBits || qv > kMaxBits) {
+    mfma_zero_tile<GU>(A, n_e, off_e, m0, nt);
+  } else if (n_e - m0 >= kDirectBelow) {
+    switch (qv) {
+      case 3: mfma_tile<3, GU>(A, e, n_e, off_e, m0, nt, lds); break;
+      case 4: mfma_tile<4, GU>(A, e, n_e, off_e, m0, nt, lds); break;
+      case 5: mfma_tile<5, GU>(A, e, n_e, off_e, m0, nt, lds); break;
+      case 6: mfma_tile<6, GU>(A, e, n_e, off_e, m0, nt, lds); break;
+      case 7: mfma_tile<7, GU>(A, e, n_e, off_e, m0, nt, lds); break;
+      default: mfma_tile<8, GU>(A, e, n_e, off_e, m0, nt, lds); break;
+    }
+  } else {
+    switch (qv) {
+      case 3: mfma_tile_direct<3, GU>(A, e, n_e, off_e, m0, nt, lds); break;
+      case 4: mfma_tile_direct<4, GU>(A, e, n_e, off_e, m0, nt, lds); break;
+      case 5: mfma_tile_direct<5, GU>(A, e, n_e, off_e, m0, nt, lds); break;
+      case 6: mfma_tile_direct<6, GU>(A, e, n_e, off_e, m0, nt, lds); break;
+      case 7: mfma_tile_direct<7, GU>(A, e, n_e, off_e, m0, nt, lds); break;
+      default: mfma_tile_direct<8, GU>(A, e, n_e, off_e, m0, nt, lds); break;
+    }
   }
 }
 

@@ -303,7 +303,10 @@ def test_forward_mfma_forced(torch, name, T):
 
 
 def test_forward_mfma_ragged_shapes(torch):
-    for (H, I, E, k, T, seed) in [(2080, 96, 5, 3, 70, 41), (96, 1056, 4, 4, 45, 42), (256, 512, 2, 1, 300, 43)]:
+    # the last case gives each expert one full 256-token tile and a partial one,
+    # with both K ranges ending half way through a 64-wide step
+    for (H, I, E, k, T, seed) in [(2080, 96, 5, 3, 70, 41), (96, 1056, 4, 4, 45, 42), (256, 512, 2, 1, 300, 43),
+                                  (160, 96, 2, 2, 260, 44)]:
         L = custom_layer(H, I, E, k, T, seed)
         say(f"forward mfma ragged H={H} I={I} E={E} k={k} T={T}")
         _, y = run_forward(torch, L, B.PW_PATH_MFMA)
