@@ -20,7 +20,9 @@
 //     strides, so an entry's address is one byte permute of the table base
 //     and the code field, and the lookups go out in batches;
 //   * row groups are double-buffered: the planes of the next group are in
-//     flight while the current one is decoded.
+//     flight while the current one is decoded;
+//   * at q = 3 the 8-entry tables are expanded in LDS into 64-entry pair
+//     tables (same 256 bytes), so one lookup gives two packed weights.
 // gate_up chunks hold 8 gate rows and the matching 8 up rows (i and I + i), so
 // SwiGLU runs in the epilogue and h = SiLU(gate) * up leaves as fp16.
 //
@@ -34,6 +36,7 @@
 namespace pw {
 
 constexpr int kChunkRows = 16;
+constexpr int kWaitVmcnt0 = 0x0F70;   // s_waitcnt vmcnt(0); expcnt and lgkmcnt not waited on
 constexpr int kMaxTabBytes = (1 << kMaxBits) * 2;          // 512 B per row table
 
 struct GemvArgs {
@@ -201,6 +204,77 @@ __device__ __forceinline__ void row_dot(const uint32_t (&R)[8], uint32_t base, c
     __builtin_amdgcn_sched_group_barrier(kDsRead, kBatch, 0);
   }
   __builtin_amdgcn_sched_group_barrier(kValu, 2 * kUseOps, 0);
+}
+
+// ---------------------------------------------------------------------------
+// 3-bit blocks: pair tables
+//
+// At q = 3 a row's table has 8 entries, so a table of all 64 entry pairs
+// (fp16 LUT[a] in the low half, LUT[b] in the high half) takes the same 256
+// bytes of LDS; one lookup then yields two weights already packed for v_dot2,
+// which halves the address, lookup and packing work per weight.  The bit
+// transpose below produces, for the pair of weights (8k + c, 8k + c + 4), the
+// byte (code_a << 5) | (code_b << 2) = 4 * pair index in byte k of R[c]
+// (c, k = 0..3): the planes enter the 8 x 8 transpose of each byte lane as
+// rows 7, 6, 5 (weights 0..3 of the lane, code bits from the most significant
+// plane down) and, shifted down by four, rows 4, 3, 2 (weights 4..7); only the
+// output rows 0..3 are formed.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void planes_to_pairs3(const uint32_t (&P)[3], uint32_t (&R)[4]) {
+  constexpr uint32_t H4 = 0xF0F0F0F0u, H2 = 0xCCCCCCCCu, H1 = 0xAAAAAAAAu;
+  // level 4, output rows 0..3 only (input rows 0, 1 are zero)
+  R[0] = P[0] & H4;
+  R[1] = (P[2] << 4) & H4;
+  R[2] = bfi(H4, P[1] << 4, P[2] >> 4);
+  R[3] = bfi(H4, P[0] << 4, P[1] >> 4);
+  // levels 2 and 1 inside rows 0..3
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const uint32_t a = R[r], b = R[r + 2];
+    R[r] = bfi(H2, b << 2, a);
+    R[r + 2] = bfi(H2, b, a >> 2);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; r += 2) {
+    const uint32_t a = R[r], b = R[r + 1];
+    R[r] = bfi(H1, b << 1, a);
+    R[r + 1] = bfi(H1, b, a >> 1);
+  }
+}
+
+typedef const __attribute__((address_space(3))) uint32_t* lds_u32_cptr;
+typedef __attribute__((address_space(3))) uint32_t* lds_u32_ptr;
+
+// acc[t] += sum over the 16 pairs of the row's 32 weights; pair (c, k) meets the
+// activation pair xr[t][4c + k] = (x[8k + c], x[8k + c + 4]).
+template <int NT>
+__device__ __forceinline__ void row_dot_pairs3(const uint32_t (&R)[4], uint32_t base, const half2_t (&xr)[NT][16],
+                                               float* acc) {
+  uint32_t v[16];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      v[4 * c + k] = *(lds_u32_cptr)(size_t)__builtin_amdgcn_perm(base, R[c], 0x07060500u | (uint32_t)k);
+#pragma unroll
+  for (int p = 0; p < 16; ++p)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, v[p]), xr[t][p], acc[t], false);
+}
+
+// In place: every 8-entry row table of the chunk (at the start of its 256-byte
+// slot) becomes its 64-entry pair table.
+__device__ __forceinline__ void build_pair_tables3(uint32_t tab_base) {
+  const int lane = threadIdx.x;
+  const uint32_t ia = 2u * (uint32_t)(lane >> 3), ib = 2u * (uint32_t)(lane & 7);
+  uint32_t pr[kChunkRows];
+#pragma unroll
+  for (int r = 0; r < kChunkRows; ++r) {
+    const uint32_t row = tab_base + 256u * (uint32_t)r;
+    pr[r] = lds_u16_at(row + ia) | (lds_u16_at(row + ib) << 16);
+  }
+#pragma unroll
+  for (int r = 0; r < kChunkRows; ++r) *(lds_u32_ptr)(size_t)(tab_base + 256u * (uint32_t)r + 4u * (uint32_t)lane) = pr[r];
 }
 
 // ---------------------------------------------------------------------------
@@ -464,14 +538,26 @@ __device__ __forceinline__ void chunk_body(const GemvArgs& A, const Slots& sl, c
       const int wc = slice * kWave + lane;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
+        uint4 u[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          uint4 u = make_uint4(0u, 0u, 0u, 0u);
-          if (xsrc[t] != nullptr && wc < W) u = *reinterpret_cast<const uint4*>(xsrc[t] + wc * 32 + v * 8);
-          xr[t][4 * v + 0] = __builtin_bit_cast(half2_t, u.x);
-          xr[t][4 * v + 1] = __builtin_bit_cast(half2_t, u.y);
-          xr[t][4 * v + 2] = __builtin_bit_cast(half2_t, u.z);
-          xr[t][4 * v + 3] = __builtin_bit_cast(half2_t, u.w);
+          u[v] = make_uint4(0u, 0u, 0u, 0u);
+          if (xsrc[t] != nullptr && wc < W) u[v] = *reinterpret_cast<const uint4*>(xsrc[t] + wc * 32 + v * 8);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          if constexpr (Q == 3) {
+            // pairs (x[8v + c], x[8v + c + 4]) at 4c + v
+            xr[t][0 + v] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(u[v].z, u[v].x, 0x05040100u));
+            xr[t][4 + v] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(u[v].z, u[v].x, 0x07060302u));
+            xr[t][8 + v] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(u[v].w, u[v].y, 0x05040100u));
+            xr[t][12 + v] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(u[v].w, u[v].y, 0x07060302u));
+          } else {
+            xr[t][4 * v + 0] = __builtin_bit_cast(half2_t, u[v].x);
+            xr[t][4 * v + 1] = __builtin_bit_cast(half2_t, u[v].y);
+            xr[t][4 * v + 2] = __builtin_bit_cast(half2_t, u[v].z);
+            xr[t][4 * v + 3] = __builtin_bit_cast(half2_t, u[v].w);
+          }
         }
       }
     };
@@ -489,9 +575,15 @@ __device__ __forceinline__ void chunk_body(const GemvArgs& A, const Slots& sl, c
         // one row at a time: keeps the scheduler from interleaving the decode
         // of several rows, which would cost registers and occupancy
         __builtin_amdgcn_sched_barrier(0);
-        uint32_t R[8];
-        planes_to_fields<Q>(P[r], R);
-        row_dot<Q, NT>(R, tab_base + (uint32_t)((g * G + r) * TSTRIDE), xr, &acc[r * NT]);
+        if constexpr (Q == 3) {
+          uint32_t R[4];
+          planes_to_pairs3(P[r], R);
+          row_dot_pairs3<NT>(R, tab_base + (uint32_t)((g * G + r) * TSTRIDE), xr, &acc[r * NT]);
+        } else {
+          uint32_t R[8];
+          planes_to_fields<Q>(P[r], R);
+          row_dot<Q, NT>(R, tab_base + (uint32_t)((g * G + r) * TSTRIDE), xr, &acc[r * NT]);
+        }
       }
       const float red = multi_reduce<M>(acc);
       // lane L = t * 16 + row takes value (row - g*G) * NT + t from lane vi << MSH
@@ -507,7 +599,13 @@ __device__ __forceinline__ void chunk_body(const GemvArgs& A, const Slots& sl, c
     if (nsteps > 0) load_group(Pa, 0);
     if (nsteps > 1) load_group(Pb, 1);
     // everything issued so far, the staged row tables included, has landed
-    if (t0 == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // (the builtin, unlike inline assembly, is seen by the compiler's wait
+    // tracking, which then does not wait for the table loads again in the
+    // row loop); 3-bit tables then become pair tables
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    if constexpr (Q == 3) {
+      if (t0 == 0) build_pair_tables3(tab_base);
+    }
     for (int st = 0; st < nsteps; st += 2) {
       compute_group(Pa, st);
       if (st + 2 < nsteps) load_group(Pa, st + 2);

@@ -168,6 +168,16 @@ def test_forward_one_token_per_expert_every_bitwidth_pair(torch, H, I, E, k, T, 
     compare(y, oracle_y(L), f"one token per expert E={E}")
 
 
+def test_forward_gemv_three_bit_pair_tables(torch):
+    """3-bit blocks run on pair tables built in LDS: every block at q=3, K not
+    a multiple of the 64-word slice (several slices), several tokens per
+    expert (token pairs and a single token left over)."""
+    L = custom_layer(2080, 1056, 4, 2, 6, 45, qvals=np.full((4, 2), 3))
+    say("forward gemv q=3 H=2080 I=1056 E=4 k=2 T=6")
+    _, y = run_forward(torch, L, B.PW_PATH_GEMV)
+    compare(y, oracle_y(L), "gemv q=3 pair tables")
+
+
 def test_forward_many_tokens_per_expert_gemv(torch):
     # experts with 3..40 tokens take several token groups on the GEMV path
     L = custom_layer(256, 512, 4, 2, 40, 34)
