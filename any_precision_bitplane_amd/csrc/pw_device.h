@@ -194,15 +194,6 @@ __device__ __forceinline__ uint32_t buf_load_u32(__amdgpu_buffer_rsrc_t r, uint3
 
 constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset that reads as zero
 
-// ---------------------------------------------------------------------------
-// Wave-wide sum (all lanes get the result).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
-}
-
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
 // Values the kernels load from memory at a wave-uniform address are the same
