@@ -26,6 +26,9 @@ pw_status check_shape(const pw_moe_shape* s, int32_t T) {
   if (s->hidden % 32 || s->inter % 32) return PW_ERR_UNSUPPORTED_SHAPE;
   if (s->num_experts > kMaxExperts || s->top_k > s->num_experts) return PW_ERR_UNSUPPORTED_SHAPE;
   if ((int64_t)T * s->top_k > INT_MAX / 4) return PW_ERR_UNSUPPORTED_SHAPE;
+  // the kernels address a block's planes (2I x H weights, 8 planes) with
+  // 32-bit byte offsets, out-of-range offsets at 2^31 and up
+  if ((int64_t)2 * s->inter * s->hidden > INT_MAX) return PW_ERR_UNSUPPORTED_SHAPE;
   return PW_OK;
 }
 

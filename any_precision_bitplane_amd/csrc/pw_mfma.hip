@@ -50,6 +50,7 @@ struct MfmaArgs {
   float* oout;           // down output
   int ntiles;            // row tiles per block
   int grid;              // launched workgroups (multiple of 8)
+  int direct_ok;         // activations addressable with 32-bit offsets (variant for partial tiles)
 };
 
 // Row of the block held at tile-local row r (0..127).
@@ -507,7 +508,7 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_kernel(MfmaArgs A) {
   const int qv = uniform(A.q[2 * e + (GU ? 0 : 1)]);
   if (qv < kMinBits || qv > kMaxBits) {
     mfma_zero_tile<GU>(A, n_e, off_e, m0, nt);
-  } else if (n_e - m0 >= kDirectBelow) {
+  } else if (n_e - m0 >= kDirectBelow || !A.direct_ok) {
     switch (qv) {
       case 3: mfma_tile<3, GU>(A, e, n_e, off_e, m0, nt, lds); break;
       case 4: mfma_tile<4, GU>(A, e, n_e, off_e, m0, nt, lds); break;
@@ -535,6 +536,8 @@ static hipError_t launch_mfma(const ExpertArgs& a, const uint16_t* act, uint16_t
   A.blocks = a.blocks; A.q = a.q; A.rt = a.rt;
   A.act = act; A.hout = h; A.oout = o;
   A.ntiles = GU ? (a.I + 63) / 64 : (a.H + kTN - 1) / kTN;
+  const long long act_bytes = 2LL * (GU ? (long long)a.T * a.H : (long long)a.T * a.k * a.I);
+  A.direct_ok = act_bytes < 0x80000000LL ? 1 : 0;
   const long long items = (long long)mtile_bound(a.E, a.T, a.k) * A.ntiles;
   const long long grid = (items + kXcds - 1) / kXcds * kXcds;
   if (grid == 0) return hipSuccess;

@@ -57,7 +57,8 @@ extern "C" {
 typedef int32_t pw_status;
 #define PW_OK                     0
 #define PW_ERR_INVALID_ARG       -1  /* null pointer, negative size, bad enum  */
-#define PW_ERR_UNSUPPORTED_SHAPE -2  /* H, I not multiples of 32, E > 256, k > E */
+#define PW_ERR_UNSUPPORTED_SHAPE -2  /* H, I not multiples of 32, E > 256, k > E,
+                                        2*I*H > 2^31 - 1, or T*k > 2^29 - 1      */
 #define PW_ERR_BITWIDTH          -3  /* host-side bitwidth outside 3..8        */
 #define PW_ERR_WORKSPACE         -4  /* workspace too small                    */
 #define PW_ERR_ALIGNMENT         -5  /* pointer not 16-byte aligned            */

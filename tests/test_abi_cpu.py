@@ -64,6 +64,9 @@ def test_shape_checks(lib):
     assert B.pw_check_shape(B.shape(2048, 1408, 4, 5), 4) == B.PW_ERR_UNSUPPORTED_SHAPE
     assert B.pw_check_shape(B.shape(2048, 1408, 257, 4), 4) == B.PW_ERR_UNSUPPORTED_SHAPE
     assert B.pw_check_shape(B.shape(0, 1408, 60, 4), 4) == B.PW_ERR_INVALID_ARG
+    # a block's planes must stay below 2^31 bytes at 8 bits (2*I*H weights)
+    assert B.pw_check_shape(B.shape(32768, 32768, 8, 2), 4) == B.PW_ERR_UNSUPPORTED_SHAPE
+    assert B.pw_check_shape(B.shape(32768, 32736, 8, 2), 4) == B.PW_OK
     assert B.pw_workspace_bytes(B.shape(2040, 1408, 60, 4), 4) == 0
 
 
