@@ -26,6 +26,11 @@ PW_ERR_WORKSPACE = -4
 PW_ERR_ALIGNMENT = -5
 PW_ERR_HIP = -6
 PW_ERR_UNSUPPORTED = -7
+PW_ERR_OUT_OF_MEMORY = -8
+
+PW_PAGE_CPU = 0
+PW_PAGE_GPU = 1
+PW_PAGE_IN_TRANSFER = 2
 
 PW_DEV_BAD_EXPERT_ID = 0x1
 PW_DEV_BAD_BITWIDTH = 0x2
@@ -52,6 +57,11 @@ class PwBlockDesc(ctypes.Structure):
 class PwMoeOptions(ctypes.Structure):
     _fields_ = [("path", c_int32), ("mfma_min_tokens", c_int32),
                 ("stage_events", c_void_p * (PW_NUM_STAGES + 1))]
+
+
+class PwPageInfo(ctypes.Structure):
+    _fields_ = [("desired", c_int32), ("committed", c_int32), ("resident", c_int32), ("pending", c_int32),
+                ("state", c_int32), ("reserved", c_int32), ("arena_offset", ctypes.c_uint64)]
 
 
 class PwError(RuntimeError):
@@ -84,6 +94,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                      c_void_p, c_void_p, c_void_p, c_size_t, POINTER(PwMoeOptions), c_void_p]),
         "pw_dequant_block": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
         "pw_get_device_status": (c_int32, [c_void_p, POINTER(c_uint32), c_void_p]),
+        "pw_pager_create": (c_int32, [c_int32, POINTER(c_int32), POINTER(c_int32), c_void_p, c_size_t, c_void_p,
+                                      c_void_p, POINTER(c_void_p)]),
+        "pw_pager_destroy": (c_int32, [c_void_p]),
+        "pw_pager_set_block": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p]),
+        "pw_pager_request": (c_int32, [c_void_p, c_int32, c_int32]),
+        "pw_pager_execute": (c_int32, [c_void_p, c_void_p]),
+        "pw_pager_commit": (c_int32, [c_void_p, c_void_p, c_int32, POINTER(c_int32)]),
+        "pw_pager_info": (c_int32, [c_void_p, c_int32, POINTER(PwPageInfo)]),
+        "pw_pager_arena_used": (c_size_t, [c_void_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -96,7 +115,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
 def exported_symbols() -> Sequence[str]:
     return ["pw_abi_version", "pw_status_str", "pw_plane_words", "pw_lut_elems", "pw_lut_offset",
             "pw_check_shape", "pw_workspace_bytes", "pw_workspace_init", "pw_moe_forward",
-            "pw_dequant_block", "pw_get_device_status"]
+            "pw_dequant_block", "pw_get_device_status", "pw_pager_create", "pw_pager_destroy",
+            "pw_pager_set_block", "pw_pager_request", "pw_pager_execute", "pw_pager_commit", "pw_pager_info",
+            "pw_pager_arena_used"]
 
 
 # ---------------------------------------------------------------------------
@@ -192,3 +213,52 @@ def pw_get_device_status(workspace, stream=None) -> int:
     _check(load().pw_get_device_status(_ptr(workspace), ctypes.byref(flags), _stream(stream)),
            "pw_get_device_status")
     return flags.value
+
+
+# --- weight pager ----------------------------------------------------------
+def pw_pager_create(rows: Sequence[int], cols: Sequence[int], arena, arena_bytes: int, blocks, q) -> int:
+    n = len(rows)
+    r = (c_int32 * n)(*rows)
+    c = (c_int32 * n)(*cols)
+    out = c_void_p(0)
+    _check(load().pw_pager_create(n, r, c, _ptr(arena), arena_bytes, _ptr(blocks), _ptr(q), ctypes.byref(out)),
+           "pw_pager_create")
+    return out.value
+
+
+def pw_pager_destroy(pager: int) -> None:
+    _check(load().pw_pager_destroy(pager), "pw_pager_destroy")
+
+
+def pw_pager_set_block(pager: int, b: int, host_planes, lut_all) -> None:
+    _check(load().pw_pager_set_block(pager, b, _ptr(host_planes), _ptr(lut_all)), "pw_pager_set_block")
+
+
+def pw_pager_request(pager: int, b: int, desired: int, check: bool = True) -> int:
+    st = load().pw_pager_request(pager, b, desired)
+    if check:
+        _check(st, "pw_pager_request")
+    return st
+
+
+def pw_pager_execute(pager: int, copy_stream=None, check: bool = True) -> int:
+    st = load().pw_pager_execute(pager, _stream(copy_stream))
+    if check:
+        _check(st, "pw_pager_execute")
+    return st
+
+
+def pw_pager_commit(pager: int, stream=None, wait: bool = True) -> int:
+    n = c_int32(0)
+    _check(load().pw_pager_commit(pager, _stream(stream), 1 if wait else 0, ctypes.byref(n)), "pw_pager_commit")
+    return n.value
+
+
+def pw_pager_info(pager: int, b: int) -> PwPageInfo:
+    info = PwPageInfo()
+    _check(load().pw_pager_info(pager, b, ctypes.byref(info)), "pw_pager_info")
+    return info
+
+
+def pw_pager_arena_used(pager: int) -> int:
+    return load().pw_pager_arena_used(pager)

@@ -50,6 +50,7 @@ const char* pw_status_str(pw_status s) {
     case PW_ERR_ALIGNMENT: return "misaligned pointer";
     case PW_ERR_HIP: return "HIP runtime error";
     case PW_ERR_UNSUPPORTED: return "unsupported option";
+    case PW_ERR_OUT_OF_MEMORY: return "arena has no free range large enough";
     default: return "unknown status";
   }
 }

@@ -84,3 +84,88 @@ class DeviceLayer:
 
     def status(self) -> int:
         return binding.pw_get_device_status(self.ws)
+
+
+class PagedLayer:
+    """One MoE layer whose plane storage the library's weight pager manages.
+
+    The host keeps every block's eight planes in pinned memory; the GPU keeps
+    the committed prefix of each block in one device arena.  The tables stay
+    resident.  Bitwidth changes go through ``request`` / ``execute`` /
+    ``commit`` (the pager calls of the C ABI); ``forward`` reads the page table
+    the pager maintains.
+    """
+
+    def __init__(self, layer, arena_bytes: int, device: str = "cuda:0"):
+        import torch
+        wl = layer.wl
+        self.wl = wl
+        self.device = device
+        self.shape = binding.shape(wl.H, wl.I, wl.E, wl.k)
+        self.T = wl.T
+        self.nblocks = 2 * wl.E
+        self.rows = [2 * wl.I if b % 2 == 0 else wl.H for b in range(self.nblocks)]
+        self.cols = [wl.H if b % 2 == 0 else wl.I for b in range(self.nblocks)]
+        self.host_planes = []
+        self.luts = []
+        for e in range(wl.E):
+            for m in (0, 1):
+                src = torch.from_numpy(np.ascontiguousarray(layer.planes[e][m]).view(np.int32))
+                hp = torch.empty(src.shape, dtype=torch.int32, pin_memory=True)
+                hp.copy_(src)
+                self.host_planes.append(hp)
+                self.luts.append(_to_dev(layer.luts[e][m], device))
+        self.blocks = torch.zeros((self.nblocks, 2), dtype=torch.int64, device=device)
+        self.q = torch.zeros(self.nblocks, dtype=torch.uint8, device=device)
+        self.arena_bytes = int(arena_bytes)
+        self.arena = torch.empty(self.arena_bytes, dtype=torch.uint8, device=device)
+        torch.cuda.synchronize()
+        self.pager = binding.pw_pager_create(self.rows, self.cols, self.arena, self.arena_bytes, self.blocks, self.q)
+        for b in range(self.nblocks):
+            binding.pw_pager_set_block(self.pager, b, self.host_planes[b].data_ptr(), self.luts[b])
+        self.x = torch.from_numpy(layer.x).to(device)
+        self.ids = _to_dev(layer.ids, device)
+        self.w = _to_dev(layer.w, device)
+        self.y = torch.empty((wl.T, wl.H), dtype=torch.float16, device=device)
+        self.ws_bytes = binding.pw_workspace_bytes(self.shape, wl.T)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        binding.pw_workspace_init(self.ws)
+
+    def plane_bytes(self, b: int) -> int:
+        return self.rows[b] * self.cols[b] // 8
+
+    def request(self, q: np.ndarray) -> None:
+        """Desired bitwidths for every block, q [E][2] (host bookkeeping)."""
+        q = np.asarray(q).reshape(-1)
+        for b in range(self.nblocks):
+            binding.pw_pager_request(self.pager, b, int(q[b]))
+
+    def execute(self, copy_stream=None, check: bool = True) -> int:
+        return binding.pw_pager_execute(self.pager, copy_stream, check=check)
+
+    def commit(self, stream=None, wait: bool = True) -> int:
+        return binding.pw_pager_commit(self.pager, stream, wait)
+
+    def info(self, b: int):
+        return binding.pw_pager_info(self.pager, b)
+
+    def committed(self) -> np.ndarray:
+        return np.array([self.info(b).committed for b in range(self.nblocks)], dtype=np.uint8).reshape(-1, 2)
+
+    def forward(self, opts=None, stream=None, check: bool = True, y=None) -> int:
+        return binding.pw_moe_forward(self.shape, self.T, self.x, self.ids, self.w, self.blocks, self.q,
+                                      self.y if y is None else y, self.ws, opts=opts, stream=stream, check=check)
+
+    def status(self) -> int:
+        return binding.pw_get_device_status(self.ws)
+
+    def close(self) -> None:
+        if getattr(self, "pager", None):
+            binding.pw_pager_destroy(self.pager)
+            self.pager = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -28,8 +28,9 @@
  *
  * Conventions of every entry point.
  *   - Pointers are DEVICE pointers unless the comment says host.  The caller
- *     owns every buffer; the library allocates nothing and keeps no state
- *     besides read-only kernel objects.
+ *     owns every device buffer; the library allocates no device memory.  Its
+ *     only state is the host-side bookkeeping of pager objects (weight pager
+ *     section below); every other entry point is stateless.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls enqueue work and return; results are ready when the stream reaches
  *     that point.  Inputs (including the q table) must not change before that:
@@ -64,6 +65,7 @@ typedef int32_t pw_status;
 #define PW_ERR_ALIGNMENT         -5  /* pointer not 16-byte aligned            */
 #define PW_ERR_HIP               -6  /* a HIP runtime call failed              */
 #define PW_ERR_UNSUPPORTED       -7  /* option not available in this build     */
+#define PW_ERR_OUT_OF_MEMORY     -8  /* pager: no free arena range large enough */
 
 /* device status bits (pw_get_device_status) */
 #define PW_DEV_BAD_EXPERT_ID  0x1u   /* some ids[t][j] outside [0, E)          */
@@ -158,6 +160,91 @@ pw_status pw_dequant_block(const uint32_t* planes, const uint16_t* lut_all,
 /* Wait for `stream`, copy the workspace status word to *flags (host), then
  * clear it.  Returns PW_ERR_HIP if the copy or the wait fails. */
 pw_status pw_get_device_status(void* workspace, uint32_t* flags /* host */, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Weight pager: the Weight Page Table kept on the host, asynchronous page
+ * movement and safe-boundary commits ("Technical summary: PagedWeight",
+ * Core components 1, third bullet: desired bitwidth d_i, committed bitwidth
+ * q_i, pages GPU-resident, CPU-resident or in transfer; Core components 3,
+ * first bullet: pages offloaded to CPU memory and reloaded asynchronously,
+ * bitwidth commits only at safe boundaries).
+ *
+ * A page is one bit plane of one block.  The host holds all eight planes of
+ * every block in pinned memory (caller-owned, never written by the library);
+ * the GPU holds planes 0..q-1 of each block as one extent of a caller-owned
+ * device arena.  The pager owns the device page table the forward reads
+ * (`blocks` [B] and `q` [B], caller-allocated device memory, q zeroed by the
+ * caller before the first commit; for a layer B = 2E and block 2e + m).
+ *
+ * Use:  pw_pager_request(b, d) for the blocks of a plan (host only), then
+ * pw_pager_execute(copy_stream) enqueues the page movement (host-to-device
+ * copies of planes the GPU lacks, device-to-device moves when an extent cannot
+ * grow in place), then pw_pager_commit(stream) at a safe boundary (between
+ * forwards on `stream`) enqueues one kernel that rewrites the page-table
+ * entries and q bytes of every staged block together.  Forwards enqueued on
+ * `stream` before the commit use the old bitwidths and storage, forwards after
+ * it the new ones.  Every forward that reads the page table must run on the
+ * commit stream or be ordered with it.  Arena ranges that a commit frees (a
+ * lowered block's plane suffix, a moved block's old extent) are reused only
+ * after `stream` has passed the commit.  The pager object is host state
+ * (malloc'd bookkeeping, HIP events); it allocates no device memory.  One
+ * pager is not thread-safe: calls on it must not overlap.
+ * ---------------------------------------------------------------------- */
+typedef struct pw_pager pw_pager;
+
+#define PW_PAGE_CPU          0   /* no plane of the block on the GPU           */
+#define PW_PAGE_GPU          1   /* planes 0..committed-1 on the GPU           */
+#define PW_PAGE_IN_TRANSFER  2   /* planes for a staged increase still copying */
+
+typedef struct {
+  int32_t desired;        /* d_i (0 = never requested)                          */
+  int32_t committed;      /* q_i in the device page table (0 = not committed)   */
+  int32_t resident;       /* planes of the committed extent on the GPU          */
+  int32_t pending;        /* bitwidth staged for the next commit, 0 if none     */
+  int32_t state;          /* PW_PAGE_*                                          */
+  int32_t reserved;
+  uint64_t arena_offset;  /* byte offset of the committed extent, UINT64_MAX if none */
+} pw_page_info;
+
+/* Create a pager for `num_blocks` blocks of rows[b] x cols[b] weights (host
+ * arrays; cols % 32 == 0).  `arena` (device, 256-byte aligned, arena_bytes
+ * long) is where resident planes live.  *out receives the handle. */
+pw_status pw_pager_create(int32_t num_blocks, const int32_t* rows /* host */, const int32_t* cols /* host */,
+                          void* arena, size_t arena_bytes, pw_block_desc* blocks, uint8_t* q,
+                          pw_pager** out /* host */);
+
+/* Wait for the pager's outstanding copies and commits, then free it. */
+pw_status pw_pager_destroy(pw_pager* pager);
+
+/* Register block b's storage before its first commit: host_planes is pinned
+ * host memory holding all 8 planes [8][N][K/32]; lut_all is the device table
+ * block [504 N] (fp16 bits, 16-byte aligned), which stays resident. */
+pw_status pw_pager_set_block(pw_pager* pager, int32_t b, const uint32_t* host_planes /* pinned host */,
+                             const uint16_t* lut_all);
+
+/* Set the desired bitwidth d_i (3..8) of block b.  Host bookkeeping only. */
+pw_status pw_pager_request(pw_pager* pager, int32_t b, int32_t desired);
+
+/* Stage every block whose desired bitwidth differs from its committed one:
+ * enqueue on copy_stream the copies of the planes it lacks.  Blocks staged
+ * earlier and not yet committed are left alone.  PW_ERR_OUT_OF_MEMORY when the
+ * arena has no room: the blocks staged before that stay staged, the rest
+ * unchanged (commit lowered blocks first to free their planes). */
+pw_status pw_pager_execute(pw_pager* pager, void* copy_stream);
+
+/* Safe boundary: commit every staged block in one step.  If copies are still
+ * in flight: with wait == 0 nothing is committed (*committed = 0); with
+ * wait != 0 `stream` is made to wait for them on the device (the host does not
+ * block).  *committed (host, may be NULL) receives the number of blocks whose
+ * entries the enqueued commit rewrites. */
+pw_status pw_pager_commit(pw_pager* pager, void* stream, int32_t wait, int32_t* committed /* host */);
+
+/* Host view of block b's page-table entry. */
+pw_status pw_pager_info(const pw_pager* pager, int32_t b, pw_page_info* info /* host */);
+
+/* Arena bytes held by extents, including ranges freed by a commit that the
+ * compute stream has not passed yet (as of the last execute/commit call). */
+size_t pw_pager_arena_used(const pw_pager* pager);
 
 #ifdef __cplusplus
 }
