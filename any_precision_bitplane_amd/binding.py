@@ -94,6 +94,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                      c_void_p, c_void_p, c_void_p, c_size_t, POINTER(PwMoeOptions), c_void_p]),
         "pw_dequant_block": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
         "pw_get_device_status": (c_int32, [c_void_p, POINTER(c_uint32), c_void_p]),
+        "pw_router_topk": (c_int32, [POINTER(PwMoeShape), c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+        "pw_moe_forward_routed": (c_int32, [POINTER(PwMoeShape), c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                            c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                            POINTER(PwMoeOptions), c_void_p]),
         "pw_pager_create": (c_int32, [c_int32, POINTER(c_int32), POINTER(c_int32), c_void_p, c_size_t, c_void_p,
                                       c_void_p, POINTER(c_void_p)]),
         "pw_pager_destroy": (c_int32, [c_void_p]),
@@ -117,7 +122,7 @@ def exported_symbols() -> Sequence[str]:
             "pw_check_shape", "pw_workspace_bytes", "pw_workspace_init", "pw_moe_forward",
             "pw_dequant_block", "pw_get_device_status", "pw_pager_create", "pw_pager_destroy",
             "pw_pager_set_block", "pw_pager_request", "pw_pager_execute", "pw_pager_commit", "pw_pager_info",
-            "pw_pager_arena_used"]
+            "pw_pager_arena_used", "pw_router_topk", "pw_moe_forward_routed"]
 
 
 # ---------------------------------------------------------------------------
@@ -213,6 +218,28 @@ def pw_get_device_status(workspace, stream=None) -> int:
     _check(load().pw_get_device_status(_ptr(workspace), ctypes.byref(flags), _stream(stream)),
            "pw_get_device_status")
     return flags.value
+
+
+# --- router ----------------------------------------------------------------
+def pw_router_topk(shp: PwMoeShape, T: int, x, router_w, ids, w, stat_count=None, stat_mass=None, workspace=None,
+                   stream=None, check: bool = True) -> int:
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = load().pw_router_topk(ctypes.byref(shp), T, _ptr(x), _ptr(router_w), _ptr(ids), _ptr(w), _ptr(stat_count),
+                               _ptr(stat_mass), _ptr(workspace), ws_bytes, _stream(stream))
+    if check:
+        _check(st, "pw_router_topk")
+    return st
+
+
+def pw_moe_forward_routed(shp: PwMoeShape, T: int, x, router_w, blocks, q, y, stat_count, stat_mass, workspace,
+                          opts: Optional[PwMoeOptions] = None, stream=None, check: bool = True) -> int:
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = load().pw_moe_forward_routed(ctypes.byref(shp), T, _ptr(x), _ptr(router_w), _ptr(blocks), _ptr(q), _ptr(y),
+                                      _ptr(stat_count), _ptr(stat_mass), _ptr(workspace), ws_bytes,
+                                      ctypes.byref(opts) if opts is not None else None, _stream(stream))
+    if check:
+        _check(st, "pw_moe_forward_routed")
+    return st
 
 
 # --- weight pager ----------------------------------------------------------

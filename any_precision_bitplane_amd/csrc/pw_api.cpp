@@ -156,6 +156,48 @@ pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T, const uint16_t* x
   return hip_status(e);
 }
 
+pw_status pw_router_topk(const pw_moe_shape* shape, int32_t T, const uint16_t* x, const uint16_t* router_w,
+                         int32_t* ids, float* w, uint32_t* stat_count, float* stat_mass, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  pw_status st = check_shape(shape, T);
+  if (st != PW_OK) return st;
+  if (shape->top_k > kMaxRouterTopK) return PW_ERR_UNSUPPORTED_SHAPE;
+  if (T == 0) return PW_OK;
+  if (!x || !router_w || !ids || !w || !workspace) return PW_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(ids, 4) || !aligned(w, 4) ||
+      !aligned(stat_count, 4) || !aligned(stat_mass, 4) || !aligned(workspace, kAlign))
+    return PW_ERR_ALIGNMENT;
+  const WsLayout L = ws_layout(shape->hidden, shape->inter, shape->num_experts, shape->top_k, T);
+  if (workspace_bytes < L.total) return PW_ERR_WORKSPACE;
+  float* logits = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + L.rlogits);
+  return hip_status(launch_router(x, router_w, T, shape->hidden, shape->num_experts, shape->top_k, logits, ids, w,
+                                  stat_count, stat_mass, (hipStream_t)stream));
+}
+
+pw_status pw_moe_forward_routed(const pw_moe_shape* shape, int32_t T, const uint16_t* x, const uint16_t* router_w,
+                                const pw_block_desc* blocks, const uint8_t* q, uint16_t* y, uint32_t* stat_count,
+                                float* stat_mass, void* workspace, size_t workspace_bytes, const pw_moe_options* opts,
+                                void* stream) {
+  pw_status st = check_shape(shape, T);
+  if (st != PW_OK) return st;
+  if (T == 0) return PW_OK;
+  if (!workspace) return PW_ERR_INVALID_ARG;
+  if (!aligned(workspace, kAlign)) return PW_ERR_ALIGNMENT;
+  const WsLayout L = ws_layout(shape->hidden, shape->inter, shape->num_experts, shape->top_k, T);
+  if (workspace_bytes < L.total) return PW_ERR_WORKSPACE;
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  int32_t* ids = reinterpret_cast<int32_t*>(ws + L.rids);
+  float* w = reinterpret_cast<float*>(ws + L.rw);
+  // argument checks of the forward before anything is enqueued
+  if (!blocks || !q || !y) return PW_ERR_INVALID_ARG;
+  if (!aligned(y, 16) || !aligned(blocks, 8)) return PW_ERR_ALIGNMENT;
+  if (opts && opts->path != PW_PATH_AUTO && opts->path != PW_PATH_GEMV && opts->path != PW_PATH_MFMA)
+    return PW_ERR_INVALID_ARG;
+  st = pw_router_topk(shape, T, x, router_w, ids, w, stat_count, stat_mass, workspace, workspace_bytes, stream);
+  if (st != PW_OK) return st;
+  return pw_moe_forward(shape, T, x, ids, w, blocks, q, y, workspace, workspace_bytes, opts, stream);
+}
+
 pw_status pw_dequant_block(const uint32_t* planes, const uint16_t* lut_all, int32_t N, int32_t K, int32_t q,
                            uint16_t* w_out, void* stream) {
   if (!planes || !lut_all || !w_out || N <= 0 || K <= 0) return PW_ERR_INVALID_ARG;

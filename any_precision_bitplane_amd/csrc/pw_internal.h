@@ -17,6 +17,7 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 constexpr int kMfmaTileM = 256;   // tokens per MFMA tile
+constexpr int kMaxRouterTopK = 64; // the router's top-k kernel keeps slot j in lane j
 
 inline int mtile_bound(int E, int T, int k) {
   const int slots = T * k;
@@ -50,6 +51,9 @@ struct WsLayout {
   size_t mtiles = 0;        // int32 [2 * mtile_bound] MFMA token tiles
   size_t h = 0;             // fp16  [T*k][I] activations between the products
   size_t o = 0;             // fp32  [kparts][T*k][H] expert outputs by slot (t*k + j), before the combine
+  size_t rlogits = 0;       // fp32  [T][E]   router logits
+  size_t rids = 0;          // int32 [T*k]    router expert ids (routed forward)
+  size_t rw = 0;            // fp32  [T*k]    router weights (routed forward)
   size_t total = 0;
 };
 
@@ -66,6 +70,9 @@ inline WsLayout ws_layout(int H, int I, int E, int k, int T) {
   L.mtiles = off;  off = align_up(off + sizeof(int32_t) * 2 * mtile_bound(E, T, k), kAlign);
   L.h = off;       off = align_up(off + sizeof(uint16_t) * slots * I, kAlign);
   L.o = off;       off = align_up(off + sizeof(float) * kp * slots * H, kAlign);
+  L.rlogits = off; off = align_up(off + sizeof(float) * (size_t)T * E, kAlign);
+  L.rids = off;    off = align_up(off + sizeof(int32_t) * slots, kAlign);
+  L.rw = off;      off = align_up(off + sizeof(float) * slots, kAlign);
   L.total = off;
   return L;
 }
@@ -120,6 +127,8 @@ hipError_t launch_combine(const float* o, const float* w, const int32_t* inv, in
 hipError_t launch_dequant(const uint32_t* planes, const uint16_t* lut_all, int N, int K, int q,
                           uint16_t* out, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_router(const uint16_t* x, const uint16_t* wr, int T, int H, int E, int k, float* logits,
+                         int32_t* ids, float* w, uint32_t* count, float* mass, hipStream_t s);
 hipError_t launch_status_clear(uint32_t* status, hipStream_t s);
 
 }  // namespace pw

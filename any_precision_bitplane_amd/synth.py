@@ -108,6 +108,11 @@ def draw_x(seed: int, T: int, H: int) -> np.ndarray:
     return _rng(seed, 4).standard_normal((T, H)).astype(np.float16)
 
 
+def draw_router_weights(seed: int, E: int, H: int) -> np.ndarray:
+    """Router matrix fp16 [E][H] ~ N(0, 1/H), so logits of N(0, 1) tokens are about N(0, 1)."""
+    return (_rng(seed, 6).standard_normal((E, H)) / np.sqrt(H)).astype(np.float16)
+
+
 def _softmax_rows(z: np.ndarray) -> np.ndarray:
     z = z - z.max(axis=1, keepdims=True)
     ez = np.exp(z)

@@ -161,6 +161,34 @@ pw_status pw_dequant_block(const uint32_t* planes, const uint16_t* lut_all,
  * clear it.  Returns PW_ERR_HIP if the copy or the wait fails. */
 pw_status pw_get_device_status(void* workspace, uint32_t* flags /* host */, void* stream);
 
+/* Router and online routing statistics ("Technical summary: PagedWeight",
+ * Core components 2, second bullet: each expert's routing mass -- how often it
+ * is selected and with what weight -- is tracked online).  The router is the
+ * top-k softmax router of a routed MoE layer:
+ *     logits[t][e] = sum_h x[t][h] * router_w[e][h]   (fp16 inputs, fp32 sums)
+ *     ids[t][0..k)  = the k largest logits, descending; lower id first on ties
+ *     w[t][j]       = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the selected
+ * and, if stat_count / stat_mass are non-NULL, for every slot
+ *     stat_count[ids[t][j]] += 1,  stat_mass[ids[t][j]] += w[t][j]
+ * (device uint32 [E] and fp32 [E], accumulated across calls; the caller
+ * zeroes them to start a window; mass is an fp32 atomic sum, so its last bits
+ * depend on the order the slots arrive in).
+ *   x fp16 [T][H], router_w fp16 [E][H] (both 16-byte aligned);
+ *   ids int32 [T][k], w fp32 [T][k] outputs; k <= 64 (else
+ *   PW_ERR_UNSUPPORTED_SHAPE); workspace as for pw_moe_forward (the logits
+ *   live in it).  T == 0 returns PW_OK and enqueues nothing.  Two launches. */
+pw_status pw_router_topk(const pw_moe_shape* shape /* host */, int32_t T, const uint16_t* x,
+                         const uint16_t* router_w, int32_t* ids, float* w, uint32_t* stat_count,
+                         float* stat_mass, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Router + fused mixed-precision layer in one call: pw_router_topk into the
+ * workspace (ids and weights are not returned), then pw_moe_forward on them.
+ * Arguments as for those two calls. */
+pw_status pw_moe_forward_routed(const pw_moe_shape* shape /* host */, int32_t T, const uint16_t* x,
+                                const uint16_t* router_w, const pw_block_desc* blocks, const uint8_t* q,
+                                uint16_t* y, uint32_t* stat_count, float* stat_mass, void* workspace,
+                                size_t workspace_bytes, const pw_moe_options* opts, void* stream);
+
 /* ------------------------------------------------------------------------
  * Weight pager: the Weight Page Table kept on the host, asynchronous page
  * movement and safe-boundary commits ("Technical summary: PagedWeight",

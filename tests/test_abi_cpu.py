@@ -116,3 +116,25 @@ def test_status_and_init_reject_bad_arguments(lib):
     assert lib.pw_get_device_status(1 << 20, None, None) == B.PW_ERR_INVALID_ARG
     assert lib.pw_workspace_init(None, 1024, None) == B.PW_ERR_INVALID_ARG
     assert lib.pw_workspace_init((1 << 20) + 16, 1024, None) == B.PW_ERR_ALIGNMENT
+
+
+def test_router_rejects_bad_arguments_before_launch(lib):
+    p = 1 << 20
+
+    def route(shp, T, x=p, wr=p, ids=p, w=p, cnt=None, mass=None, ws=p, ws_bytes=1 << 40):
+        return lib.pw_router_topk(ctypes.byref(shp), T, x, wr, ids, w, cnt, mass, ws, ws_bytes, None)
+
+    shp = B.shape(256, 512, 8, 2)
+    assert route(shp, 0) == B.PW_OK
+    assert route(shp, 4, wr=None) == B.PW_ERR_INVALID_ARG
+    assert route(shp, 4, ids=None) == B.PW_ERR_INVALID_ARG
+    assert route(shp, 4, x=p + 2) == B.PW_ERR_ALIGNMENT
+    assert route(shp, 4, cnt=p + 2) == B.PW_ERR_ALIGNMENT
+    assert route(shp, 4, ws_bytes=100) == B.PW_ERR_WORKSPACE
+    assert route(B.shape(256, 512, 128, 65), 4) == B.PW_ERR_UNSUPPORTED_SHAPE   # k > 64
+    assert route(B.shape(256, 512, 8, 9), 4) == B.PW_ERR_UNSUPPORTED_SHAPE      # k > E
+    f = lib.pw_moe_forward_routed
+    assert f(ctypes.byref(shp), 4, p, p, None, p, p, None, None, p, 1 << 40, None, None) == B.PW_ERR_INVALID_ARG
+    assert f(ctypes.byref(shp), 4, p, p, p, p, p + 2, None, None, p, 1 << 40, None, None) == B.PW_ERR_ALIGNMENT
+    assert f(ctypes.byref(shp), 4, p, p, p, p, p, None, None, p, 100, None, None) == B.PW_ERR_WORKSPACE
+    assert f(ctypes.byref(shp), 0, p, p, p, p, p, None, None, p, 1 << 40, None, None) == B.PW_OK
