@@ -64,6 +64,13 @@ class PwPageInfo(ctypes.Structure):
                 ("state", c_int32), ("reserved", c_int32), ("arena_offset", ctypes.c_uint64)]
 
 
+class PwPlanProblem(ctypes.Structure):
+    _fields_ = [("num_blocks", c_int32), ("num_experts", c_int32), ("expert_of", c_void_p),
+                ("plane_bytes", c_void_p), ("sensitivity", c_void_p), ("correction", c_void_p),
+                ("routing_mass", c_void_p), ("hot_fraction", ctypes.c_double), ("floor_cold", c_int32),
+                ("floor_hot", c_int32), ("hot_multiplier", ctypes.c_float), ("reserved", c_int32)]
+
+
 class PwError(RuntimeError):
     def __init__(self, status: int, what: str = ""):
         self.status = status
@@ -99,6 +106,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "pw_moe_forward_routed": (c_int32, [POINTER(PwMoeShape), c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                             c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                             POINTER(PwMoeOptions), c_void_p]),
+        "pw_plan_bitwidths": (c_int32, [POINTER(PwPlanProblem), c_void_p, ctypes.c_int64, c_void_p,
+                                        POINTER(ctypes.c_int64), POINTER(c_int32)]),
         "pw_pager_create": (c_int32, [c_int32, POINTER(c_int32), POINTER(c_int32), c_void_p, c_size_t, c_void_p,
                                       c_void_p, POINTER(c_void_p)]),
         "pw_pager_destroy": (c_int32, [c_void_p]),
@@ -122,7 +131,7 @@ def exported_symbols() -> Sequence[str]:
             "pw_check_shape", "pw_workspace_bytes", "pw_workspace_init", "pw_moe_forward",
             "pw_dequant_block", "pw_get_device_status", "pw_pager_create", "pw_pager_destroy",
             "pw_pager_set_block", "pw_pager_request", "pw_pager_execute", "pw_pager_commit", "pw_pager_info",
-            "pw_pager_arena_used", "pw_router_topk", "pw_moe_forward_routed"]
+            "pw_pager_arena_used", "pw_router_topk", "pw_moe_forward_routed", "pw_plan_bitwidths"]
 
 
 # ---------------------------------------------------------------------------
@@ -240,6 +249,32 @@ def pw_moe_forward_routed(shp: PwMoeShape, T: int, x, router_w, blocks, q, y, st
     if check:
         _check(st, "pw_moe_forward_routed")
     return st
+
+
+# --- planner ----------------------------------------------------------------
+def pw_plan_bitwidths(q_cur, plane_bytes, expert_of, sensitivity, correction=None, routing_mass=None,
+                      hot_fraction: float = 0.0, floor_cold: int = 3, floor_hot: int = 3,
+                      hot_multiplier: float = 1.0, budget_bytes: int = 0, check: bool = True):
+    """Host arrays (numpy) in, (status, q_out int32 [B], plane bytes, fits) out."""
+    import numpy as np
+    q_cur = np.ascontiguousarray(q_cur, dtype=np.int32)
+    pb = np.ascontiguousarray(plane_bytes, dtype=np.int64)
+    eo = np.ascontiguousarray(expert_of, dtype=np.int32)
+    S = np.ascontiguousarray(sensitivity, dtype=np.float32).reshape(len(q_cur), 6)
+    R = None if correction is None else np.ascontiguousarray(correction, dtype=np.float32).reshape(len(q_cur), 6)
+    M = None if routing_mass is None else np.ascontiguousarray(routing_mass, dtype=np.float32)
+    E = int(eo.max()) + 1 if M is None else len(M)
+    prob = PwPlanProblem(len(q_cur), E, eo.ctypes.data, pb.ctypes.data, S.ctypes.data,
+                         None if R is None else R.ctypes.data, None if M is None else M.ctypes.data,
+                         float(hot_fraction), int(floor_cold), int(floor_hot), float(hot_multiplier), 0)
+    out = np.zeros(len(q_cur), dtype=np.int32)
+    used = ctypes.c_int64(0)
+    fits = c_int32(0)
+    st = load().pw_plan_bitwidths(ctypes.byref(prob), q_cur.ctypes.data, int(budget_bytes), out.ctypes.data,
+                                  ctypes.byref(used), ctypes.byref(fits))
+    if check:
+        _check(st, "pw_plan_bitwidths")
+    return st, out, used.value, bool(fits.value)
 
 
 # --- weight pager ----------------------------------------------------------

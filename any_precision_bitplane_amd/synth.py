@@ -113,6 +113,15 @@ def draw_router_weights(seed: int, E: int, H: int) -> np.ndarray:
     return (_rng(seed, 6).standard_normal((E, H)) / np.sqrt(H)).astype(np.float16)
 
 
+def draw_sensitivity(seed: int, nblocks: int) -> np.ndarray:
+    """Synthetic offline sensitivity scores fp32 [nblocks][6] for bitwidths 3..8:
+    positive, decreasing in the bitwidth, zero-free (stand-ins for Hessian-weighted
+    scores, which need trained weights)."""
+    rng = _rng(seed, 7)
+    steps = rng.exponential(1.0, size=(nblocks, 6)) * rng.lognormal(0.0, 1.0, size=(nblocks, 1))
+    return np.cumsum(steps[:, ::-1], axis=1)[:, ::-1].astype(np.float32)
+
+
 def _softmax_rows(z: np.ndarray) -> np.ndarray:
     z = z - z.max(axis=1, keepdims=True)
     ez = np.exp(z)

@@ -190,6 +190,51 @@ pw_status pw_moe_forward_routed(const pw_moe_shape* shape /* host */, int32_t T,
                                 size_t workspace_bytes, const pw_moe_options* opts, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Quality-aware bitwidth planner (host code; "Technical summary: PagedWeight",
+ * Core components 2: offline sensitivity per block, online routing statistics
+ * with hot experts protected by higher floors and damage multipliers, a
+ * prompt-specific correction, and a greedy choice of the reductions with the
+ * least damage per byte saved until a memory target is met).
+ *
+ *   D_b(q) = mu_b * (S_b(q) + R_b(q))   damage of block b at bitwidth q
+ *   mu_b   = hot_multiplier for blocks of hot experts, else 1
+ *   hot    = the ceil(hot_fraction * E) experts with the largest positive
+ *            routing mass (equal masses: lower expert id)
+ *   floor  = floor_hot for blocks of hot experts, else floor_cold; a block
+ *            below its floor is raised to it first
+ * If the resident plane bytes sum_b q_b * plane_bytes[b] exceed the budget,
+ * one-bit reductions are taken in increasing (D_b(q-1) - D_b(q)) /
+ * plane_bytes[b] (equal: lower b) until they fit or every block sits on its
+ * floor.  Otherwise one-bit restorations are taken in decreasing
+ * (D_b(q) - D_b(q+1)) / plane_bytes[b] (equal: lower b) among the steps that
+ * still fit, up to 8 bits.  Costs are evaluated in fp64 exactly as written.
+ * The result feeds pw_pager_request.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t num_blocks;          /* B                                                  */
+  int32_t num_experts;         /* E                                                  */
+  const int32_t* expert_of;    /* host [B]: expert of block b, in [0, E)             */
+  const int64_t* plane_bytes;  /* host [B]: bytes of one bit plane of block b (> 0)  */
+  const float* sensitivity;    /* host [B][6]: offline score S_b(q), column q - 3    */
+  const float* correction;     /* host [B][6]: prompt correction R_b(q); NULL = 0    */
+  const float* routing_mass;   /* host [E]; NULL = no expert is hot                  */
+  double hot_fraction;
+  int32_t floor_cold;          /* 3..8 */
+  int32_t floor_hot;           /* 3..8 */
+  float hot_multiplier;
+  int32_t reserved;
+} pw_plan_problem;
+
+/* Plan bitwidths for a plane-byte budget.  q_cur (host [B], 3..8): current
+ * desired bitwidths; q_out (host [B]) receives the plan; *plane_bytes_out
+ * (may be NULL) the resident plane bytes of the plan; *fits (may be NULL) 1 if
+ * they fit the budget, 0 if the floors alone exceed it (the plan then holds
+ * every block at its floor).  Pure host computation; no device access. */
+pw_status pw_plan_bitwidths(const pw_plan_problem* problem /* host */, const int32_t* q_cur /* host */,
+                            int64_t budget_bytes, int32_t* q_out /* host */, int64_t* plane_bytes_out /* host */,
+                            int32_t* fits /* host */);
+
+/* ------------------------------------------------------------------------
  * Weight pager: the Weight Page Table kept on the host, asynchronous page
  * movement and safe-boundary commits ("Technical summary: PagedWeight",
  * Core components 1, third bullet: desired bitwidth d_i, committed bitwidth

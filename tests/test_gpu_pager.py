@@ -253,3 +253,49 @@ def test_captured_graph_follows_commits(torch, tiny, static):
             torch.cuda.synchronize()
     assert paged.status() == 0
     paged.close()
+
+
+def test_routing_statistics_plan_and_commit(torch, tiny, static):
+    say("pager: tiny layer, router statistics -> planner at 55% of the 8-bit plane bytes -> pager -> forward")
+    import oracle.routing_oracle as ro
+    wl = tiny.wl
+    paged = make_paged(tiny, 2 * full_arena(tiny))
+    copy = torch.cuda.Stream()
+    paged.request(np.full(tiny.q.shape, 8, np.uint8))
+    paged.execute(copy)
+    paged.commit(wait=True)
+    # route the tokens on the GPU, collecting the routing statistics
+    wr = synth.draw_router_weights(wl.seed, wl.E, wl.H)
+    wrd = torch.from_numpy(wr).to(paged.device)
+    ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device=paged.device)
+    w = torch.empty((wl.T, wl.k), dtype=torch.float32, device=paged.device)
+    cnt = torch.zeros(wl.E, dtype=torch.int32, device=paged.device)
+    mass = torch.zeros(wl.E, dtype=torch.float32, device=paged.device)
+    B.pw_router_topk(paged.shape, wl.T, paged.x, wrd, ids, w, cnt, mass, paged.ws)
+    torch.cuda.synchronize()
+    pb = np.array(plane_bytes(tiny), np.int64)
+    budget = int(0.55 * (8 * pb).sum())
+    sens = synth.draw_sensitivity(wl.seed, 2 * wl.E)
+    st, plan, used, fits = B.pw_plan_bitwidths(np.full(2 * wl.E, 8), pb, np.arange(2 * wl.E) // 2, sens,
+                                               routing_mass=mass.cpu().numpy(), hot_fraction=0.25, floor_cold=3,
+                                               floor_hot=6, hot_multiplier=2.0, budget_bytes=budget)
+    assert fits and used <= budget
+    hot = np.argsort(-mass.cpu().numpy(), kind="stable")[:2]
+    assert all(plan[2 * e + m] >= 6 for e in hot for m in (0, 1))
+    paged.request(plan.reshape(-1, 2))
+    paged.execute(copy)
+    paged.commit(wait=True)
+    paged.ids, paged.w = ids, w
+    y = paged_y(torch, paged)
+    oids, ow, _ = ro.route(tiny.x, wr, wl.k)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    ref = orc.moe_forward_layer(tiny, q=plan.reshape(-1, 2).astype(np.uint8), ids=oids, w=ow.astype(np.float32))
+    got = y.view(np.float16).astype(np.float64)
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    mx = float(np.max(np.abs(got - ref)))
+    say(f"  plan {plan.tolist()} ({used} of {int((8 * pb).sum())} plane bytes): rel_l2={rel:.3e} max_abs={mx:.3e}")
+    assert rel <= REL_L2 and mx <= MAX_ABS
+    torch.cuda.synchronize()
+    paged.execute(copy)
+    assert B.pw_pager_arena_used(paged.pager) == sum(rnd(int(plan[b]) * int(pb[b])) for b in range(len(pb)))
+    paged.close()
