@@ -102,6 +102,120 @@ def cpu_baseline(layer, budget_s: float):
                       f"{el:.1f} s, fp64 numpy; cores = BLAS threads"}
 
 
+def timed_ms(evs, stream, fn, n: int) -> float:
+    """Average ms per call of fn() over n calls, from HIP events on `stream`."""
+    a, b = evs.create(), evs.create()
+    evs.record(a, stream.cuda_stream)
+    for i in range(n):
+        fn(i)
+    evs.record(b, stream.cuda_stream)
+    return evs.elapsed_ms(a, b) / n
+
+
+def next_rows(layer, dev, copies, opts, stream, evs, steps: int):
+    """Secondary measurements of the parts around the fused layer, on the same
+    layer: the router (and the routed layer call), a captured HIP graph of
+    consecutive layer calls, and the pager's asynchronous plane reload."""
+    import torch
+    from any_precision_bitplane_amd import binding as B
+    from any_precision_bitplane_amd import synth
+    from any_precision_bitplane_amd.device import PagedLayer
+    wl = layer.wl
+    out = {}
+    # router: logits + top-k + statistics, and router + layer in one call
+    wr = torch.from_numpy(synth.draw_router_weights(wl.seed, wl.E, wl.H)).to(dev.device)
+    ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device=dev.device)
+    w = torch.empty((wl.T, wl.k), dtype=torch.float32, device=dev.device)
+    cnt = torch.zeros(wl.E, dtype=torch.int32, device=dev.device)
+    mass = torch.zeros(wl.E, dtype=torch.float32, device=dev.device)
+    y2 = torch.empty_like(dev.y)
+    route = lambda i: B.pw_router_topk(dev.shape, wl.T, dev.x, wr, ids, w, cnt, mass, dev.ws, stream=stream)
+    routed = lambda i: B.pw_moe_forward_routed(dev.shape, wl.T, dev.x, wr, dev.blocks[i % copies], dev.q, y2, cnt,
+                                               mass, dev.ws, opts=opts, stream=stream)
+    for i in range(10):
+        routed(i)
+    torch.cuda.synchronize()
+    out["router_us"] = 1e3 * timed_ms(evs, stream, route, steps)
+    out["routed_layer_us"] = 1e3 * timed_ms(evs, stream, routed, steps)
+    torch.cuda.synchronize()
+    # HIP graph of G consecutive layer calls (rotating storage copies), replayed
+    G = 16
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for i in range(G):
+            dev.forward(opts, copy=i % copies)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(G):
+            dev.forward(opts, copy=i % copies)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // G)
+    out["graph_layer_us"] = 1e3 * timed_ms(evs, stream, lambda i: g.replay(), reps) / G
+    out["eager_layer_us"] = 1e3 * timed_ms(evs, stream, lambda i: dev.forward(opts, copy=i % copies, stream=stream),
+                                           steps)
+    del g
+    torch.cuda.synchronize()
+    # pager: all blocks lowered to 3 bits, then the layer's bitwidths reloaded
+    # from pinned host memory on a copy stream while layer calls run
+    full = sum(8 * (2 * wl.I * wl.H if b % 2 == 0 else wl.H * wl.I) // 8 for b in range(2 * wl.E))
+    paged = PagedLayer(layer, 2 * full + (1 << 20), device=dev.device)
+    copy = torch.cuda.Stream()
+    paged.request(layer.q)
+    paged.execute(copy)
+    paged.commit(stream, wait=True)
+    paged.request(np.full(layer.q.shape, 3, np.uint8))
+    paged.execute(copy)
+    paged.commit(stream, wait=True)
+    torch.cuda.synchronize()
+    pfwd = lambda i: paged.forward(opts, stream=stream)
+    for i in range(5):
+        pfwd(i)
+    torch.cuda.synchronize()
+    alone_us = 1e3 * timed_ms(evs, stream, pfwd, steps)
+    torch.cuda.synchronize()
+    paged.request(layer.q)
+    a, b = evs.create(), evs.create()
+    evs.record(a, copy.cuda_stream)
+    paged.execute(copy)
+    evs.record(b, copy.cuda_stream)
+    c, d = evs.create(), evs.create()
+    evs.record(c, stream.cuda_stream)
+    n_during = 0
+    while True:   # layer calls enqueued while the copies are in flight
+        pfwd(n_during)
+        n_during += 1
+        if n_during >= 20 and (B.pw_pager_info(paged.pager, 0).state != B.PW_PAGE_IN_TRANSFER or n_during >= 400):
+            break
+    evs.record(d, stream.cuda_stream)
+    reload_ms = evs.elapsed_ms(a, b)
+    during_us = 1e3 * evs.elapsed_ms(c, d) / n_during
+    paged.commit(stream, wait=True)
+    torch.cuda.synchronize()
+    pb = [(2 * wl.I * wl.H if b % 2 == 0 else wl.H * wl.I) // 8 for b in range(2 * wl.E)]
+    moved = sum((int(layer.q.reshape(-1)[b]) - 3) * pb[b] for b in range(2 * wl.E))
+    out["pager"] = {"reload_bytes": moved, "reload_ms": reload_ms, "reload_h2d_gbs": moved / (reload_ms * 1e-3) / 1e9,
+                    "layer_us_alone_q3": alone_us, "layer_us_during_reload": during_us,
+                    "layer_calls_during_reload": n_during}
+    paged.close()
+    # planner: host time for 24 layers of this shape
+    nb = 24 * 2 * wl.E
+    sens = synth.draw_sensitivity(wl.seed, nb)
+    pbs = np.array(pb * 24, np.int64)
+    t0 = time.perf_counter()
+    _, plan, used, fits = B.pw_plan_bitwidths(np.full(nb, 8), pbs, np.arange(nb) // 2, sens,
+                                              routing_mass=np.tile(mass.cpu().numpy(), 24), hot_fraction=0.2,
+                                              floor_hot=6, hot_multiplier=2.0,
+                                              budget_bytes=int(0.5 * (8 * pbs).sum()))
+    out["planner_ms_24_layers"] = 1e3 * (time.perf_counter() - t0)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,6 +229,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes (counter calibration)")
+    ap.add_argument("--no-extras", action="store_true", help="skip the router / graph / pager measurements")
     ap.add_argument("--uniform-q", type=int, default=0,
                     help="commit one bitwidth for every block (mixed-vs-uniform comparison)")
     args = ap.parse_args()
@@ -255,6 +370,8 @@ def main():
             "avg_launch_ms": dom_ms,
         },
     }
+    if not args.no_extras and not args.uniform_q:
+        rec["around_the_layer"] = next_rows(layer, dev, copies, opts, stream, evs, args.steps)
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(layer, args.cpu_budget)
     print(json.dumps(rec), flush=True)
