@@ -48,3 +48,14 @@ def module_bytes(q, ids, H, I, E, T, k, module: int) -> int:
 
 def layer_flops(T, k, H, I) -> int:
     return 6 * T * k * H * I
+
+
+def module_flops(T, k, H, I, module: int) -> int:
+    """Flops of one product: 2 per weight per routed slot (gate_up 2I x H, down H x I)."""
+    return 2 * T * k * (2 * I * H if module == 0 else H * I)
+
+
+def bound(flops: float, nbytes: float) -> str:
+    """'mfma' when the arithmetic intensity exceeds the ridge point of the two peaks."""
+    ridge = MFMA_FP16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    return "mfma" if flops / max(nbytes, 1) > ridge else "hbm"

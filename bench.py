@@ -313,12 +313,18 @@ def main():
     dn_ms = float(stage_avg[B.PW_STAGE_DOWN])
     fwd_ms = gpu_step_ms
 
-    # dominant kernel: the larger of the two expert products
-    if gu_bytes / max(gu_ms, 1e-9) >= 0 and gu_ms >= dn_ms:
-        dom, dom_bytes, dom_ms = "gate_up", gu_bytes, gu_ms
+    # dominant kernel: the longer of the two expert products; priced against
+    # HBM bandwidth or fp16 MFMA throughput, whichever bounds its work
+    if gu_ms >= dn_ms:
+        dom, dom_bytes, dom_ms, dom_m = "gate_up", gu_bytes, gu_ms, 0
     else:
-        dom, dom_bytes, dom_ms = "down", dn_bytes, dn_ms
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+        dom, dom_bytes, dom_ms, dom_m = "down", dn_bytes, dn_ms, 1
+    dom_flops = RL.module_flops(T, k, H, I, dom_m)
+    dom_bound = RL.bound(dom_flops, dom_bytes)
+    if dom_bound == "mfma":
+        achieved, peak, unit = dom_flops / (dom_ms * 1e-3) / 1e12, RL.MFMA_FP16_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = dom_bytes / (dom_ms * 1e-3) / 1e9, RL.HBM_PEAK_GBS, "GB/s"
 
     status = dev.status()
     y = dev.y.float().cpu().numpy()
@@ -344,7 +350,10 @@ def main():
             "mean_q_routed": float(np.mean([layer.q[e] for e in routed])),
             "storage_copies_rotated": copies,
             "path": ["auto", "gemv", "mfma"][args.path],
-            "bitwidths": f"uniform {args.uniform_q}" if args.uniform_q else "per block, uniform in 3..8",
+            "bitwidths": (f"uniform {args.uniform_q}" if args.uniform_q else
+                          {"uniform38": "per block, uniform in 3..8",
+                           "hot8": "hottest 20% of experts at 8 bits, others uniform in {3,4,5}",
+                           "skewed": "per module a permutation of [8,8,4,4,4,3,3,3]"}.get(wl.qmode, wl.qmode)),
         },
         "layer": {
             "algorithmic_bytes": lbytes,
@@ -356,17 +365,19 @@ def main():
             "hbm_frac_gpu_timeline": lbytes / (fwd_ms * 1e-3) / 1e9 / RL.HBM_PEAK_GBS,
             "hbm_gbs_wall": lbytes / (ms_per_step * 1e-3) / 1e9,
             "tflops_wall": flops / (ms_per_step * 1e-3) / 1e12,
+            "mfma_frac_wall": flops / (ms_per_step * 1e-3) / 1e12 / RL.MFMA_FP16_PEAK_TFLOPS,
             "output_finite_and_status_clear": ok,
         },
         "roofline": {
             "kernel": dom,
-            "bound": "hbm",
+            "bound": dom_bound,
             "achieved": achieved,
-            "peak": RL.HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved / RL.HBM_PEAK_GBS,
+            "peak": peak,
+            "unit": unit,
+            "frac": achieved / peak,
             "traffic": measured_traffic(dom, args.workload) if not (args.uniform_q or args.T) else None,
             "algorithmic_bytes_per_launch": dom_bytes,
+            "algorithmic_flops_per_launch": dom_flops,
             "avg_launch_ms": dom_ms,
         },
     }
