@@ -38,6 +38,7 @@ PW_DEV_BAD_BITWIDTH = 0x2
 PW_PATH_AUTO = 0
 PW_PATH_GEMV = 1
 PW_PATH_MFMA = 2
+PW_PATH_MGEMV = 3
 
 PW_STAGE_ROUTE = 0
 PW_STAGE_GATE_UP = 1
@@ -56,7 +57,8 @@ class PwBlockDesc(ctypes.Structure):
 
 class PwMoeOptions(ctypes.Structure):
     _fields_ = [("path", c_int32), ("mfma_min_tokens", c_int32),
-                ("stage_events", c_void_p * (PW_NUM_STAGES + 1))]
+                ("stage_events", c_void_p * (PW_NUM_STAGES + 1)),
+                ("mgemv_min_tokens", c_int32), ("reserved", c_int32)]
 
 
 class PwPageInfo(ctypes.Structure):
@@ -194,10 +196,12 @@ def pw_workspace_init(workspace, stream=None) -> None:
                                     _stream(stream)), "pw_workspace_init")
 
 
-def make_options(path: int = PW_PATH_AUTO, mfma_min_tokens: int = 0, events=None) -> PwMoeOptions:
+def make_options(path: int = PW_PATH_AUTO, mfma_min_tokens: int = 0, events=None,
+                 mgemv_min_tokens: int = 0) -> PwMoeOptions:
     o = PwMoeOptions()
     o.path = path
     o.mfma_min_tokens = mfma_min_tokens
+    o.mgemv_min_tokens = mgemv_min_tokens
     if events is not None:
         for i, ev in enumerate(events):
             o.stage_events[i] = ev

@@ -15,8 +15,10 @@ using namespace pw;
 
 namespace {
 
-// AUTO: experts with at least this many routed tokens take the MFMA kernels.
-constexpr int kDefaultMfmaMinTokens = 8;
+// AUTO: experts with at least this many routed tokens take the matrix-core
+// GEMV kernels, and from the second threshold on the MFMA kernels.
+constexpr int kDefaultMgemvMinTokens = 4;
+constexpr int kDefaultMfmaMinTokens = 64;
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -88,7 +90,8 @@ pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T, const uint16_t* x
   if (T == 0) return PW_OK;
   if (!x || !ids || !w || !blocks || !q || !y || !workspace) return PW_ERR_INVALID_ARG;
   const int path = opts ? opts->path : PW_PATH_AUTO;
-  if (path != PW_PATH_AUTO && path != PW_PATH_GEMV && path != PW_PATH_MFMA) return PW_ERR_INVALID_ARG;
+  if (path != PW_PATH_AUTO && path != PW_PATH_GEMV && path != PW_PATH_MFMA && path != PW_PATH_MGEMV)
+    return PW_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ids, 4) || !aligned(w, 4) || !aligned(blocks, 8) ||
       !aligned(workspace, kAlign))
     return PW_ERR_ALIGNMENT;
@@ -97,17 +100,31 @@ pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T, const uint16_t* x
   const WsLayout L = ws_layout(H, I, E, k, T);
   if (workspace_bytes < L.total) return PW_ERR_WORKSPACE;
 
-  int thresh;
-  if (path == PW_PATH_GEMV) thresh = INT_MAX;
-  else if (path == PW_PATH_MFMA) thresh = 0;
-  else thresh = (opts && opts->mfma_min_tokens > 0) ? opts->mfma_min_tokens : kDefaultMfmaMinTokens;
+  // Token-count bands per expert: GEMV [0, b1), matrix-core GEMV [b1, b2),
+  // MFMA [b2, inf).  A band whose lower end no expert can reach (an expert
+  // gets at most T tokens unless a token lists it twice) is not launched and
+  // the band below it takes its experts.
+  int b1, b2;
+  if (path == PW_PATH_GEMV) b1 = b2 = INT_MAX;
+  else if (path == PW_PATH_MFMA) b1 = b2 = 0;
+  else if (path == PW_PATH_MGEMV) { b1 = 0; b2 = INT_MAX; }
+  else {
+    b2 = (opts && opts->mfma_min_tokens > 0) ? opts->mfma_min_tokens : kDefaultMfmaMinTokens;
+    b1 = (opts && opts->mgemv_min_tokens > 0) ? opts->mgemv_min_tokens : kDefaultMgemvMinTokens;
+    if (b1 > b2) b1 = b2;
+  }
   const int max_slots = T * k;
-  // An expert gets at most T tokens unless a token lists it twice; the MFMA
-  // family is launched only when some expert can reach the threshold that way.
-  // The GEMV family handles every expert the MFMA family does not.
-  const bool use_mfma = thresh <= T;
-  const bool use_gemv = thresh > 0;
-  if (!use_mfma) thresh = INT_MAX;
+  // the matrix-core GEMV addresses activations with 32-bit offsets
+  const bool mg_ok = 2LL * (long long)T * (H > k * I ? H : k * I) < 0x80000000LL;
+  if (path == PW_PATH_MGEMV && !mg_ok) return PW_ERR_UNSUPPORTED_SHAPE;
+  const bool use_mfma = b2 <= T;
+  if (!use_mfma) b2 = INT_MAX;
+  // AUTO keeps batches of at most 64 slots on the GEMV kernels, which route by
+  // themselves (three launches for a decode step)
+  const bool use_mg = b1 < b2 && b1 <= T && mg_ok && (path == PW_PATH_MGEMV || max_slots > 64);
+  if (!use_mg) b1 = b2;
+  const bool use_gemv = b1 > 0;
+  const int thresh = b2;            // MFMA from here (INT_MAX: not launched)
 
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   Route rt;
@@ -124,16 +141,18 @@ pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T, const uint16_t* x
   float* o = reinterpret_cast<float*>(ws + L.o);
 
   const bool small = max_slots <= 64;
-  const bool inline_route = small && !use_mfma;
+  const bool inline_route = small && !use_mfma && !use_mg;
   ExpertArgs mfma{H, I, E, k, T, blocks, q, rt, thresh == 0 ? 1 : thresh, INT_MAX};
+  ExpertArgs mg{H, I, E, k, T, blocks, q, rt, b1 == 0 ? 1 : b1, b2};
   GemvLaunch g{};
   g.H = H; g.I = I; g.E = E; g.k = k; g.T = T;
   g.blocks = blocks; g.q = q; g.ids = ids; g.rt = rt;
   g.inline_route = inline_route ? 1 : 0;
   g.min_tokens = 0;
-  g.max_tokens = thresh == 0 ? 0 : thresh;
+  g.max_tokens = b1;
   g.x = x; g.h = h; g.o = o;
-  g.kparts = down_kparts(H, I, E, k, T);
+  // the other families write one K part of o; the GEMV splits K only when it runs alone
+  g.kparts = (use_mfma || use_mg) ? 1 : down_kparts(H, I, E, k, T);
 
   hipStream_t s = (hipStream_t)stream;
   void* const* ev = (opts && opts->stage_events[0]) ? opts->stage_events : nullptr;
@@ -145,9 +164,11 @@ pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T, const uint16_t* x
   if (e == hipSuccess && !inline_route) e = launch_route(ids, T, k, E, use_mfma ? (thresh == 0 ? 1 : thresh) : INT_MAX, rt, s);
   if (e == hipSuccess) e = mark(PW_STAGE_GATE_UP);
   if (e == hipSuccess && use_gemv) e = launch_gemv_gate_up(g, s);
+  if (e == hipSuccess && use_mg) e = launch_mgemv_gate_up(mg, x, h, s);
   if (e == hipSuccess && use_mfma) e = launch_mfma_gate_up(mfma, x, h, s);
   if (e == hipSuccess) e = mark(PW_STAGE_DOWN);
   if (e == hipSuccess && use_gemv) e = launch_gemv_down(g, s);
+  if (e == hipSuccess && use_mg) e = launch_mgemv_down(mg, h, o, s);
   if (e == hipSuccess && use_mfma) e = launch_mfma_down(mfma, h, o, s);
   if (e == hipSuccess) e = mark(PW_STAGE_COMBINE);
   if (e == hipSuccess) e = launch_combine(o, w, rt.inv, T, k, H, g.kparts, y, s);
@@ -191,7 +212,8 @@ pw_status pw_moe_forward_routed(const pw_moe_shape* shape, int32_t T, const uint
   // argument checks of the forward before anything is enqueued
   if (!blocks || !q || !y) return PW_ERR_INVALID_ARG;
   if (!aligned(y, 16) || !aligned(blocks, 8)) return PW_ERR_ALIGNMENT;
-  if (opts && opts->path != PW_PATH_AUTO && opts->path != PW_PATH_GEMV && opts->path != PW_PATH_MFMA)
+  if (opts && opts->path != PW_PATH_AUTO && opts->path != PW_PATH_GEMV && opts->path != PW_PATH_MFMA &&
+      opts->path != PW_PATH_MGEMV)
     return PW_ERR_INVALID_ARG;
   st = pw_router_topk(shape, T, x, router_w, ids, w, stat_count, stat_mass, workspace, workspace_bytes, stream);
   if (st != PW_OK) return st;

@@ -122,6 +122,8 @@ hipError_t launch_gemv_gate_up(const GemvLaunch& g, hipStream_t s);
 hipError_t launch_gemv_down(const GemvLaunch& g, hipStream_t s);
 hipError_t launch_mfma_gate_up(const ExpertArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s);
 hipError_t launch_mfma_down(const ExpertArgs& a, const uint16_t* h, float* o, hipStream_t s);
+hipError_t launch_mgemv_gate_up(const ExpertArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s);
+hipError_t launch_mgemv_down(const ExpertArgs& a, const uint16_t* h, float* o, hipStream_t s);
 hipError_t launch_combine(const float* o, const float* w, const int32_t* inv, int T, int k, int H, int kparts,
                           uint16_t* y, hipStream_t s);
 hipError_t launch_dequant(const uint32_t* planes, const uint16_t* lut_all, int N, int K, int q,

@@ -1,0 +1,257 @@
+// Matrix-core GEMV kernels for experts with a moderate number of tokens (a
+// few to a few dozen; any count is handled, 64 tokens per pass over K).
+// "Technical summary: PagedWeight", Core components 3 (fused mixed-precision
+// kernel): every block is read at its own committed bitwidth q from the
+// device page table.
+//
+// A workgroup is one wave and owns 16 weight rows of one routed block for the
+// whole K range (gate_up: 8 gate rows and the matching 8 up rows; down: 16
+// rows).  Each weight is decoded exactly once, in registers, straight into the
+// matrix cores' B operand, and multiplies up to 64 tokens (four 16-token
+// groups) with v_mfma_f32_16x16x32_f16 -- no weight tile in LDS, no barrier in
+// the K loop.  For v_mfma_f32_16x16x32_f16 lane l supplies B column l & 15
+// (the weight row) and K slots 8 (l >> 4) .. +8, and A row l & 15 (the token)
+// at the same K slots.  The K order inside one instruction is free as long as
+// A and B agree, so over a 128-wide K chunk c lane group g = l >> 4 takes plane
+// word 4c + g of its row (32 weights), transposes its q plane words into code
+// fields once, looks the 32 weights up in the row's table in LDS, and feeds
+// byte b of the word (weights 8b .. 8b + 7) to sub-step b; the activations of
+// sub-step b are x[token][32 (4c + g) + 8b .. +8], one 16-byte load.  Plane
+// words are requested two chunks ahead, activations at the start of their
+// chunk (the decode covers their latency).  gate_up pairs gate and up rows
+// in columns n and n + 8, so SwiGLU is one lane swap on the accumulators.
+#include "pw_device.h"
+#include "pw_internal.h"
+
+namespace pw {
+
+constexpr int kMgRows = 16;
+constexpr int kMgGroups = 4;                 // 16-token groups per wave
+constexpr int kMgMaxTokens = 16 * kMgGroups; // tokens per pass over K
+
+typedef _Float16 mg_half8 __attribute__((ext_vector_type(8)));
+typedef float mg_float4 __attribute__((ext_vector_type(4)));
+
+struct MgArgs {
+  int H, I, E, k, T;
+  const pw_block_desc* blocks;
+  const uint8_t* q;
+  Route rt;
+  const uint16_t* act;   // gate_up: x [T][H]; down: h [slots][I] by sorted position
+  uint16_t* hout;
+  float* oout;           // o [slots][H] by slot (one K part)
+  int chunks;            // row chunks per block
+  int min_tokens, max_tokens;
+  uint32_t act_bytes;    // < 2^31: out-of-range offsets read zero
+};
+
+// Tile-local row r (0..15) of chunk ch -> block row, and whether it exists.
+template <bool GU>
+__device__ __forceinline__ int mg_row(int ch, int r, int I, int H, bool& ok) {
+  if constexpr (GU) {
+    const int x = 8 * ch + (r & 7);
+    ok = x < I;
+    return (r < 8 ? 0 : I) + x;
+  } else {
+    const int x = 16 * ch + r;
+    ok = x < H;
+    return x;
+  }
+}
+
+template <int Q, bool GU>
+__device__ __forceinline__ void mg_chunk(const MgArgs& A, int e, int n_e, int off_e, int ch, uint8_t* tabs) {
+  constexpr int TAB = (1 << Q) * 2;
+  const int lane = threadIdx.x;
+  const int n = lane & 15, g = lane >> 4;
+  const int H = A.H, I = A.I;
+  const int N = GU ? 2 * I : H;
+  const int K = GU ? H : I;
+  const int W = K >> 5;
+  const int nc = (W + 3) >> 2;
+
+  const pw_block_desc d = A.blocks[2 * e + (GU ? 0 : 1)];
+  const uint32_t pstride = (uint32_t)N * (uint32_t)W * 4u;
+  const __amdgpu_buffer_rsrc_t prs = make_rsrc(uniform_ptr(d.planes), pstride * (uint32_t)Q);
+  const uint16_t* __restrict__ lut = uniform_ptr(d.lut_all) + lut_offset(N, Q);
+
+  bool row_ok;
+  const int row = mg_row<GU>(ch, n, I, H, row_ok);
+
+  auto load_planes = [&](uint32_t (&P)[Q], int c) {
+    const int wd = 4 * c + g;
+    const uint32_t voff = (row_ok && c < nc && wd < W) ? ((uint32_t)row * (uint32_t)W + (uint32_t)wd) * 4u
+                                                       : kOutOfRange;
+#pragma unroll
+    for (int p = 0; p < Q; ++p) P[p] = buf_load_u32(prs, voff, (uint32_t)p * pstride);
+  };
+  uint32_t P0[Q], P1[Q];
+  load_planes(P0, 0);
+  load_planes(P1, 1);
+
+  // the 16 row tables -> LDS, row r at r * TAB (rows outside the block read as zero)
+  for (int c = lane; c < kMgRows * TAB / 16; c += kWave) {
+    const int r = c / (TAB / 16), cc = c % (TAB / 16);
+    bool ok;
+    const int rr = mg_row<GU>(ch, r, I, H, ok);
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (ok) v = *reinterpret_cast<const uint4*>(lut + (size_t)rr * (1 << Q) + cc * 8);
+    *reinterpret_cast<uint4*>(tabs + c * 16) = v;
+  }
+  __syncthreads();
+  const uint32_t base = lds_addr(tabs) + (uint32_t)(n * TAB);
+
+  // activation rows of the lane's token in each group (A row = lane & 15)
+  const int ntg = (n_e + 15) >> 4;
+  const __amdgpu_buffer_rsrc_t ars = make_rsrc(A.act, A.act_bytes);
+  uint32_t aoff[kMgGroups];
+#pragma unroll
+  for (int tg = 0; tg < kMgGroups; ++tg) {
+    const int m = 16 * tg + n;
+    aoff[tg] = kOutOfRange;
+    if (m < n_e) {
+      const int pos = off_e + m;
+      aoff[tg] = GU ? (uint32_t)(A.rt.perm[pos] / A.k) * (uint32_t)H * 2u : (uint32_t)pos * (uint32_t)I * 2u;
+    }
+  }
+
+  mg_float4 acc[kMgGroups];
+#pragma unroll
+  for (int tg = 0; tg < kMgGroups; ++tg) acc[tg] = mg_float4{0.f, 0.f, 0.f, 0.f};
+
+  auto step = [&](const uint32_t (&P)[Q], int c) {
+    const int wd = 4 * c + g;
+    uint4 ar[kMgGroups][4];
+#pragma unroll
+    for (int tg = 0; tg < kMgGroups; ++tg) {
+      if (tg >= ntg) continue;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const uint32_t voff = wd < W ? aoff[tg] + (uint32_t)(wd * 32 + 8 * b) * 2u : kOutOfRange;
+        ar[tg][b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ars, (int)voff, 0, 0));
+      }
+    }
+    uint32_t R[8];
+    planes_to_fields<Q>(P, R);
+    uint32_t packed[16];
+    GroupDecode<Q, 0>::run(R, base, packed);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const mg_half8 bop = __builtin_bit_cast(
+          mg_half8, make_uint4(packed[4 * b], packed[4 * b + 1], packed[4 * b + 2], packed[4 * b + 3]));
+#pragma unroll
+      for (int tg = 0; tg < kMgGroups; ++tg) {
+        if (tg >= ntg) continue;
+        acc[tg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(mg_half8, ar[tg][b]), bop, acc[tg], 0,
+                                                         0, 0);
+      }
+    }
+  };
+
+  for (int c = 0; c < nc; c += 2) {
+    step(P0, c);
+    load_planes(P0, c + 2);
+    if (c + 1 >= nc) break;
+    step(P1, c + 1);
+    load_planes(P1, c + 3);
+  }
+
+  // acc[tg] element v: token 16 tg + 4 g + v, tile column n
+#pragma unroll
+  for (int tg = 0; tg < kMgGroups; ++tg) {
+    if (tg >= ntg) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = 16 * tg + 4 * g + v;
+      if constexpr (GU) {
+        const float gate = acc[tg][v];
+        const float up = __shfl_xor(gate, 8, kWave);   // column n + 8 holds the matching up row
+        if (n < 8 && row_ok && m < n_e) {
+          const _Float16 hh = (_Float16)(silu_f32(gate) * up);
+          A.hout[(size_t)(off_e + m) * I + 8 * ch + n] = __builtin_bit_cast(uint16_t, hh);
+        }
+      } else {
+        if (row_ok && m < n_e) {
+          const size_t slot = (size_t)A.rt.perm[off_e + m];
+          A.oout[slot * H + row] = acc[tg][v];
+        }
+      }
+    }
+  }
+}
+
+template <bool GU>
+__device__ __forceinline__ void mg_zero(const MgArgs& A, int n_e, int off_e, int ch) {
+  for (int i = threadIdx.x; i < n_e * kMgRows; i += kWave) {
+    const int m = i / kMgRows, r = i % kMgRows;
+    bool ok;
+    const int row = mg_row<GU>(ch, r, A.I, A.H, ok);
+    if (!ok) continue;
+    if constexpr (GU) {
+      if (r < 8) A.hout[(size_t)(off_e + m) * A.I + 8 * ch + r] = 0;
+    } else {
+      A.oout[(size_t)A.rt.perm[off_e + m] * A.H + row] = 0.0f;
+    }
+  }
+  if (threadIdx.x == 0 && ch == 0) raise_status(A.rt.status, PW_DEV_BAD_BITWIDTH);
+}
+
+template <bool GU>
+__global__ __launch_bounds__(kWave) void mgemv_kernel(MgArgs A) {
+  __shared__ __align__(16) uint8_t tabs[kMgRows * (1 << kMaxBits) * 2];
+  const int a = (int)blockIdx.x / A.chunks;
+  const int ch = (int)blockIdx.x - a * A.chunks;
+  if (a >= uniform(*A.rt.num_active)) return;
+  const int e = uniform(A.rt.active[a]);
+  const int n_e = uniform(A.rt.counts[e]);
+  if (n_e < A.min_tokens || n_e >= A.max_tokens) return;
+  const int off_e = uniform(A.rt.offsets[e]);
+  const int qv = uniform(A.q[2 * e + (GU ? 0 : 1)]);
+  if (qv < kMinBits || qv > kMaxBits) {
+    mg_zero<GU>(A, n_e, off_e, ch);
+    return;
+  }
+  // more than 64 tokens: one pass over K per 64 of them (the weights are decoded again)
+  for (int m0 = 0; m0 < n_e; m0 += kMgMaxTokens) {
+    const int nm = n_e - m0 < kMgMaxTokens ? n_e - m0 : kMgMaxTokens;
+    if (m0 > 0) __syncthreads();   // the previous pass's lookups are done before the tables are rewritten
+    switch (qv) {
+      case 3: mg_chunk<3, GU>(A, e, nm, off_e + m0, ch, tabs); break;
+      case 4: mg_chunk<4, GU>(A, e, nm, off_e + m0, ch, tabs); break;
+      case 5: mg_chunk<5, GU>(A, e, nm, off_e + m0, ch, tabs); break;
+      case 6: mg_chunk<6, GU>(A, e, nm, off_e + m0, ch, tabs); break;
+      case 7: mg_chunk<7, GU>(A, e, nm, off_e + m0, ch, tabs); break;
+      default: mg_chunk<8, GU>(A, e, nm, off_e + m0, ch, tabs); break;
+    }
+  }
+}
+
+template <bool GU>
+static hipError_t launch_mg(const ExpertArgs& a, const uint16_t* act, uint16_t* h, float* o, hipStream_t s) {
+  MgArgs A{};
+  A.H = a.H; A.I = a.I; A.E = a.E; A.k = a.k; A.T = a.T;
+  A.blocks = a.blocks; A.q = a.q; A.rt = a.rt;
+  A.act = act; A.hout = h; A.oout = o;
+  A.chunks = GU ? (a.I + 7) / 8 : (a.H + kMgRows - 1) / kMgRows;
+  A.min_tokens = a.min_tokens;
+  A.max_tokens = a.max_tokens;
+  const long long act_bytes = 2LL * (GU ? (long long)a.T * a.H : (long long)a.T * a.k * a.I);
+  if (act_bytes >= 0x80000000LL) return hipErrorInvalidValue;
+  A.act_bytes = (uint32_t)act_bytes;
+  const long long bound = a.E < (long long)a.T * a.k ? a.E : (long long)a.T * a.k;
+  const long long grid = bound * A.chunks;
+  if (grid == 0 || A.min_tokens >= A.max_tokens) return hipSuccess;
+  if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mgemv_kernel<GU>, dim3((unsigned)grid), dim3(kWave), 0, s, A);
+  return hipGetLastError();
+}
+
+hipError_t launch_mgemv_gate_up(const ExpertArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s) {
+  return launch_mg<true>(a, x, h, nullptr, s);
+}
+
+hipError_t launch_mgemv_down(const ExpertArgs& a, const uint16_t* h, float* o, hipStream_t s) {
+  return launch_mg<false>(a, h, nullptr, o, s);
+}
+
+}  // namespace pw

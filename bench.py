@@ -224,7 +224,7 @@ def main():
     ap.add_argument("--workload", default="qwen_decode")
     ap.add_argument("--T", type=int, default=None)
     ap.add_argument("--copies", type=int, default=0, help="storage copies to rotate (0: auto, >= 1 GB)")
-    ap.add_argument("--path", type=int, default=0, help="0 auto, 1 GEMV, 2 MFMA")
+    ap.add_argument("--path", type=int, default=0, help="0 auto, 1 GEMV, 2 MFMA, 3 matrix-core GEMV")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -349,7 +349,7 @@ def main():
             "routed_experts": len(routed),
             "mean_q_routed": float(np.mean([layer.q[e] for e in routed])),
             "storage_copies_rotated": copies,
-            "path": ["auto", "gemv", "mfma"][args.path],
+            "path": ["auto", "gemv", "mfma", "mgemv"][args.path],
             "bitwidths": (f"uniform {args.uniform_q}" if args.uniform_q else
                           {"uniform38": "per block, uniform in 3..8",
                            "hot8": "hottest 20% of experts at 8 bits, others uniform in {3,4,5}",

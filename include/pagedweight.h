@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define PW_ABI_VERSION 1
+#define PW_ABI_VERSION 2
 
 typedef int32_t pw_status;
 #define PW_OK                     0
@@ -89,9 +89,11 @@ typedef struct {
 } pw_block_desc;
 
 /* Kernel family for the expert products. */
-#define PW_PATH_AUTO 0   /* per expert: MFMA when its token count >= mfma_min_tokens */
-#define PW_PATH_GEMV 1   /* every expert on the bit-plane GEMV kernels            */
-#define PW_PATH_MFMA 2   /* every expert on the dequant-to-LDS MFMA kernels       */
+#define PW_PATH_AUTO  0  /* per expert by its token count n: GEMV below mgemv_min_tokens,
+                            matrix-core GEMV up to mfma_min_tokens, MFMA from there */
+#define PW_PATH_GEMV  1  /* every expert on the bit-plane GEMV kernels            */
+#define PW_PATH_MFMA  2  /* every expert on the dequant-to-LDS MFMA kernels       */
+#define PW_PATH_MGEMV 3  /* every expert on the matrix-core GEMV kernels          */
 
 /* Stage boundaries at which optional events are recorded. */
 #define PW_STAGE_ROUTE   0
@@ -102,11 +104,14 @@ typedef struct {
 
 typedef struct {
   int32_t path;              /* PW_PATH_*                                     */
-  int32_t mfma_min_tokens;   /* AUTO threshold; <= 0 selects the default (8)  */
+  int32_t mfma_min_tokens;   /* AUTO: MFMA from this many tokens; <= 0: default */
   /* Optional hipEvent_t handles (as void*).  If stage_events[0] is non-NULL,
    * event s is recorded on `stream` right before stage s and event
    * PW_NUM_STAGES after the last stage, so the caller can time each stage. */
   void* stage_events[PW_NUM_STAGES + 1];
+  int32_t mgemv_min_tokens;  /* AUTO: matrix-core GEMV from this many tokens
+                                (below mfma_min_tokens); <= 0: default        */
+  int32_t reserved;
 } pw_moe_options;
 
 /* ABI version of the loaded library (PW_ABI_VERSION). */

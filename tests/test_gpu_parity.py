@@ -353,3 +353,61 @@ def test_forward_mixtral_prefill_sampled(torch):
     toks = sorted(set(toks))
     ref = oracle_y(L, tokens=toks)
     compare(y[toks], ref, f"mixtral_prefill sampled tokens {toks}")
+
+
+# ---------------------------------------------------------------------------
+# matrix-core GEMV (weights decoded in registers into the MFMA B operand)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,T", [("tiny", None), ("qwen_decode", None), ("mixtral_decode", 8),
+                                    ("mixtral_decode", 64)])
+def test_forward_mgemv_forced(torch, name, T):
+    L = layer_for(name, T=T)
+    say(f"forward {name} T={L.wl.T} path=MGEMV")
+    _, y = run_forward(torch, L, B.PW_PATH_MGEMV)
+    compare(y, oracle_y(L), f"{name} mgemv")
+
+
+def test_forward_mgemv_ragged_and_many_tokens(torch):
+    # K tails inside a 128-wide chunk (gate_up K = 2080: 65 words; down K = 96: 3 words), experts with more than
+    # 64 tokens (second pass over K), a single token, and I not a multiple of 8 rows' pairs
+    for (H, I, E, k, T, seed) in [(2080, 96, 5, 3, 70, 51), (96, 1056, 4, 4, 45, 52), (256, 512, 2, 1, 150, 53),
+                                  (160, 224, 3, 2, 1, 54), (64, 40 * 32, 2, 2, 33, 55)]:
+        L = custom_layer(H, I, E, k, T, seed)
+        say(f"forward mgemv ragged H={H} I={I} E={E} k={k} T={T}")
+        _, y = run_forward(torch, L, B.PW_PATH_MGEMV)
+        compare(y, oracle_y(L), f"mgemv ragged H={H} I={I} T={T}")
+
+
+def test_forward_mgemv_every_bitwidth_pair(torch):
+    H, I, E, k, T, seed = 512, 256, 36, 4, 45, 56
+    qvals = [(3 + e % 6, 3 + (e // 6) % 6) for e in range(E)]
+    L = custom_layer(H, I, E, k, T, seed, qvals=qvals)
+    say("forward mgemv every (gate_up, down) bitwidth pair")
+    _, y = run_forward(torch, L, B.PW_PATH_MGEMV)
+    compare(y, oracle_y(L), "mgemv bitwidth pairs")
+
+
+def test_forward_mgemv_invalid_bitwidth_flagged_and_zero(torch):
+    from any_precision_bitplane_amd.device import DeviceLayer
+    L = custom_layer(256, 512, 4, 2, 40, 57)
+    L.q[1, 0] = 9
+    L.q[2, 1] = 2
+    dev = DeviceLayer(L)
+    say("forward mgemv with invalid bitwidths on two blocks")
+    dev.forward(B.make_options(path=B.PW_PATH_MGEMV))
+    torch.cuda.synchronize()
+    assert dev.status() & B.PW_DEV_BAD_BITWIDTH
+    compare(dev.y.float().cpu().numpy(), oracle_y(L), "mgemv invalid bitwidths")
+
+
+def test_forward_auto_three_families(torch):
+    """Batched Qwen-shaped layer under the default AUTO bands: experts below 4
+    tokens on the GEMV kernels, 4..63 on the matrix-core GEMV, 64 and more on
+    the MFMA kernels, in one call."""
+    L = layer_for("qwen_batched")
+    counts = np.bincount(L.ids.reshape(-1), minlength=L.wl.E)
+    c = counts[counts > 0]
+    assert (c < 4).any() and ((c >= 4) & (c < 64)).any() and (c >= 64).any()
+    say("forward qwen_batched T=256 AUTO default bands")
+    _, y = run_forward(torch, L, B.PW_PATH_AUTO)
+    compare(y, oracle_y(L), "qwen_batched auto three families")
