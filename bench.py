@@ -225,6 +225,9 @@ def main():
     ap.add_argument("--T", type=int, default=None)
     ap.add_argument("--copies", type=int, default=0, help="storage copies to rotate (0: auto, >= 1 GB)")
     ap.add_argument("--path", type=int, default=0, help="0 auto, 1 GEMV, 2 MFMA, 3 matrix-core GEMV")
+    ap.add_argument("--mfma-min", type=int, default=0, help="AUTO: MFMA from this many tokens (0: library default)")
+    ap.add_argument("--mgemv-min", type=int, default=0,
+                    help="AUTO: matrix-core GEMV from this many tokens (0: library default)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -272,7 +275,7 @@ def main():
     copies = min(copies, 64)
 
     dev = DeviceLayer(layer, copies=copies, experts=routed)
-    opts = B.make_options(path=args.path)
+    opts = B.make_options(path=args.path, mfma_min_tokens=args.mfma_min, mgemv_min_tokens=args.mgemv_min)
     stream = torch.cuda.current_stream()
 
     for i in range(args.warmup):
@@ -299,7 +302,8 @@ def main():
     # Stage timing: the same K calls again, with events recorded by the library
     # on the stream between its kernels (kernel duration plus its launch gap).
     events = [[evs.create() for _ in range(nst)] for _ in range(args.steps)]
-    step_opts = [B.make_options(path=args.path, events=events[i]) for i in range(args.steps)]
+    step_opts = [B.make_options(path=args.path, events=events[i], mfma_min_tokens=args.mfma_min,
+                                mgemv_min_tokens=args.mgemv_min) for i in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         dev.forward(step_opts[i], copy=i % copies, stream=stream)

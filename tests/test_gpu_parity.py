@@ -401,13 +401,20 @@ def test_forward_mgemv_invalid_bitwidth_flagged_and_zero(torch):
 
 
 def test_forward_auto_three_families(torch):
-    """Batched Qwen-shaped layer under the default AUTO bands: experts below 4
-    tokens on the GEMV kernels, 4..63 on the matrix-core GEMV, 64 and more on
-    the MFMA kernels, in one call."""
+    """Batched Qwen-shaped layer with AUTO bands at 4 and 64 tokens: experts
+    below 4 tokens on the GEMV kernels, 4..63 on the matrix-core GEMV, 64 and
+    more on the MFMA kernels, in one call; then the default bands."""
     L = layer_for("qwen_batched")
     counts = np.bincount(L.ids.reshape(-1), minlength=L.wl.E)
     c = counts[counts > 0]
     assert (c < 4).any() and ((c >= 4) & (c < 64)).any() and (c >= 64).any()
+    say("forward qwen_batched T=256 AUTO bands 4 / 64")
+    from any_precision_bitplane_amd.device import DeviceLayer
+    dev = DeviceLayer(L)
+    dev.forward(B.make_options(path=B.PW_PATH_AUTO, mgemv_min_tokens=4, mfma_min_tokens=64))
+    torch.cuda.synchronize()
+    ref = oracle_y(L)
+    compare(dev.y.float().cpu().numpy(), ref, "qwen_batched auto three families")
     say("forward qwen_batched T=256 AUTO default bands")
-    _, y = run_forward(torch, L, B.PW_PATH_AUTO)
-    compare(y, oracle_y(L), "qwen_batched auto three families")
+    _, y = run_forward(torch, L, B.PW_PATH_AUTO, dev=dev)
+    compare(y, ref, "qwen_batched auto default bands")
