@@ -12,13 +12,15 @@
 // the K loop.  For v_mfma_f32_16x16x32_f16 lane l supplies B column l & 15
 // (the weight row) and K slots 8 (l >> 4) .. +8, and A row l & 15 (the token)
 // at the same K slots.  The K order inside one instruction is free as long as
-// A and B agree, so over a 128-wide K chunk c lane group g = l >> 4 takes plane
-// word 4c + g of its row (32 weights), transposes its q plane words into code
-// fields once, looks the 32 weights up in the row's table in LDS, and feeds
-// byte b of the word (weights 8b .. 8b + 7) to sub-step b; the activations of
-// sub-step b are x[token][32 (4c + g) + 8b .. +8], one 16-byte load.  Plane
-// words are requested two chunks ahead, activations at the start of their
-// chunk (the decode covers their latency).  gate_up pairs gate and up rows
+// A and B agree, so lane group g = l >> 4 takes plane word w of its row (32
+// weights), transposes its q plane words into code fields once, looks the 32
+// weights up in the row's table in LDS, and feeds byte b of the word (weights
+// 8b .. 8b + 7) to sub-step b; the activations of sub-step b are
+// x[token][32 w + 8b .. +8], one 16-byte load.  In a 512-wide super-chunk C,
+// group g reads words 16 C + 4 g .. +4 with one load per plane (the four
+// groups cover a row's 64-byte line) and sub-chunk i uses word 16 C + 4 g + i.
+// Plane words are requested two super-chunks ahead, activations at the start
+// of their sub-chunk (the decode covers their latency).  gate_up pairs gate and up rows
 // in columns n and n + 8, so SwiGLU is one lane swap on the accumulators.
 #include "pw_device.h"
 #include "pw_internal.h"
@@ -68,7 +70,6 @@ __device__ __forceinline__ void mg_chunk(const MgArgs& A, int e, int n_e, int of
   const int N = GU ? 2 * I : H;
   const int K = GU ? H : I;
   const int W = K >> 5;
-  const int nc = (W + 3) >> 2;
 
   const pw_block_desc d = A.blocks[2 * e + (GU ? 0 : 1)];
   const uint32_t pstride = (uint32_t)N * (uint32_t)W * 4u;
@@ -78,14 +79,35 @@ __device__ __forceinline__ void mg_chunk(const MgArgs& A, int e, int n_e, int of
   bool row_ok;
   const int row = mg_row<GU>(ch, n, I, H, row_ok);
 
-  auto load_planes = [&](uint32_t (&P)[Q], int c) {
-    const int wd = 4 * c + g;
-    const uint32_t voff = (row_ok && c < nc && wd < W) ? ((uint32_t)row * (uint32_t)W + (uint32_t)wd) * 4u
+  // K is walked in 512-wide super-chunks: lane group g reads plane words
+  // 16 C + 4 g .. +4 of its row (64 contiguous bytes per row and plane across
+  // the four groups, one line), and word 16 C + 4 g + i feeds sub-chunk i.
+  // Rows start on 16-byte boundaries when W % 4 == 0 (one 16-byte load per
+  // plane); otherwise four 4-byte loads.  Words past the row's end belong to
+  // the next row (or read as zero past the buffer); their activations read as
+  // zero, so they add nothing.
+  const int ns = (W + 15) >> 4;
+  const bool vec = (W & 3) == 0;
+  auto load_planes = [&](uint32_t (&P)[Q][4], int C) {
+    const int wd = 16 * C + 4 * g;
+    const uint32_t voff = (row_ok && C < ns && wd < W) ? ((uint32_t)row * (uint32_t)W + (uint32_t)wd) * 4u
                                                        : kOutOfRange;
+    if (vec) {
 #pragma unroll
-    for (int p = 0; p < Q; ++p) P[p] = buf_load_u32(prs, voff, (uint32_t)p * pstride);
+      for (int p = 0; p < Q; ++p) {
+        const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      prs, (int)voff, (int)((uint32_t)p * pstride), 0));
+        P[p][0] = v.x; P[p][1] = v.y; P[p][2] = v.z; P[p][3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < Q; ++p)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          P[p][i] = buf_load_u32(prs, voff == kOutOfRange ? kOutOfRange : voff + 4u * i, (uint32_t)p * pstride);
+    }
   };
-  uint32_t P0[Q], P1[Q];
+  uint32_t P0[Q][4], P1[Q][4];
   load_planes(P0, 0);
   load_planes(P1, 1);
 
@@ -119,8 +141,8 @@ __device__ __forceinline__ void mg_chunk(const MgArgs& A, int e, int n_e, int of
 #pragma unroll
   for (int tg = 0; tg < kMgGroups; ++tg) acc[tg] = mg_float4{0.f, 0.f, 0.f, 0.f};
 
-  auto step = [&](const uint32_t (&P)[Q], int c) {
-    const int wd = 4 * c + g;
+  // sub-chunk: plane word wd (its four plane bytes b = sub-steps)
+  auto sub = [&](const uint32_t (&P)[Q][4], int i, int wd) {
     uint4 ar[kMgGroups][4];
 #pragma unroll
     for (int tg = 0; tg < kMgGroups; ++tg) {
@@ -131,8 +153,11 @@ __device__ __forceinline__ void mg_chunk(const MgArgs& A, int e, int n_e, int of
         ar[tg][b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ars, (int)voff, 0, 0));
       }
     }
+    uint32_t W8[Q];
+#pragma unroll
+    for (int p = 0; p < Q; ++p) W8[p] = P[p][i];
     uint32_t R[8];
-    planes_to_fields<Q>(P, R);
+    planes_to_fields<Q>(W8, R);
     uint32_t packed[16];
     GroupDecode<Q, 0>::run(R, base, packed);
 #pragma unroll
@@ -147,13 +172,21 @@ __device__ __forceinline__ void mg_chunk(const MgArgs& A, int e, int n_e, int of
       }
     }
   };
+  auto superchunk = [&](const uint32_t (&P)[Q][4], int C) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int wd = 16 * C + 4 * g + i;
+      if (16 * C + i >= W) break;   // no group has a word left (uniform)
+      sub(P, i, wd);
+    }
+  };
 
-  for (int c = 0; c < nc; c += 2) {
-    step(P0, c);
-    load_planes(P0, c + 2);
-    if (c + 1 >= nc) break;
-    step(P1, c + 1);
-    load_planes(P1, c + 3);
+  for (int C = 0; C < ns; C += 2) {
+    superchunk(P0, C);
+    load_planes(P0, C + 2);
+    if (C + 1 >= ns) break;
+    superchunk(P1, C + 1);
+    load_planes(P1, C + 3);
   }
 
   // acc[tg] element v: token 16 tg + 4 g + v, tile column n
