@@ -371,7 +371,8 @@ def test_forward_mgemv_ragged_and_many_tokens(torch):
     # K tails inside a 128-wide chunk (gate_up K = 2080: 65 words; down K = 96: 3 words), experts with more than
     # 64 tokens (second pass over K), a single token, and I not a multiple of 8 rows' pairs
     for (H, I, E, k, T, seed) in [(2080, 96, 5, 3, 70, 51), (96, 1056, 4, 4, 45, 52), (256, 512, 2, 1, 150, 53),
-                                  (160, 224, 3, 2, 1, 54), (64, 40 * 32, 2, 2, 33, 55), (256, 512, 2, 1, 48, 58)]:
+                                  (160, 224, 3, 2, 1, 54), (64, 40 * 32, 2, 2, 33, 55), (256, 512, 2, 1, 48, 58),
+                                  (64, 4128, 3, 2, 20, 59)]:
         L = custom_layer(H, I, E, k, T, seed)
         say(f"forward mgemv ragged H={H} I={I} E={E} k={k} T={T}")
         _, y = run_forward(torch, L, B.PW_PATH_MGEMV)
