@@ -143,6 +143,8 @@ pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T, const uint16_t* x
   rt.inv = reinterpret_cast<int32_t*>(ws + L.inv);
   rt.mtiles = reinterpret_cast<int32_t*>(ws + L.mtiles);
   rt.num_mtiles = reinterpret_cast<int32_t*>(ws + L.num_mtiles);
+  rt.mgtiles = reinterpret_cast<int32_t*>(ws + L.mgtiles);
+  rt.num_mgtiles = reinterpret_cast<int32_t*>(ws + L.num_mgtiles);
   uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
   float* o = reinterpret_cast<float*>(ws + L.o);
 
@@ -167,7 +169,9 @@ pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T, const uint16_t* x
   };
 
   hipError_t e = mark(PW_STAGE_ROUTE);
-  if (e == hipSuccess && !inline_route) e = launch_route(ids, T, k, E, use_mfma ? (thresh == 0 ? 1 : thresh) : INT_MAX, rt, s);
+  if (e == hipSuccess && !inline_route)
+    e = launch_route(ids, T, k, E, use_mfma ? (thresh == 0 ? 1 : thresh) : INT_MAX, use_mg ? (b1 == 0 ? 1 : b1) : INT_MAX,
+                     use_mg ? b2 : INT_MAX, rt, s);
   if (e == hipSuccess) e = mark(PW_STAGE_GATE_UP);
   if (e == hipSuccess && use_gemv) e = launch_gemv_gate_up(g, s);
   if (e == hipSuccess && use_mg) e = launch_mgemv_gate_up(mg, x, h, s);

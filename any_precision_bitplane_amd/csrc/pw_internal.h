@@ -24,6 +24,13 @@ inline int mtile_bound(int E, int T, int k) {
   return (E < slots ? E : slots) + (slots + kMfmaTileM - 1) / kMfmaTileM;
 }
 
+constexpr int kMgTileM = 64;      // tokens per matrix-core GEMV pass
+
+inline int mgtile_bound(int E, int T, int k) {
+  const int slots = T * k;
+  return (E < slots ? E : slots) + (slots + kMgTileM - 1) / kMgTileM;
+}
+
 // Parts of the down product's K range given to separate waves when a small
 // batch would otherwise leave most of the chip idle.
 inline int down_kparts(int H, int I, int E, int k, int T) {
@@ -43,12 +50,14 @@ struct WsLayout {
   size_t status = 0;        // uint32 status bits
   size_t num_active = 4;    // int32 number of experts with at least one slot
   size_t num_mtiles = 8;    // int32 number of MFMA token tiles
+  size_t num_mgtiles = 12;  // int32 number of matrix-core GEMV token tiles
   size_t counts = 0;        // int32 [E]    slots per expert
   size_t offsets = 0;       // int32 [E+1]  first sorted position per expert
   size_t active = 0;        // int32 [E]    active expert ids, ascending
   size_t perm = 0;          // int32 [T*k]  sorted position -> slot (t*k + j)
   size_t inv = 0;           // int32 [T*k]  slot -> sorted position, -1 if dropped
   size_t mtiles = 0;        // int32 [2 * mtile_bound] MFMA token tiles
+  size_t mgtiles = 0;       // int32 [2 * mgtile_bound] matrix-core GEMV token tiles
   size_t h = 0;             // fp16  [T*k][I] activations between the products
   size_t o = 0;             // fp32  [kparts][T*k][H] expert outputs by slot (t*k + j), before the combine
   size_t rlogits = 0;       // fp32  [T][E]   router logits
@@ -68,6 +77,7 @@ inline WsLayout ws_layout(int H, int I, int E, int k, int T) {
   L.perm = off;    off = align_up(off + sizeof(int32_t) * slots, kAlign);
   L.inv = off;     off = align_up(off + sizeof(int32_t) * slots, kAlign);
   L.mtiles = off;  off = align_up(off + sizeof(int32_t) * 2 * mtile_bound(E, T, k), kAlign);
+  L.mgtiles = off; off = align_up(off + sizeof(int32_t) * 2 * mgtile_bound(E, T, k), kAlign);
   L.h = off;       off = align_up(off + sizeof(uint16_t) * slots * I, kAlign);
   L.o = off;       off = align_up(off + sizeof(float) * kp * slots * H, kAlign);
   L.rlogits = off; off = align_up(off + sizeof(float) * (size_t)T * E, kAlign);
@@ -88,6 +98,8 @@ struct Route {
   int32_t* inv;
   int32_t* mtiles;        // (expert, first sorted position) per MFMA token tile
   int32_t* num_mtiles;
+  int32_t* mgtiles;       // (expert, first token) per matrix-core GEMV token tile
+  int32_t* num_mgtiles;
 };
 
 
@@ -116,8 +128,8 @@ struct GemvLaunch {
 };
 
 // Launchers (return hipSuccess or the launch error).
-hipError_t launch_route(const int32_t* ids, int T, int k, int E, int mfma_min_tokens, const Route& rt,
-                        hipStream_t s);
+hipError_t launch_route(const int32_t* ids, int T, int k, int E, int mfma_min_tokens, int mg_min_tokens,
+                        int mg_max_tokens, const Route& rt, hipStream_t s);
 hipError_t launch_gemv_gate_up(const GemvLaunch& g, hipStream_t s);
 hipError_t launch_gemv_down(const GemvLaunch& g, hipStream_t s);
 hipError_t launch_mfma_gate_up(const ExpertArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s);

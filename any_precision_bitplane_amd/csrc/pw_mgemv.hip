@@ -29,7 +29,7 @@ namespace pw {
 
 constexpr int kMgRows = 16;
 constexpr int kMgGroups = 4;                 // 16-token groups per wave
-constexpr int kMgMaxTokens = 16 * kMgGroups; // tokens per pass over K
+static_assert(16 * kMgGroups == kMgTileM, "a tile fills the token groups");
 
 typedef _Float16 mg_half8 __attribute__((ext_vector_type(8)));
 typedef float mg_float4 __attribute__((ext_vector_type(4)));
@@ -43,7 +43,6 @@ struct MgArgs {
   uint16_t* hout;
   float* oout;           // o [slots][H] by slot (one K part)
   int chunks;            // row chunks per block
-  int min_tokens, max_tokens;
   uint32_t act_bytes;    // < 2^31: out-of-range offsets read zero
 };
 
@@ -214,7 +213,7 @@ __device__ __forceinline__ void mg_chunk(const MgArgs& A, int e, int n_e, int of
 }
 
 template <bool GU>
-__device__ __forceinline__ void mg_zero(const MgArgs& A, int n_e, int off_e, int ch) {
+__device__ __forceinline__ void mg_zero(const MgArgs& A, int n_e, int off_e, int ch, bool first_tile) {
   for (int i = threadIdx.x; i < n_e * kMgRows; i += kWave) {
     const int m = i / kMgRows, r = i % kMgRows;
     bool ok;
@@ -226,36 +225,32 @@ __device__ __forceinline__ void mg_zero(const MgArgs& A, int n_e, int off_e, int
       A.oout[(size_t)A.rt.perm[off_e + m] * A.H + row] = 0.0f;
     }
   }
-  if (threadIdx.x == 0 && ch == 0) raise_status(A.rt.status, PW_DEV_BAD_BITWIDTH);
+  if (threadIdx.x == 0 && ch == 0 && first_tile) raise_status(A.rt.status, PW_DEV_BAD_BITWIDTH);
 }
 
+// One wave per (64-token tile, row chunk): the route kernel lists the tiles of
+// the experts in this family's band, so an expert with many tokens gets more
+// waves instead of longer ones.
 template <bool GU>
 __global__ __launch_bounds__(kWave) void mgemv_kernel(MgArgs A) {
   __shared__ __align__(16) uint8_t tabs[kMgRows * (1 << kMaxBits) * 2];
-  const int a = (int)blockIdx.x / A.chunks;
-  const int ch = (int)blockIdx.x - a * A.chunks;
-  if (a >= uniform(*A.rt.num_active)) return;
-  const int e = uniform(A.rt.active[a]);
+  const int t = (int)blockIdx.x / A.chunks;
+  const int ch = (int)blockIdx.x - t * A.chunks;
+  if (t >= uniform(*A.rt.num_mgtiles)) return;
+  const int e = uniform(A.rt.mgtiles[2 * t]);
+  const int m0 = uniform(A.rt.mgtiles[2 * t + 1]);
   const int n_e = uniform(A.rt.counts[e]);
-  if (n_e < A.min_tokens || n_e >= A.max_tokens) return;
-  const int off_e = uniform(A.rt.offsets[e]);
+  const int nm = n_e - m0 < kMgTileM ? n_e - m0 : kMgTileM;
+  const int off_e = uniform(A.rt.offsets[e]) + m0;
   const int qv = uniform(A.q[2 * e + (GU ? 0 : 1)]);
-  if (qv < kMinBits || qv > kMaxBits) {
-    mg_zero<GU>(A, n_e, off_e, ch);
-    return;
-  }
-  // more than 64 tokens: one pass over K per 64 of them (the weights are decoded again)
-  for (int m0 = 0; m0 < n_e; m0 += kMgMaxTokens) {
-    const int nm = n_e - m0 < kMgMaxTokens ? n_e - m0 : kMgMaxTokens;
-    if (m0 > 0) __syncthreads();   // the previous pass's lookups are done before the tables are rewritten
-    switch (qv) {
-      case 3: mg_chunk<3, GU>(A, e, nm, off_e + m0, ch, tabs); break;
-      case 4: mg_chunk<4, GU>(A, e, nm, off_e + m0, ch, tabs); break;
-      case 5: mg_chunk<5, GU>(A, e, nm, off_e + m0, ch, tabs); break;
-      case 6: mg_chunk<6, GU>(A, e, nm, off_e + m0, ch, tabs); break;
-      case 7: mg_chunk<7, GU>(A, e, nm, off_e + m0, ch, tabs); break;
-      default: mg_chunk<8, GU>(A, e, nm, off_e + m0, ch, tabs); break;
-    }
+  switch (qv) {
+    case 3: mg_chunk<3, GU>(A, e, nm, off_e, ch, tabs); break;
+    case 4: mg_chunk<4, GU>(A, e, nm, off_e, ch, tabs); break;
+    case 5: mg_chunk<5, GU>(A, e, nm, off_e, ch, tabs); break;
+    case 6: mg_chunk<6, GU>(A, e, nm, off_e, ch, tabs); break;
+    case 7: mg_chunk<7, GU>(A, e, nm, off_e, ch, tabs); break;
+    case 8: mg_chunk<8, GU>(A, e, nm, off_e, ch, tabs); break;
+    default: mg_zero<GU>(A, nm, off_e, ch, m0 == 0); break;
   }
 }
 
@@ -266,14 +261,11 @@ static hipError_t launch_mg(const ExpertArgs& a, const uint16_t* act, uint16_t* 
   A.blocks = a.blocks; A.q = a.q; A.rt = a.rt;
   A.act = act; A.hout = h; A.oout = o;
   A.chunks = GU ? (a.I + 7) / 8 : (a.H + kMgRows - 1) / kMgRows;
-  A.min_tokens = a.min_tokens;
-  A.max_tokens = a.max_tokens;
   const long long act_bytes = 2LL * (GU ? (long long)a.T * a.H : (long long)a.T * a.k * a.I);
   if (act_bytes >= 0x80000000LL) return hipErrorInvalidValue;
   A.act_bytes = (uint32_t)act_bytes;
-  const long long bound = a.E < (long long)a.T * a.k ? a.E : (long long)a.T * a.k;
-  const long long grid = bound * A.chunks;
-  if (grid == 0 || A.min_tokens >= A.max_tokens) return hipSuccess;
+  const long long grid = (long long)mgtile_bound(a.E, a.T, a.k) * A.chunks;
+  if (grid == 0 || a.min_tokens >= a.max_tokens) return hipSuccess;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(mgemv_kernel<GU>, dim3((unsigned)grid), dim3(kWave), 0, s, A);
   return hipGetLastError();

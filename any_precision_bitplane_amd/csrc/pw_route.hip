@@ -5,8 +5,9 @@
 // routing mass as selection frequency and weight; the layer consumes both).
 //
 // One workgroup of 1024 threads handles any number of slots: counts with LDS
-// integer atomics (order-free, so deterministic), a serial scan over <= 256
-// experts, then the slots in chunks of 1024 in slot order.  Inside a chunk each
+// integer atomics (order-free, so deterministic), one wave's scan over <= 256
+// experts (which also lists the token tiles of the MFMA and matrix-core GEMV
+// families), then the slots in chunks of 1024 in slot order.  Inside a chunk each
 // wave ranks its lanes per expert with ballots, and the per-wave counts are
 // scanned per expert, so a slot's position is
 //   offsets[e] + #{earlier slots routed to e}
@@ -20,7 +21,8 @@ constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / kWave;
 
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __restrict__ ids, int T, int k,
-                                                              int E, int mfma_min_tokens, Route rt) {
+                                                              int E, int mfma_min_tokens, int mg_min_tokens,
+                                                              int mg_max_tokens, Route rt) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int off[kMaxExperts + 1];
   __shared__ int base[kMaxExperts];
@@ -46,27 +48,54 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
   if (bad) raise_status(rt.status, PW_DEV_BAD_EXPERT_ID);
   __syncthreads();
 
-  if (tid == 0) {
-    int acc = 0, na = 0;
-    for (int e = 0; e < E; ++e) {
-      off[e] = acc;
-      acc += cnt[e];
-      if (cnt[e] > 0) rt.active[na++] = e;
+  if (wave == 0) {
+    // Lane l owns experts 4l .. 4l+3 (E <= 256).  Four exclusive scans over the
+    // wave give each expert its offset, its index in the active list and the
+    // first entries of its MFMA (256-token) and matrix-core GEMV (64-token)
+    // tiles, so every list is written in parallel, in expert order.
+    int c[4], na[4], nm[4], ng[4];
+    int sc = 0, sa = 0, sm = 0, sg = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      c[i] = e < E ? cnt[e] : 0;
+      na[i] = c[i] > 0 ? 1 : 0;
+      nm[i] = (c[i] > 0 && c[i] >= mfma_min_tokens) ? (c[i] + kMfmaTileM - 1) / kMfmaTileM : 0;
+      ng[i] = (c[i] > 0 && c[i] >= mg_min_tokens && c[i] < mg_max_tokens) ? (c[i] + kMgTileM - 1) / kMgTileM : 0;
+      sc += c[i]; sa += na[i]; sm += nm[i]; sg += ng[i];
     }
-    off[E] = acc;
-    *rt.num_active = na;
-    rt.offsets[E] = acc;
-    // token tiles of the experts that take the MFMA kernels, in expert order
-    int nm = 0;
-    for (int e = 0; e < E; ++e) {
-      if (cnt[e] < mfma_min_tokens || cnt[e] == 0) continue;
-      for (int m0 = 0; m0 < cnt[e]; m0 += kMfmaTileM) {
-        rt.mtiles[2 * nm] = e;
-        rt.mtiles[2 * nm + 1] = m0;
-        ++nm;
+    int xc = sc, xa = sa, xm = sm, xg = sg;   // inclusive scans
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int yc = __shfl_up(xc, d, kWave), ya = __shfl_up(xa, d, kWave);
+      const int ym = __shfl_up(xm, d, kWave), yg = __shfl_up(xg, d, kWave);
+      if (lane >= d) { xc += yc; xa += ya; xm += ym; xg += yg; }
+    }
+    int pc = xc - sc, pa = xa - sa, pm = xm - sm, pg = xg - sg;   // exclusive
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      if (e < E) {
+        off[e] = pc;
+        if (na[i]) rt.active[pa] = e;
+        for (int t = 0; t < nm[i]; ++t) {
+          rt.mtiles[2 * (pm + t)] = e;
+          rt.mtiles[2 * (pm + t) + 1] = t * kMfmaTileM;
+        }
+        for (int t = 0; t < ng[i]; ++t) {
+          rt.mgtiles[2 * (pg + t)] = e;
+          rt.mgtiles[2 * (pg + t) + 1] = t * kMgTileM;
+        }
       }
+      pc += c[i]; pa += na[i]; pm += nm[i]; pg += ng[i];
     }
-    *rt.num_mtiles = nm;
+    if (lane == kWave - 1) {
+      off[E] = xc;
+      rt.offsets[E] = xc;
+      *rt.num_active = xa;
+      *rt.num_mtiles = xm;
+      *rt.num_mgtiles = xg;
+    }
   }
   __syncthreads();
   for (int e = tid; e < E; e += kRouteThreads) {
@@ -122,9 +151,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
   }
 }
 
-hipError_t launch_route(const int32_t* ids, int T, int k, int E, int mfma_min_tokens, const Route& rt,
-                        hipStream_t s) {
-  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, s, ids, T, k, E, mfma_min_tokens, rt);
+hipError_t launch_route(const int32_t* ids, int T, int k, int E, int mfma_min_tokens, int mg_min_tokens,
+                        int mg_max_tokens, const Route& rt, hipStream_t s) {
+  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, s, ids, T, k, E, mfma_min_tokens, mg_min_tokens,
+                     mg_max_tokens, rt);
   return hipGetLastError();
 }
 
