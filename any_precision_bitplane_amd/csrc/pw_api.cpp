@@ -17,10 +17,12 @@ namespace {
 
 // AUTO: experts with at least this many routed tokens take the matrix-core
 // GEMV kernels, and from the second threshold on the MFMA kernels.
-// Measured on the Qwen- and Mixtral-shaped layers: the matrix-core GEMV beats
-// the GEMV from about 3 tokens per expert, and beats the dequant-to-LDS MFMA
-// kernels (one 256-token tile) up to about 256 tokens.
-constexpr int kDefaultMgemvMinTokens = 3;
+// Measured on the Qwen- and Mixtral-shaped layers: once a batch averages 3 or
+// more slots per routed expert, the matrix-core GEMV taking every expert below
+// the MFMA band beats any mix with the GEMV (one launch fewer per product), and
+// it beats the dequant-to-LDS MFMA kernels (one 256-token tile) up to about
+// 256 tokens.
+constexpr int kDefaultMgemvMinTokens = 1;
 constexpr int kDefaultMfmaMinTokens = 256;
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -122,14 +124,14 @@ pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T, const uint16_t* x
   if (path == PW_PATH_MGEMV && !mg_ok) return PW_ERR_UNSUPPORTED_SHAPE;
   const bool use_mfma = b2 <= T;
   if (!use_mfma) b2 = INT_MAX;
-  // AUTO keeps batches of at most 64 slots on the GEMV kernels, which route by
-  // themselves (three launches for a decode step), and batches averaging fewer
-  // than 3 slots per routed expert too (one family launch is cheaper there)
+  // AUTO keeps batches averaging fewer than 3 slots per routed expert on the
+  // GEMV kernels alone (which route by themselves up to 64 slots: three
+  // launches for a decode step); from 3 on the matrix-core GEMV is faster
   const int routed_bound = E < max_slots ? E : max_slots;
-  const bool mg_worth = max_slots > 64 && (long long)max_slots >= 3LL * routed_bound;
+  const bool mg_worth = (long long)max_slots >= 3LL * routed_bound;
   const bool use_mg = b1 < b2 && b1 <= T && mg_ok && (path == PW_PATH_MGEMV || mg_worth);
   if (!use_mg) b1 = b2;
-  const bool use_gemv = b1 > 0;
+  const bool use_gemv = b1 > 1;     // a routed expert has at least one token
   const int thresh = b2;            // MFMA from here (INT_MAX: not launched)
 
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);

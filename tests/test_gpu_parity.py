@@ -325,7 +325,7 @@ def test_forward_mfma_ragged_shapes(torch):
 
 def test_forward_qwen_batched_auto_mixes_paths(torch):
     """Zipf routing: hot experts (many tokens, 8 bits) on the MFMA kernels, the
-    rest on the GEMV kernels, in one call."""
+    rest on the matrix-core GEMV, in one call; then every expert on the GEMV."""
     L = layer_for("qwen_batched")
     counts = np.bincount(L.ids.reshape(-1), minlength=L.wl.E)
     assert counts.max() >= 16 and counts[counts > 0].min() < 16
