@@ -213,7 +213,8 @@ def test_unused_arena_is_never_read(torch, tiny, static):
     torch.cuda.synchronize()
     y = paged_y(torch, paged)
     assert np.array_equal(y, static_y(torch, static, q1))
-    assert np.array_equal(paged_y(torch, paged, B.PW_PATH_MFMA), static_y(torch, static, q1, B.PW_PATH_MFMA))
+    for path in (B.PW_PATH_GEMV, B.PW_PATH_MGEMV, B.PW_PATH_MFMA):
+        assert np.array_equal(paged_y(torch, paged, path), static_y(torch, static, q1, path)), path
     assert paged.status() == 0
     paged.close()
 
