@@ -419,3 +419,15 @@ def test_forward_auto_three_families(torch):
     say("forward qwen_batched T=256 AUTO default bands")
     _, y = run_forward(torch, L, B.PW_PATH_AUTO, dev=dev)
     compare(y, ref, "qwen_batched auto default bands")
+
+
+@pytest.mark.parametrize("H,I,E,k,T,seed", [(256, 512, 1, 1, 5, 61), (256, 512, 1, 1, 300, 62),
+                                            (128, 256, 4, 4, 20, 63), (96, 160, 3, 3, 260, 64)])
+def test_forward_auto_edge_layers(torch, H, I, E, k, T, seed):
+    """AUTO on degenerate routing: one expert (a plain SwiGLU FFN) below and
+    above the MFMA band, and k = E (every expert takes every token)."""
+    L = custom_layer(H, I, E, k, T, seed)
+    say(f"forward AUTO edge H={H} I={I} E={E} k={k} T={T}")
+    dev, y = run_forward(torch, L, B.PW_PATH_AUTO)
+    assert dev.status() == 0
+    compare(y, oracle_y(L), f"auto edge E={E} k={k} T={T}")
