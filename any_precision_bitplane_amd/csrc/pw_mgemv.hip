@@ -28,6 +28,7 @@
 namespace pw {
 
 constexpr int kMgRows = 16;
+constexpr long long kMgMaxGrid = 32768;   // workgroups per launch (several per SIMD)
 constexpr int kMgGroups = 4;                 // 16-token groups per wave
 static_assert(16 * kMgGroups == kMgTileM, "a tile fills the token groups");
 
@@ -231,26 +232,34 @@ __device__ __forceinline__ void mg_zero(const MgArgs& A, int n_e, int off_e, int
 // One wave per (64-token tile, row chunk): the route kernel lists the tiles of
 // the experts in this family's band, so an expert with many tokens gets more
 // waves instead of longer ones.
+// Work items are (64-token tile, row chunk) pairs; the route kernel lists the
+// tiles of the experts in this family's band, so an expert with many tokens
+// gets more items rather than longer ones.  The grid is capped and each
+// workgroup walks items grid-strided, so a launch whose band holds no expert
+// costs a few microseconds whatever the bound on the tile count.
 template <bool GU>
 __global__ __launch_bounds__(kWave) void mgemv_kernel(MgArgs A) {
   __shared__ __align__(16) uint8_t tabs[kMgRows * (1 << kMaxBits) * 2];
-  const int t = (int)blockIdx.x / A.chunks;
-  const int ch = (int)blockIdx.x - t * A.chunks;
-  if (t >= uniform(*A.rt.num_mgtiles)) return;
-  const int e = uniform(A.rt.mgtiles[2 * t]);
-  const int m0 = uniform(A.rt.mgtiles[2 * t + 1]);
-  const int n_e = uniform(A.rt.counts[e]);
-  const int nm = n_e - m0 < kMgTileM ? n_e - m0 : kMgTileM;
-  const int off_e = uniform(A.rt.offsets[e]) + m0;
-  const int qv = uniform(A.q[2 * e + (GU ? 0 : 1)]);
-  switch (qv) {
-    case 3: mg_chunk<3, GU>(A, e, nm, off_e, ch, tabs); break;
-    case 4: mg_chunk<4, GU>(A, e, nm, off_e, ch, tabs); break;
-    case 5: mg_chunk<5, GU>(A, e, nm, off_e, ch, tabs); break;
-    case 6: mg_chunk<6, GU>(A, e, nm, off_e, ch, tabs); break;
-    case 7: mg_chunk<7, GU>(A, e, nm, off_e, ch, tabs); break;
-    case 8: mg_chunk<8, GU>(A, e, nm, off_e, ch, tabs); break;
-    default: mg_zero<GU>(A, nm, off_e, ch, m0 == 0); break;
+  const int items = uniform(*A.rt.num_mgtiles) * A.chunks;
+  for (int item = (int)blockIdx.x; item < items; item += (int)gridDim.x) {
+    if (item != (int)blockIdx.x) __syncthreads();   // the previous item's lookups are done before new tables land
+    const int t = item / A.chunks;
+    const int ch = item - t * A.chunks;
+    const int e = uniform(A.rt.mgtiles[2 * t]);
+    const int m0 = uniform(A.rt.mgtiles[2 * t + 1]);
+    const int n_e = uniform(A.rt.counts[e]);
+    const int nm = n_e - m0 < kMgTileM ? n_e - m0 : kMgTileM;
+    const int off_e = uniform(A.rt.offsets[e]) + m0;
+    const int qv = uniform(A.q[2 * e + (GU ? 0 : 1)]);
+    switch (qv) {
+      case 3: mg_chunk<3, GU>(A, e, nm, off_e, ch, tabs); break;
+      case 4: mg_chunk<4, GU>(A, e, nm, off_e, ch, tabs); break;
+      case 5: mg_chunk<5, GU>(A, e, nm, off_e, ch, tabs); break;
+      case 6: mg_chunk<6, GU>(A, e, nm, off_e, ch, tabs); break;
+      case 7: mg_chunk<7, GU>(A, e, nm, off_e, ch, tabs); break;
+      case 8: mg_chunk<8, GU>(A, e, nm, off_e, ch, tabs); break;
+      default: mg_zero<GU>(A, nm, off_e, ch, m0 == 0); break;
+    }
   }
 }
 
@@ -264,9 +273,10 @@ static hipError_t launch_mg(const ExpertArgs& a, const uint16_t* act, uint16_t* 
   const long long act_bytes = 2LL * (GU ? (long long)a.T * a.H : (long long)a.T * a.k * a.I);
   if (act_bytes >= 0x80000000LL) return hipErrorInvalidValue;
   A.act_bytes = (uint32_t)act_bytes;
-  const long long grid = (long long)mgtile_bound(a.E, a.T, a.k) * A.chunks;
+  long long grid = (long long)mgtile_bound(a.E, a.T, a.k) * A.chunks;
+  if (grid > 0x7FFFFFFFLL - kMgMaxGrid) return hipErrorInvalidValue;   // the kernel counts items in int
   if (grid == 0 || a.min_tokens >= a.max_tokens) return hipSuccess;
-  if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  if (grid > kMgMaxGrid) grid = kMgMaxGrid;
   hipLaunchKernelGGL(mgemv_kernel<GU>, dim3((unsigned)grid), dim3(kWave), 0, s, A);
   return hipGetLastError();
 }
