@@ -24,7 +24,7 @@ inline int mtile_bound(int E, int T, int k) {
   return (E < slots ? E : slots) + (slots + kMfmaTileM - 1) / kMfmaTileM;
 }
 
-constexpr int kMgTileM = 64;      // tokens per matrix-core GEMV pass
+constexpr int kMgTileM = 32;      // tokens per matrix-core GEMV pass
 
 inline int mgtile_bound(int E, int T, int k) {
   const int slots = T * k;

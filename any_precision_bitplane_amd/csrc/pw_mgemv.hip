@@ -1,5 +1,5 @@
 // Matrix-core GEMV kernels for experts with a moderate number of tokens (a
-// few to a few dozen; any count is handled, 64 tokens per pass over K).
+// few to a few hundred; any count is handled, 32 tokens per pass over K).
 // "Technical summary: PagedWeight", Core components 3 (fused mixed-precision
 // kernel): every block is read at its own committed bitwidth q from the
 // device page table.
@@ -7,7 +7,7 @@
 // A workgroup is one wave and owns 16 weight rows of one routed block for the
 // whole K range (gate_up: 8 gate rows and the matching 8 up rows; down: 16
 // rows).  Each weight is decoded exactly once, in registers, straight into the
-// matrix cores' B operand, and multiplies up to 64 tokens (four 16-token
+// matrix cores' B operand, and multiplies up to 32 tokens (two 16-token
 // groups) with v_mfma_f32_16x16x32_f16 -- no weight tile in LDS, no barrier in
 // the K loop.  For v_mfma_f32_16x16x32_f16 lane l supplies B column l & 15
 // (the weight row) and K slots 8 (l >> 4) .. +8, and A row l & 15 (the token)
@@ -19,9 +19,9 @@
 // x[token][32 w + 8b .. +8], one 16-byte load.  In a 512-wide super-chunk C,
 // group g reads words 16 C + 4 g .. +4 with one load per plane (the four
 // groups cover a row's 64-byte line) and sub-chunk i uses word 16 C + 4 g + i.
-// Plane words are requested two super-chunks ahead, activations at the start
-// of their sub-chunk (the decode covers their latency).  gate_up pairs gate and up rows
-// in columns n and n + 8, so SwiGLU is one lane swap on the accumulators.
+// Plane words are requested two super-chunks ahead and activations one
+// sub-chunk ahead.  gate_up pairs gate and up rows in columns n and n + 8, so
+// SwiGLU is one lane swap on the accumulators.
 #include "pw_device.h"
 #include "pw_internal.h"
 
@@ -29,7 +29,7 @@ namespace pw {
 
 constexpr int kMgRows = 16;
 constexpr long long kMgMaxGrid = 32768;   // workgroups per launch (several per SIMD)
-constexpr int kMgGroups = 4;                 // 16-token groups per wave
+constexpr int kMgGroups = 2;                 // 16-token groups per wave
 static_assert(16 * kMgGroups == kMgTileM, "a tile fills the token groups");
 
 typedef _Float16 mg_half8 __attribute__((ext_vector_type(8)));
@@ -142,8 +142,13 @@ __device__ __forceinline__ void mg_chunk(const MgArgs& A, int e, int n_e, int of
   for (int tg = 0; tg < kMgGroups; ++tg) acc[tg] = mg_float4{0.f, 0.f, 0.f, 0.f};
 
   // sub-chunk: plane word wd (its four plane bytes b = sub-steps)
-  auto sub = [&](const uint32_t (&P)[Q][4], int i, int wd) {
-    uint4 ar[kMgGroups][4];
+  // Software-pipelined sub-chunks (sub-chunk s = word 16 (s >> 2) + 4 g + (s & 3)):
+  // each step issues its lookups, then requests the next sub-chunk's
+  // activations and transposes its plane words while the lookups are in
+  // flight, and only then multiplies.  Unrolled over two super-chunks so every
+  // register index is static.
+  auto load_a = [&](uint4 (&ar)[kMgGroups][4], int s) {
+    const int wd = 16 * (s >> 2) + 4 * g + (s & 3);
 #pragma unroll
     for (int tg = 0; tg < kMgGroups; ++tg) {
       if (tg >= ntg) continue;
@@ -153,13 +158,14 @@ __device__ __forceinline__ void mg_chunk(const MgArgs& A, int e, int n_e, int of
         ar[tg][b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ars, (int)voff, 0, 0));
       }
     }
+  };
+  auto fields = [&](const uint32_t (&P)[Q][4], int i, uint32_t (&R)[8]) {
     uint32_t W8[Q];
 #pragma unroll
     for (int p = 0; p < Q; ++p) W8[p] = P[p][i];
-    uint32_t R[8];
     planes_to_fields<Q>(W8, R);
-    uint32_t packed[16];
-    GroupDecode<Q, 0>::run(R, base, packed);
+  };
+  auto multiply = [&](const uint4 (&ar)[kMgGroups][4], const uint32_t (&packed)[16]) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const mg_half8 bop = __builtin_bit_cast(
@@ -172,22 +178,39 @@ __device__ __forceinline__ void mg_chunk(const MgArgs& A, int e, int n_e, int of
       }
     }
   };
-  auto superchunk = [&](const uint32_t (&P)[Q][4], int C) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int wd = 16 * C + 4 * g + i;
-      if (16 * C + i >= W) break;   // no group has a word left (uniform)
-      sub(P, i, wd);
-    }
-  };
 
-  for (int C = 0; C < ns; C += 2) {
-    superchunk(P0, C);
-    load_planes(P0, C + 2);
-    if (C + 1 >= ns) break;
-    superchunk(P1, C + 1);
+  const int S = 4 * ns;   // sub-chunks (past the last word they read zero activations)
+  uint4 A0[kMgGroups][4], A1[kMgGroups][4];
+  uint32_t R[8];
+  load_a(A0, 0);
+  fields(P0, 0, R);
+  // one step: lookups of s (fields in R), next activations into An, fields of s + 1
+  // from (Pn, in) into R, then the products of s with Ac
+#define PW_MG_STEP(Ac, An, Pn, in, s_)                         \
+  {                                                            \
+    uint32_t packed[16];                                       \
+    GroupDecode<Q, 0>::run(R, base, packed);                   \
+    if ((s_) + 1 < S) {                                        \
+      load_a(An, (s_) + 1);                                    \
+      fields(Pn, in, R);                                       \
+    }                                                          \
+    multiply(Ac, packed);                                      \
+  }
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    const int C = s0 >> 2;
+    PW_MG_STEP(A0, A1, P0, 1, s0);
+    PW_MG_STEP(A1, A0, P0, 2, s0 + 1);
+    PW_MG_STEP(A0, A1, P0, 3, s0 + 2);
+    PW_MG_STEP(A1, A0, P1, 0, s0 + 3);
+    load_planes(P0, C + 2);   // super-chunk C is transposed; its buffer takes C + 2
+    if (s0 + 4 >= S) break;
+    PW_MG_STEP(A0, A1, P1, 1, s0 + 4);
+    PW_MG_STEP(A1, A0, P1, 2, s0 + 5);
+    PW_MG_STEP(A0, A1, P1, 3, s0 + 6);
+    PW_MG_STEP(A1, A0, P0, 0, s0 + 7);
     load_planes(P1, C + 3);
   }
+#undef PW_MG_STEP
 
   // acc[tg] element v: token 16 tg + 4 g + v, tile column n
 #pragma unroll
@@ -229,10 +252,7 @@ __device__ __forceinline__ void mg_zero(const MgArgs& A, int n_e, int off_e, int
   if (threadIdx.x == 0 && ch == 0 && first_tile) raise_status(A.rt.status, PW_DEV_BAD_BITWIDTH);
 }
 
-// One wave per (64-token tile, row chunk): the route kernel lists the tiles of
-// the experts in this family's band, so an expert with many tokens gets more
-// waves instead of longer ones.
-// Work items are (64-token tile, row chunk) pairs; the route kernel lists the
+// Work items are (32-token tile, row chunk) pairs; the route kernel lists the
 // tiles of the experts in this family's band, so an expert with many tokens
 // gets more items rather than longer ones.  The grid is capped and each
 // workgroup walks items grid-strided, so a launch whose band holds no expert

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
   if (wave == 0) {
     // Lane l owns experts 4l .. 4l+3 (E <= 256).  Four exclusive scans over the
     // wave give each expert its offset, its index in the active list and the
-    // first entries of its MFMA (256-token) and matrix-core GEMV (64-token)
+    // first entries of its MFMA (256-token) and matrix-core GEMV (32-token)
     // tiles, so every list is written in parallel, in expert order.
     int c[4], na[4], nm[4], ng[4];
     int sc = 0, sa = 0, sm = 0, sg = 0;
