@@ -8,8 +8,8 @@
 // integer atomics (order-free, so deterministic), one wave's scan over <= 256
 // experts (which also lists the token tiles of the MFMA and matrix-core GEMV
 // families), then the slots in chunks of 1024 in slot order.  Inside a chunk each
-// wave ranks its lanes per expert with ballots, and the per-wave counts are
-// scanned per expert, so a slot's position is
+// wave ranks its lanes per expert with one ballot per expert-id bit, and the
+// per-wave counts are scanned per expert, so a slot's position is
 //   offsets[e] + #{earlier slots routed to e}
 // exactly (a stable counting sort).
 #include "pw_device.h"
@@ -113,17 +113,17 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
       e = ids[s];
       if (e < 0 || e >= E) e = -1;
     }
+    // lanes routed to the same expert: one ballot per bit of the expert id
+    // (at most 8 for E <= 256) instead of one round per distinct expert
+    unsigned long long same = __ballot(e >= 0);
+    for (int bit = 0; (1 << bit) < E; ++bit) {
+      const unsigned long long ones = __ballot(e >= 0 && ((e >> bit) & 1));
+      same &= ((e >> bit) & 1) ? ones : ~ones;
+    }
     int rank = 0;
-    unsigned long long todo = __ballot(e >= 0);
-    while (todo) {
-      const int leader = __ffsll(todo) - 1;
-      const int le = __shfl(e, leader, kWave);
-      const unsigned long long m = __ballot(e == le);
-      if (e == le) {
-        rank = __popcll(m & ((1ull << lane) - 1ull));
-        if (lane == leader) wcnt[wave][le] = __popcll(m);
-      }
-      todo &= ~m;
+    if (e >= 0) {
+      rank = __popcll(same & ((1ull << lane) - 1ull));
+      if (rank == 0) wcnt[wave][e] = __popcll(same);   // the expert's first lane in the wave
     }
     __syncthreads();
 
