@@ -300,3 +300,38 @@ def test_routing_statistics_plan_and_commit(torch, tiny, static):
     paged.execute(copy)
     assert B.pw_pager_arena_used(paged.pager) == sum(rnd(int(plan[b]) * int(pb[b])) for b in range(len(pb)))
     paged.close()
+
+
+def test_forwards_during_a_full_size_reload_use_the_old_bitwidths(torch):
+    say("pager: Qwen-shaped decode layer, every block at 3 bits, layer bitwidths reloaded (about 150 MB of planes) "
+        "on a copy stream while 40 forwards run")
+    from any_precision_bitplane_amd.device import DeviceLayer
+    wl = synth.WORKLOADS["qwen_decode"]
+    layer = synth.make_routed_layer(wl)
+    static = DeviceLayer(layer)
+    q3 = np.full(layer.q.shape, 3, np.uint8)
+    want3 = static_y(torch, static, q3)
+    want = static_y(torch, static, layer.q)
+    paged = make_paged(layer, 2 * full_arena(layer))
+    copy = torch.cuda.Stream()
+    paged.request(q3)
+    paged.execute(copy)
+    paged.commit(wait=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(paged_y(torch, paged), want3)
+    paged.request(layer.q)
+    paged.execute(copy)                  # host-to-device copies of planes 3..q-1 in flight
+    seen_in_transfer = any(paged.info(b).state == B.PW_PAGE_IN_TRANSFER for b in range(paged.nblocks))
+    ys = [torch.empty_like(paged.y) for _ in range(40)]
+    for y in ys:
+        paged.forward(y=y)
+    torch.cuda.synchronize()
+    for i, y in enumerate(ys):
+        assert np.array_equal(y.cpu().numpy().view(np.uint16), want3), i
+    assert seen_in_transfer
+    paged.commit(wait=True)
+    y = paged_y(torch, paged)
+    assert np.array_equal(y, want)
+    oracle_check(layer, y, layer.q)
+    assert paged.status() == 0
+    paged.close()
