@@ -231,17 +231,23 @@ pw_status pw_pager_execute(pw_pager* p, void* copy_stream) {
       e = hipMemcpyAsync(p->arena + dst + ext_bytes(k, k.resident),
                          reinterpret_cast<const uint8_t*>(k.host) + ext_bytes(k, k.resident),
                          ext_bytes(k, d - k.resident), hipMemcpyHostToDevice, s);
-    // the block is staged even if a copy failed to enqueue, so its range stays
-    // reserved; the error is returned below
+    if (e != hipSuccess) {
+      // not staged: the range goes back (any copy that did enqueue runs on this
+      // stream before whatever reuses it) and the block keeps its committed state
+      if (dst == k.off)
+        p->alloc.release(k.off + p->alloc.round(ext_bytes(k, k.resident)),
+                         p->alloc.round(ext_bytes(k, d)) - p->alloc.round(ext_bytes(k, k.resident)));
+      else
+        p->alloc.release(dst, ext_bytes(k, d));
+      copied = copied || moved;
+      st = PW_ERR_HIP;
+      break;
+    }
     copied = true;
     k.pending = true;
     k.target = d;
     k.new_off = dst;
     k.event = ev_index;
-    if (e != hipSuccess) {
-      st = PW_ERR_HIP;
-      break;
-    }
   }
   if (copied) {
     // one fence for every copy this call enqueued (also when it stopped early)

@@ -306,8 +306,9 @@ pw_status pw_pager_request(pw_pager* pager, int32_t b, int32_t desired);
 /* Stage every block whose desired bitwidth differs from its committed one:
  * enqueue on copy_stream the copies of the planes it lacks.  Blocks staged
  * earlier and not yet committed are left alone.  PW_ERR_OUT_OF_MEMORY when the
- * arena has no room: the blocks staged before that stay staged, the rest
- * unchanged (commit lowered blocks first to free their planes). */
+ * arena has no room, PW_ERR_HIP when a copy cannot be enqueued: the blocks
+ * staged before that stay staged, the rest keep their committed state
+ * (commit lowered blocks first to free their planes). */
 pw_status pw_pager_execute(pw_pager* pager, void* copy_stream);
 
 /* Safe boundary: commit every staged block in one step.  If copies are still
