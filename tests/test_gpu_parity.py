@@ -431,3 +431,30 @@ def test_forward_auto_edge_layers(torch, H, I, E, k, T, seed):
     dev, y = run_forward(torch, L, B.PW_PATH_AUTO)
     assert dev.status() == 0
     compare(y, oracle_y(L), f"auto edge E={E} k={k} T={T}")
+
+
+def _random_case(seed):
+    rng = np.random.default_rng(9000 + seed)
+    H = 32 * int(rng.integers(1, 40))
+    I = 32 * int(rng.integers(1, 40))
+    E = int(rng.integers(1, 24))
+    k = int(rng.integers(1, min(E, 6) + 1))
+    T = int(rng.choice([1, 2, 3, 5, 8, 17, 40, 70, 130, 300]))
+    L = custom_layer(H, I, E, k, T, 9100 + seed)
+    L.q[:] = rng.integers(3, 9, L.q.shape).astype(np.uint8)
+    if seed % 5 == 0 and k > 1:   # some tokens list one expert twice
+        L.ids[::3, 1] = L.ids[::3, 0]
+    path = [B.PW_PATH_AUTO, B.PW_PATH_GEMV, B.PW_PATH_MGEMV, B.PW_PATH_MFMA][seed % 4]
+    return L, path
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_forward_random_layers_every_path(torch, seed):
+    """Seeded random shapes (H, I multiples of 32 up to 1248; E up to 23; k up
+    to 6; T from 1 to 300), random bitwidths, some duplicate ids, each kernel
+    family forced in turn and AUTO."""
+    L, path = _random_case(seed)
+    wl = L.wl
+    say(f"forward random seed={seed} H={wl.H} I={wl.I} E={wl.E} k={wl.k} T={wl.T} path={path}")
+    _, y = run_forward(torch, L, path)
+    compare(y, oracle_y(L), f"random seed={seed} path={path}")
