@@ -239,7 +239,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the layer's multi-GPU sharding is "
-              f"described in DESIGN.md but not built.", file=sys.stderr)
+              f"designed (expert parallelism over RCCL) but not built.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -64,7 +64,7 @@ typedef int32_t pw_status;
 #define PW_ERR_WORKSPACE         -4  /* workspace too small                    */
 #define PW_ERR_ALIGNMENT         -5  /* pointer not 16-byte aligned            */
 #define PW_ERR_HIP               -6  /* a HIP runtime call failed              */
-#define PW_ERR_UNSUPPORTED       -7  /* option not available in this build     */
+#define PW_ERR_UNSUPPORTED       -7  /* option the library does not support     */
 #define PW_ERR_OUT_OF_MEMORY     -8  /* pager: no free arena range large enough */
 
 /* device status bits (pw_get_device_status) */
