@@ -15,13 +15,16 @@ using namespace pw;
 
 namespace {
 
-// AUTO: experts with at least this many routed tokens take the matrix-core
-// GEMV kernels, and from the second threshold on the MFMA kernels.
-// Measured on the Qwen- and Mixtral-shaped layers: once a batch averages 3 or
-// more slots per routed expert, the matrix-core GEMV taking every expert below
-// the MFMA band beats any mix with the GEMV (one launch fewer per product), and
-// it beats the dequant-to-LDS MFMA kernels (one 256-token tile) up to about
-// 256 tokens.
+// AUTO picks one kernel family per call from the mean number of routed slots
+// per routed expert (measured on the Qwen- and Mixtral-shaped layers: the
+// families run one after another, so a call that mixes them pays each one's
+// fill and drain): GEMV below a mean of 2, the matrix-core GEMV up to 64, MFMA
+// above.  The MFMA/matrix-core crossover lies near a mean of 50 on the Qwen
+// shape and between 64 and 96 on the Mixtral shape.
+constexpr int kGemvBelowMean = 2;
+constexpr int kMgemvUpToMean = 64;
+// With explicit thresholds in the options (either one > 0) AUTO splits the
+// experts into token-count bands instead; these fill the one not given.
 constexpr int kDefaultMgemvMinTokens = 1;
 constexpr int kDefaultMfmaMinTokens = 256;
 
@@ -109,26 +112,32 @@ pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T, const uint16_t* x
   // MFMA [b2, inf).  A band whose lower end no expert can reach (an expert
   // gets at most T tokens unless a token lists it twice) is not launched and
   // the band below it takes its experts.
+  const int max_slots = T * k;
+  const int routed_bound = E < max_slots ? E : max_slots;   // routed experts, at most
+  // the matrix-core GEMV addresses activations with 32-bit offsets
+  const bool mg_ok = 2LL * (long long)T * (H > k * I ? H : k * I) < 0x80000000LL;
+  if (path == PW_PATH_MGEMV && !mg_ok) return PW_ERR_UNSUPPORTED_SHAPE;
+  const bool explicit_bands = opts && (opts->mfma_min_tokens > 0 || opts->mgemv_min_tokens > 0);
   int b1, b2;
   if (path == PW_PATH_GEMV) b1 = b2 = INT_MAX;
   else if (path == PW_PATH_MFMA) b1 = b2 = 0;
   else if (path == PW_PATH_MGEMV) { b1 = 0; b2 = INT_MAX; }
-  else {
-    b2 = (opts && opts->mfma_min_tokens > 0) ? opts->mfma_min_tokens : kDefaultMfmaMinTokens;
-    b1 = (opts && opts->mgemv_min_tokens > 0) ? opts->mgemv_min_tokens : kDefaultMgemvMinTokens;
+  else if (explicit_bands) {
+    b2 = opts->mfma_min_tokens > 0 ? opts->mfma_min_tokens : kDefaultMfmaMinTokens;
+    b1 = opts->mgemv_min_tokens > 0 ? opts->mgemv_min_tokens : kDefaultMgemvMinTokens;
     if (b1 > b2) b1 = b2;
+  } else if ((long long)max_slots < (long long)kGemvBelowMean * routed_bound) {
+    b1 = b2 = INT_MAX;                        // decode: GEMV alone
+  } else if ((long long)max_slots <= (long long)kMgemvUpToMean * routed_bound && mg_ok) {
+    b1 = 0; b2 = INT_MAX;                     // moderate batches: matrix-core GEMV alone
+  } else {
+    b1 = b2 = 0;                              // prefill: MFMA alone
   }
-  const int max_slots = T * k;
-  // the matrix-core GEMV addresses activations with 32-bit offsets
-  const bool mg_ok = 2LL * (long long)T * (H > k * I ? H : k * I) < 0x80000000LL;
-  if (path == PW_PATH_MGEMV && !mg_ok) return PW_ERR_UNSUPPORTED_SHAPE;
   const bool use_mfma = b2 <= T;
   if (!use_mfma) b2 = INT_MAX;
-  // AUTO keeps batches averaging fewer than 3 slots per routed expert on the
-  // GEMV kernels alone (which route by themselves up to 64 slots: three
-  // launches for a decode step); from 3 on the matrix-core GEMV is faster
-  const int routed_bound = E < max_slots ? E : max_slots;
-  const bool mg_worth = (long long)max_slots >= 3LL * routed_bound;
+  // with explicit bands, calls averaging fewer than kGemvBelowMean slots per
+  // routed expert still stay on the GEMV kernels alone
+  const bool mg_worth = !explicit_bands || (long long)max_slots >= (long long)kGemvBelowMean * routed_bound;
   const bool use_mg = b1 < b2 && b1 <= T && mg_ok && (path == PW_PATH_MGEMV || mg_worth);
   if (!use_mg) b1 = b2;
   const bool use_gemv = b1 > 1;     // a routed expert has at least one token

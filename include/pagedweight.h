@@ -89,8 +89,15 @@ typedef struct {
 } pw_block_desc;
 
 /* Kernel family for the expert products. */
-#define PW_PATH_AUTO  0  /* per expert by its token count n: GEMV below mgemv_min_tokens,
-                            matrix-core GEMV up to mfma_min_tokens, MFMA from there */
+#define PW_PATH_AUTO  0  /* one family per call by the mean routed slots per
+                            routed expert m = T*top_k / min(E, T*top_k): GEMV for
+                            m < 2, matrix-core GEMV for 2 <= m <= 64, MFMA above.
+                            If either *_min_tokens option is > 0 and m >= 2, per
+                            expert by its token count n instead: GEMV below
+                            mgemv_min_tokens (default 1), matrix-core GEMV below
+                            mfma_min_tokens (default 256), MFMA from there; with
+                            m < 2 the GEMV still takes every expert below
+                            mfma_min_tokens */
 #define PW_PATH_GEMV  1  /* every expert on the bit-plane GEMV kernels            */
 #define PW_PATH_MFMA  2  /* every expert on the dequant-to-LDS MFMA kernels       */
 #define PW_PATH_MGEMV 3  /* every expert on the matrix-core GEMV kernels          */
@@ -104,13 +111,15 @@ typedef struct {
 
 typedef struct {
   int32_t path;              /* PW_PATH_*                                     */
-  int32_t mfma_min_tokens;   /* AUTO: MFMA from this many tokens; <= 0: default */
+  int32_t mfma_min_tokens;   /* AUTO bands: MFMA from this many tokens per
+                                expert; <= 0: per-call rule or default 256    */
   /* Optional hipEvent_t handles (as void*).  If stage_events[0] is non-NULL,
    * event s is recorded on `stream` right before stage s and event
    * PW_NUM_STAGES after the last stage, so the caller can time each stage. */
   void* stage_events[PW_NUM_STAGES + 1];
-  int32_t mgemv_min_tokens;  /* AUTO: matrix-core GEMV from this many tokens
-                                (below mfma_min_tokens); <= 0: default        */
+  int32_t mgemv_min_tokens;  /* AUTO bands: matrix-core GEMV from this many
+                                tokens per expert (below mfma_min_tokens);
+                                <= 0: per-call rule or default 1              */
   int32_t reserved;
 } pw_moe_options;
 
@@ -146,7 +155,7 @@ pw_status pw_workspace_init(void* workspace, size_t workspace_bytes, void* strea
  *           pw_workspace_bytes(shape, T) bytes, 256-byte aligned; its first
  *           bytes hold the status word.  Concurrent calls need distinct
  *           workspaces.
- *   opts    host, may be NULL (AUTO path, default threshold, no events).
+ *   opts    host, may be NULL (AUTO path, per-call rule, no events).
  * Accumulation is fp32; h is rounded to fp16 before the down product.
  * Results are deterministic: the same inputs give the same bits. */
 pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T,

@@ -404,7 +404,7 @@ def test_forward_mgemv_invalid_bitwidth_flagged_and_zero(torch):
 def test_forward_auto_three_families(torch):
     """Batched Qwen-shaped layer with AUTO bands at 4 and 64 tokens: experts
     below 4 tokens on the GEMV kernels, 4..63 on the matrix-core GEMV, 64 and
-    more on the MFMA kernels, in one call; then the default bands."""
+    more on the MFMA kernels, in one call; then the default per-call rule."""
     L = layer_for("qwen_batched")
     counts = np.bincount(L.ids.reshape(-1), minlength=L.wl.E)
     c = counts[counts > 0]
@@ -416,9 +416,9 @@ def test_forward_auto_three_families(torch):
     torch.cuda.synchronize()
     ref = oracle_y(L)
     compare(dev.y.float().cpu().numpy(), ref, "qwen_batched auto three families")
-    say("forward qwen_batched T=256 AUTO default bands")
+    say("forward qwen_batched T=256 AUTO default rule")
     _, y = run_forward(torch, L, B.PW_PATH_AUTO, dev=dev)
-    compare(y, ref, "qwen_batched auto default bands")
+    compare(y, ref, "qwen_batched auto default rule")
 
 
 @pytest.mark.parametrize("H,I,E,k,T,seed", [(256, 512, 1, 1, 5, 61), (256, 512, 1, 1, 300, 62),
