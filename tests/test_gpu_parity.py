@@ -433,6 +433,32 @@ def test_forward_auto_edge_layers(torch, H, I, E, k, T, seed):
     compare(y, oracle_y(L), f"auto edge E={E} k={k} T={T}")
 
 
+_FAMILIES = {B.PW_PATH_GEMV: "gemv", B.PW_PATH_MGEMV: "mgemv", B.PW_PATH_MFMA: "mfma"}
+
+
+@pytest.mark.parametrize("T,family", [(7, B.PW_PATH_GEMV), (8, B.PW_PATH_MGEMV), (256, B.PW_PATH_MGEMV),
+                                      (257, B.PW_PATH_MFMA)])
+def test_auto_family_at_the_mean_edges(torch, T, family):
+    """AUTO runs one kernel family per call, chosen from the mean routed slots
+    per routed expert m = T*k / min(E, T*k): GEMV for m < 2, matrix-core GEMV
+    for 2 <= m <= 64, MFMA above.  With E = 8, k = 2 the batches T = 7 / 8 /
+    256 / 257 sit on either side of both edges.  Every family is deterministic
+    and sums in its own order, so AUTO's output equals the chosen family's
+    forced output bit for bit and differs from the other two."""
+    L = custom_layer(1024, 1024, 8, 2, T, 700 + T)
+    say(f"forward AUTO family edge T={T} (expect {_FAMILIES[family]})")
+    dev, y_auto = run_forward(torch, L, B.PW_PATH_AUTO)
+    assert dev.status() == 0
+    same = []
+    for f, name in _FAMILIES.items():
+        say(f"  forced {name}")
+        _, y_f = run_forward(torch, L, f, dev=dev)
+        if np.array_equal(y_auto, y_f):
+            same.append(f)
+    assert same == [family], [_FAMILIES[f] for f in same]
+    compare(y_auto, oracle_y(L), f"auto family edge T={T}")
+
+
 def _random_case(seed):
     rng = np.random.default_rng(9000 + seed)
     H = 32 * int(rng.integers(1, 40))
