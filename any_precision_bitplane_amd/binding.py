@@ -66,6 +66,11 @@ class PwPageInfo(ctypes.Structure):
                 ("state", c_int32), ("reserved", c_int32), ("arena_offset", ctypes.c_uint64)]
 
 
+class PwPathInfo(ctypes.Structure):
+    _fields_ = [("gemv", c_int32), ("mgemv", c_int32), ("mfma", c_int32), ("mgemv_from", c_int32),
+                ("mfma_from", c_int32), ("inline_route", c_int32), ("down_kparts", c_int32), ("launches", c_int32)]
+
+
 class PwPlanProblem(ctypes.Structure):
     _fields_ = [("num_blocks", c_int32), ("num_experts", c_int32), ("expert_of", c_void_p),
                 ("plane_bytes", c_void_p), ("sensitivity", c_void_p), ("correction", c_void_p),
@@ -101,6 +106,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "pw_workspace_init": (c_int32, [c_void_p, c_size_t, c_void_p]),
         "pw_moe_forward": (c_int32, [POINTER(PwMoeShape), c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_void_p, c_void_p, c_size_t, POINTER(PwMoeOptions), c_void_p]),
+        "pw_moe_path_info": (c_int32, [POINTER(PwMoeShape), c_int32, POINTER(PwMoeOptions), POINTER(PwPathInfo)]),
         "pw_dequant_block": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
         "pw_get_device_status": (c_int32, [c_void_p, POINTER(c_uint32), c_void_p]),
         "pw_router_topk": (c_int32, [POINTER(PwMoeShape), c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -130,7 +136,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
 
 def exported_symbols() -> Sequence[str]:
     return ["pw_abi_version", "pw_status_str", "pw_plane_words", "pw_lut_elems", "pw_lut_offset",
-            "pw_check_shape", "pw_workspace_bytes", "pw_workspace_init", "pw_moe_forward",
+            "pw_check_shape", "pw_workspace_bytes", "pw_workspace_init", "pw_moe_forward", "pw_moe_path_info",
             "pw_dequant_block", "pw_get_device_status", "pw_pager_create", "pw_pager_destroy",
             "pw_pager_set_block", "pw_pager_request", "pw_pager_execute", "pw_pager_commit", "pw_pager_info",
             "pw_pager_arena_used", "pw_router_topk", "pw_moe_forward_routed", "pw_plan_bitwidths"]
@@ -217,6 +223,13 @@ def pw_moe_forward(shp: PwMoeShape, T: int, x, ids, w, blocks, q, y, workspace,
     if check:
         _check(st, "pw_moe_forward")
     return st
+
+
+def pw_moe_path_info(shp: PwMoeShape, T: int, opts: Optional[PwMoeOptions] = None) -> PwPathInfo:
+    info = PwPathInfo()
+    _check(load().pw_moe_path_info(ctypes.byref(shp), T, ctypes.byref(opts) if opts is not None else None,
+                                   ctypes.byref(info)), "pw_moe_path_info")
+    return info
 
 
 def pw_dequant_block(planes, lut_all, N: int, K: int, q: int, w_out, stream=None, check: bool = True) -> int:

@@ -19,8 +19,8 @@ namespace {
 // per routed expert (measured on the Qwen- and Mixtral-shaped layers: the
 // families run one after another, so a call that mixes them pays each one's
 // fill and drain): GEMV below a mean of 2, the matrix-core GEMV up to 64, MFMA
-// above.  The MFMA/matrix-core crossover lies near a mean of 50 on the Qwen
-// shape and between 64 and 96 on the Mixtral shape.
+// above.  The MFMA/matrix-core crossover lies at a mean of about 60-68 on the
+// Qwen shape and 80-96 on the Mixtral shape.
 constexpr int kGemvBelowMean = 2;
 constexpr int kMgemvUpToMean = 64;
 // With explicit thresholds in the options (either one > 0) AUTO splits the
@@ -43,6 +43,60 @@ pw_status check_shape(const pw_moe_shape* s, int32_t T) {
 }
 
 pw_status hip_status(hipError_t e) { return e == hipSuccess ? PW_OK : PW_ERR_HIP; }
+
+// Which kernel families a call runs and how the experts split between them:
+// token-count bands per expert, GEMV [0, b1), matrix-core GEMV [b1, b2), MFMA
+// [b2, inf).  A band whose lower end no expert can reach (an expert gets at
+// most T tokens unless a token lists it twice) is not launched and the band
+// below it takes its experts.
+struct Plan {
+  bool gemv, mgemv, mfma;
+  int b1, b2;          // b2 == INT_MAX: no MFMA launch
+  bool inline_route;   // <= 64 slots on the GEMV alone: the gate_up kernel routes
+  int kparts;          // parts of the GEMV down product's K range
+};
+
+pw_status make_plan(const pw_moe_shape* shape, int32_t T, const pw_moe_options* opts, Plan& pl) {
+  const int path = opts ? opts->path : PW_PATH_AUTO;
+  if (path != PW_PATH_AUTO && path != PW_PATH_GEMV && path != PW_PATH_MFMA && path != PW_PATH_MGEMV)
+    return PW_ERR_INVALID_ARG;
+  const int H = shape->hidden, I = shape->inter, E = shape->num_experts, k = shape->top_k;
+  const int max_slots = T * k;
+  const int routed_bound = E < max_slots ? E : max_slots;   // routed experts, at most
+  // the matrix-core GEMV addresses activations with 32-bit offsets
+  const bool mg_ok = 2LL * (long long)T * (H > k * I ? H : k * I) < 0x80000000LL;
+  if (path == PW_PATH_MGEMV && !mg_ok) return PW_ERR_UNSUPPORTED_SHAPE;
+  const bool explicit_bands = opts && (opts->mfma_min_tokens > 0 || opts->mgemv_min_tokens > 0);
+  int b1, b2;
+  if (path == PW_PATH_GEMV) b1 = b2 = INT_MAX;
+  else if (path == PW_PATH_MFMA) b1 = b2 = 0;
+  else if (path == PW_PATH_MGEMV) { b1 = 0; b2 = INT_MAX; }
+  else if (explicit_bands) {
+    b2 = opts->mfma_min_tokens > 0 ? opts->mfma_min_tokens : kDefaultMfmaMinTokens;
+    b1 = opts->mgemv_min_tokens > 0 ? opts->mgemv_min_tokens : kDefaultMgemvMinTokens;
+    if (b1 > b2) b1 = b2;
+  } else if ((long long)max_slots < (long long)kGemvBelowMean * routed_bound) {
+    b1 = b2 = INT_MAX;                        // decode: GEMV alone
+  } else if ((long long)max_slots <= (long long)kMgemvUpToMean * routed_bound && mg_ok) {
+    b1 = 0; b2 = INT_MAX;                     // moderate batches: matrix-core GEMV alone
+  } else {
+    b1 = b2 = 0;                              // prefill: MFMA alone
+  }
+  pl.mfma = b2 <= T;
+  if (!pl.mfma) b2 = INT_MAX;
+  // with explicit bands, calls averaging fewer than kGemvBelowMean slots per
+  // routed expert still stay on the GEMV kernels alone
+  const bool mg_worth = !explicit_bands || (long long)max_slots >= (long long)kGemvBelowMean * routed_bound;
+  pl.mgemv = b1 < b2 && b1 <= T && mg_ok && (path == PW_PATH_MGEMV || mg_worth);
+  if (!pl.mgemv) b1 = b2;
+  pl.gemv = b1 > 1;     // a routed expert has at least one token
+  pl.b1 = b1;
+  pl.b2 = b2;
+  pl.inline_route = max_slots <= 64 && !pl.mfma && !pl.mgemv;
+  // the other families write one K part of o; the GEMV splits K only when it runs alone
+  pl.kparts = (pl.mfma || pl.mgemv) ? 1 : down_kparts(H, I, E, k, T);
+  return PW_OK;
+}
 
 }  // namespace
 
@@ -108,40 +162,11 @@ pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T, const uint16_t* x
   const WsLayout L = ws_layout(H, I, E, k, T);
   if (workspace_bytes < L.total) return PW_ERR_WORKSPACE;
 
-  // Token-count bands per expert: GEMV [0, b1), matrix-core GEMV [b1, b2),
-  // MFMA [b2, inf).  A band whose lower end no expert can reach (an expert
-  // gets at most T tokens unless a token lists it twice) is not launched and
-  // the band below it takes its experts.
-  const int max_slots = T * k;
-  const int routed_bound = E < max_slots ? E : max_slots;   // routed experts, at most
-  // the matrix-core GEMV addresses activations with 32-bit offsets
-  const bool mg_ok = 2LL * (long long)T * (H > k * I ? H : k * I) < 0x80000000LL;
-  if (path == PW_PATH_MGEMV && !mg_ok) return PW_ERR_UNSUPPORTED_SHAPE;
-  const bool explicit_bands = opts && (opts->mfma_min_tokens > 0 || opts->mgemv_min_tokens > 0);
-  int b1, b2;
-  if (path == PW_PATH_GEMV) b1 = b2 = INT_MAX;
-  else if (path == PW_PATH_MFMA) b1 = b2 = 0;
-  else if (path == PW_PATH_MGEMV) { b1 = 0; b2 = INT_MAX; }
-  else if (explicit_bands) {
-    b2 = opts->mfma_min_tokens > 0 ? opts->mfma_min_tokens : kDefaultMfmaMinTokens;
-    b1 = opts->mgemv_min_tokens > 0 ? opts->mgemv_min_tokens : kDefaultMgemvMinTokens;
-    if (b1 > b2) b1 = b2;
-  } else if ((long long)max_slots < (long long)kGemvBelowMean * routed_bound) {
-    b1 = b2 = INT_MAX;                        // decode: GEMV alone
-  } else if ((long long)max_slots <= (long long)kMgemvUpToMean * routed_bound && mg_ok) {
-    b1 = 0; b2 = INT_MAX;                     // moderate batches: matrix-core GEMV alone
-  } else {
-    b1 = b2 = 0;                              // prefill: MFMA alone
-  }
-  const bool use_mfma = b2 <= T;
-  if (!use_mfma) b2 = INT_MAX;
-  // with explicit bands, calls averaging fewer than kGemvBelowMean slots per
-  // routed expert still stay on the GEMV kernels alone
-  const bool mg_worth = !explicit_bands || (long long)max_slots >= (long long)kGemvBelowMean * routed_bound;
-  const bool use_mg = b1 < b2 && b1 <= T && mg_ok && (path == PW_PATH_MGEMV || mg_worth);
-  if (!use_mg) b1 = b2;
-  const bool use_gemv = b1 > 1;     // a routed expert has at least one token
-  const int thresh = b2;            // MFMA from here (INT_MAX: not launched)
+  Plan pl;
+  st = make_plan(shape, T, opts, pl);
+  if (st != PW_OK) return st;
+  const bool use_gemv = pl.gemv, use_mg = pl.mgemv, use_mfma = pl.mfma;
+  const int b1 = pl.b1, b2 = pl.b2, thresh = pl.b2;
 
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   Route rt;
@@ -159,8 +184,7 @@ pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T, const uint16_t* x
   uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
   float* o = reinterpret_cast<float*>(ws + L.o);
 
-  const bool small = max_slots <= 64;
-  const bool inline_route = small && !use_mfma && !use_mg;
+  const bool inline_route = pl.inline_route;
   ExpertArgs mfma{H, I, E, k, T, blocks, q, rt, thresh == 0 ? 1 : thresh, INT_MAX};
   ExpertArgs mg{H, I, E, k, T, blocks, q, rt, b1 == 0 ? 1 : b1, b2};
   GemvLaunch g{};
@@ -171,7 +195,7 @@ pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T, const uint16_t* x
   g.max_tokens = b1;
   g.x = x; g.h = h; g.o = o;
   // the other families write one K part of o; the GEMV splits K only when it runs alone
-  g.kparts = (use_mfma || use_mg) ? 1 : down_kparts(H, I, E, k, T);
+  g.kparts = pl.kparts;
 
   hipStream_t s = (hipStream_t)stream;
   void* const* ev = (opts && opts->stage_events[0]) ? opts->stage_events : nullptr;
@@ -216,6 +240,27 @@ pw_status pw_router_topk(const pw_moe_shape* shape, int32_t T, const uint16_t* x
                                   stat_count, stat_mass, (hipStream_t)stream));
 }
 
+pw_status pw_moe_path_info(const pw_moe_shape* shape, int32_t T, const pw_moe_options* opts, pw_path_info* info) {
+  if (!info) return PW_ERR_INVALID_ARG;
+  pw_status st = check_shape(shape, T);
+  if (st != PW_OK) return st;
+  memset(info, 0, sizeof(*info));
+  if (T == 0) return PW_OK;
+  Plan pl;
+  st = make_plan(shape, T, opts, pl);
+  if (st != PW_OK) return st;
+  info->gemv = pl.gemv ? 1 : 0;
+  info->mgemv = pl.mgemv ? 1 : 0;
+  info->mfma = pl.mfma ? 1 : 0;
+  info->mgemv_from = pl.mgemv ? (pl.b1 == 0 ? 1 : pl.b1) : 0;
+  info->mfma_from = pl.mfma ? (pl.b2 == 0 ? 1 : pl.b2) : 0;
+  info->inline_route = pl.inline_route ? 1 : 0;
+  info->down_kparts = pl.kparts;
+  const int families = (int)pl.gemv + (int)pl.mgemv + (int)pl.mfma;
+  info->launches = (pl.inline_route ? 0 : 1) + 2 * families + 1;
+  return PW_OK;
+}
+
 pw_status pw_moe_forward_routed(const pw_moe_shape* shape, int32_t T, const uint16_t* x, const uint16_t* router_w,
                                 const pw_block_desc* blocks, const uint8_t* q, uint16_t* y, uint32_t* stat_count,
                                 float* stat_mass, void* workspace, size_t workspace_bytes, const pw_moe_options* opts,
@@ -233,9 +278,9 @@ pw_status pw_moe_forward_routed(const pw_moe_shape* shape, int32_t T, const uint
   // argument checks of the forward before anything is enqueued
   if (!blocks || !q || !y) return PW_ERR_INVALID_ARG;
   if (!aligned(y, 16) || !aligned(blocks, 8)) return PW_ERR_ALIGNMENT;
-  if (opts && opts->path != PW_PATH_AUTO && opts->path != PW_PATH_GEMV && opts->path != PW_PATH_MFMA &&
-      opts->path != PW_PATH_MGEMV)
-    return PW_ERR_INVALID_ARG;
+  Plan pl;   // a path the forward would refuse is refused before the router runs
+  st = make_plan(shape, T, opts, pl);
+  if (st != PW_OK) return st;
   st = pw_router_topk(shape, T, x, router_w, ids, w, stat_count, stat_mass, workspace, workspace_bytes, stream);
   if (st != PW_OK) return st;
   return pw_moe_forward(shape, T, x, ids, w, blocks, q, y, workspace, workspace_bytes, opts, stream);

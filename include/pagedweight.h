@@ -164,6 +164,31 @@ pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T,
                          uint16_t* y, void* workspace, size_t workspace_bytes,
                          const pw_moe_options* opts, void* stream);
 
+/* The kernel families a pw_moe_forward call with this shape, T and options
+ * runs (the fused kernel's dispatch between its decode, moderate-batch and
+ * prefill forms, Core components 3), without touching the GPU.  Host only;
+ * the result does not depend on the routing itself. */
+typedef struct {
+  int32_t gemv;          /* 1: the bit-plane GEMV kernels run                 */
+  int32_t mgemv;         /* 1: the matrix-core GEMV kernels run               */
+  int32_t mfma;          /* 1: the dequant-to-LDS MFMA kernels run            */
+  int32_t mgemv_from;    /* experts with at least this many tokens (and below
+                            mfma_from, if MFMA runs) take the matrix-core GEMV;
+                            0 if it does not run                               */
+  int32_t mfma_from;     /* experts with at least this many tokens take MFMA;
+                            0 if it does not run                               */
+  int32_t inline_route;  /* 1: no separate routing kernel (GEMV alone, at most
+                            64 slots: the gate_up kernel routes)               */
+  int32_t down_kparts;   /* parts of the K range of the GEMV down product    */
+  int32_t launches;      /* kernels the call enqueues (T > 0)                 */
+} pw_path_info;
+
+/*   shape, opts  host, as for pw_moe_forward (opts may be NULL)
+ *   info         host, overwritten (all zero for T == 0)
+ * Errors: those pw_moe_forward reports for the shape, T and options. */
+pw_status pw_moe_path_info(const pw_moe_shape* shape, int32_t T, const pw_moe_options* opts,
+                           pw_path_info* info);
+
 /* Dequantize one block at bitwidth q (host value, 3..8): w_out fp16 bits
  * [N][K] = LUT_q[n][code_q(n, c)].  The same device decode the forward uses;
  * bit-exact by definition (a table copy).  Core components 1. */

@@ -138,3 +138,64 @@ def test_router_rejects_bad_arguments_before_launch(lib):
     assert f(ctypes.byref(shp), 4, p, p, p, p, p + 2, None, None, p, 1 << 40, None, None) == B.PW_ERR_ALIGNMENT
     assert f(ctypes.byref(shp), 4, p, p, p, p, p, None, None, p, 100, None, None) == B.PW_ERR_WORKSPACE
     assert f(ctypes.byref(shp), 0, p, p, p, p, p, None, None, p, 1 << 40, None, None) == B.PW_OK
+
+
+def _families(info):
+    return tuple(n for n in ("gemv", "mgemv", "mfma") if getattr(info, n))
+
+
+@pytest.mark.parametrize("shp,T,fams,inline,launches,kparts", [
+    # E = 8, k = 2: the mean routed slots per routed expert m = T*k / min(E, T*k) crosses 2 at T = 8 and 64 at T = 256
+    ((1024, 1024, 8, 2), 1, ("gemv",), 1, 3, None),
+    ((1024, 1024, 8, 2), 7, ("gemv",), 1, 3, None),
+    ((1024, 1024, 8, 2), 8, ("mgemv",), 0, 4, 1),
+    ((1024, 1024, 8, 2), 256, ("mgemv",), 0, 4, 1),
+    ((1024, 1024, 8, 2), 257, ("mfma",), 0, 4, 1),
+    # Qwen-shaped layer: decode, 16 tokens (64 slots, still routed inline), 17 tokens (a route kernel), batched
+    ((2048, 1408, 60, 4), 4, ("gemv",), 1, 3, 1),
+    ((2048, 1408, 60, 4), 16, ("gemv",), 1, 3, None),
+    ((2048, 1408, 60, 4), 17, ("gemv",), 0, 4, 1),
+    ((2048, 1408, 60, 4), 256, ("mgemv",), 0, 4, 1),
+    # Mixtral-shaped layer: one token splits the down product's K range over 4 waves; prefill is MFMA
+    ((4096, 14336, 8, 2), 1, ("gemv",), 1, 3, 4),
+    ((4096, 14336, 8, 2), 4096, ("mfma",), 0, 4, 1),
+])
+def test_path_info_auto_rule(lib, shp, T, fams, inline, launches, kparts):
+    info = B.pw_moe_path_info(B.shape(*shp), T)
+    assert _families(info) == fams
+    assert info.inline_route == inline and info.launches == launches
+    if kparts is not None:
+        assert info.down_kparts == kparts
+    assert info.mgemv_from == (1 if "mgemv" in fams else 0)
+    assert info.mfma_from == (1 if "mfma" in fams else 0)
+
+
+def test_path_info_forced_paths_and_bands(lib):
+    s = B.shape(2048, 1408, 60, 4)
+    i = B.pw_moe_path_info(s, 4096, B.make_options(path=B.PW_PATH_GEMV))
+    assert _families(i) == ("gemv",) and i.launches == 4 and i.down_kparts == 1
+    i = B.pw_moe_path_info(s, 1, B.make_options(path=B.PW_PATH_MFMA))
+    assert _families(i) == ("mfma",) and i.mfma_from == 1 and i.inline_route == 0
+    i = B.pw_moe_path_info(s, 1, B.make_options(path=B.PW_PATH_MGEMV))
+    assert _families(i) == ("mgemv",) and i.mgemv_from == 1
+    # explicit bands on a batch averaging 17 slots per expert: all three families, in one call
+    i = B.pw_moe_path_info(s, 256, B.make_options(mgemv_min_tokens=4, mfma_min_tokens=64))
+    assert _families(i) == ("gemv", "mgemv", "mfma") and (i.mgemv_from, i.mfma_from) == (4, 64)
+    assert i.launches == 1 + 2 * 3 + 1
+    # an MFMA band no expert can reach is not launched; below a mean of 2 the GEMV keeps every expert
+    i = B.pw_moe_path_info(s, 4, B.make_options(mfma_min_tokens=256))
+    assert _families(i) == ("gemv",) and i.inline_route == 1
+    # nothing to do
+    i = B.pw_moe_path_info(s, 0)
+    assert _families(i) == () and i.launches == 0
+
+
+def test_path_info_rejects_what_the_forward_rejects(lib):
+    s = B.shape(2048, 1408, 60, 4)
+    with pytest.raises(B.PwError):
+        B.pw_moe_path_info(s, 4, B.make_options(path=7))
+    with pytest.raises(B.PwError):
+        B.pw_moe_path_info(B.shape(2048, 1408, 60, 61), 4)          # top_k > E
+    with pytest.raises(B.PwError):                                     # 32-bit activation offsets
+        B.pw_moe_path_info(B.shape(4096, 14336, 8, 2), 40000, B.make_options(path=B.PW_PATH_MGEMV))
+    assert lib.pw_moe_path_info(ctypes.byref(s), 4, None, None) == B.PW_ERR_INVALID_ARG

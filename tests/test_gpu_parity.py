@@ -446,6 +446,8 @@ def test_auto_family_at_the_mean_edges(torch, T, family):
     and sums in its own order, so AUTO's output equals the chosen family's
     forced output bit for bit and differs from the other two."""
     L = custom_layer(1024, 1024, 8, 2, T, 700 + T)
+    info = B.pw_moe_path_info(B.shape(1024, 1024, 8, 2), T)
+    assert [n for n in ("gemv", "mgemv", "mfma") if getattr(info, n)] == [_FAMILIES[family]]
     say(f"forward AUTO family edge T={T} (expect {_FAMILIES[family]})")
     dev, y_auto = run_forward(torch, L, B.PW_PATH_AUTO)
     assert dev.status() == 0
