@@ -181,6 +181,7 @@ pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T, const uint16_t* x
   rt.num_mtiles = reinterpret_cast<int32_t*>(ws + L.num_mtiles);
   rt.mgtiles = reinterpret_cast<int32_t*>(ws + L.mgtiles);
   rt.num_mgtiles = reinterpret_cast<int32_t*>(ws + L.num_mgtiles);
+  rt.adesc = reinterpret_cast<ActiveDesc*>(ws + L.adesc);
   uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
   float* o = reinterpret_cast<float*>(ws + L.o);
 

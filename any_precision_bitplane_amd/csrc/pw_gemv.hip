@@ -51,6 +51,7 @@ struct GemvArgs {
   uint16_t* hout;           // gate_up: h [slots][I]
   float* oout;              // down: o [kparts][slots][H], rows by slot t*k + j
   int kparts;               // parts of the K range (down)
+  int desc_mode;            // down after inline routing: work descriptors, fixed split
 };
 
 // ---------------------------------------------------------------------------
@@ -282,6 +283,7 @@ __device__ __forceinline__ void build_pair_tables3(uint32_t tab_base) {
 // ---------------------------------------------------------------------------
 struct Slots {
   int e, n_e, off_e, num_active;
+  int qd;                    // down bitwidth from the work descriptor (desc_mode)
   unsigned long long mask;   // inline routing: slots routed to e (bit = slot)
   pw_block_desc d;           // page-table entry of this product's block of e
 };
@@ -325,6 +327,41 @@ __device__ __forceinline__ void publish_route(const GemvArgs& A, RouteLds& L, in
     const int pos = valid ? L.off[id] + rank : -1;
     A.rt.inv[lane] = pos;
     if (valid) A.rt.perm[pos] = lane;
+  }
+}
+
+// The down kernel's work descriptors, one per routed expert in active order.
+// Written by the grid's last wave, which seldom has an expert of its own, so
+// the page-table loads here do not lengthen a wave that does.
+__device__ __forceinline__ void publish_desc(const GemvArgs& A, const int (&c)[4], int nzr, int run) {
+  const int lane = threadIdx.x;
+  int qd[4];
+  pw_block_desc bd[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {   // every entry requested before any record is stored
+    const int ex = 4 * lane + i;
+    qd[i] = 0;
+    bd[i].planes = nullptr;
+    bd[i].lut_all = nullptr;
+    if (ex < A.E && c[i] > 0) {
+      qd[i] = A.q[2 * ex + 1];
+      bd[i] = A.blocks[2 * ex + 1];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ex = 4 * lane + i;
+    if (ex < A.E && c[i] > 0) {
+      ActiveDesc dsc;
+      dsc.e = ex;
+      dsc.n_e = c[i];
+      dsc.off_e = run;
+      dsc.q = qd[i];
+      dsc.planes = bd[i].planes;
+      dsc.lut_all = bd[i].lut_all;
+      A.rt.adesc[nzr++] = dsc;
+    }
+    run += c[i];
   }
 }
 
@@ -386,6 +423,7 @@ __device__ __forceinline__ bool find_expert_inline(const GemvArgs& A, int& a, Sl
   }
   __syncthreads();
   if (blockIdx.x == 0) publish_route(A, L, id, valid, c, nzr_base, run_base);
+  if (blockIdx.x == gridDim.x - 1) publish_desc(A, c, nzr_base, run_base);
   // Values read back from LDS are the same in every lane; saying so keeps the
   // block's buffer descriptor in scalar registers.
   sl.num_active = __builtin_amdgcn_readfirstlane(n_act);
@@ -409,6 +447,28 @@ __device__ __forceinline__ bool find_expert_routed(const GemvArgs& A, int& a, Sl
   sl.n_e = uniform(A.rt.counts[e]);
   sl.off_e = uniform(A.rt.offsets[e]);
   sl.mask = 0ull;
+  return true;
+}
+
+// Down product after inline routing: once the active count is known, one
+// load of the wave's 32-byte work descriptor gives the expert, its token
+// range and the page-table entry of its down block (instead of three dependent
+// loads: expert id, count and offset, page-table entry).
+__device__ __forceinline__ bool find_expert_desc(const GemvArgs& A, int& a, Slots& sl, int& per) {
+  const int n_act = uniform(*A.rt.num_active);
+  sl.num_active = n_act;
+  sl.mask = 0ull;
+  if (n_act <= 0) return false;
+  per = waves_per_segment<false>(A, n_act);
+  a = ((int)blockIdx.x / per) / A.kparts;
+  if (a >= n_act) return false;
+  const ActiveDesc dsc = A.rt.adesc[a];
+  sl.e = uniform(dsc.e);
+  sl.n_e = uniform(dsc.n_e);
+  sl.off_e = uniform(dsc.off_e);
+  sl.qd = uniform(dsc.q);
+  sl.d.planes = uniform_ptr(dsc.planes);
+  sl.d.lut_all = uniform_ptr(dsc.lut_all);
   return true;
 }
 
@@ -661,13 +721,18 @@ __global__ __launch_bounds__(kWave) void gemv_kernel(GemvArgs A) {
   __shared__ __align__(512) uint8_t tabs[kChunkRows * kMaxTabBytes];   // row tables at kTabStride<Q>
   __shared__ RouteLds L;
   Slots sl;
-  int a = 0;
-  const bool have = A.inline_route ? find_expert_inline(A, a, sl, L) : find_expert_routed<GU>(A, a, sl);
+  int a = 0, per = 1;
+  bool have;
+  if (!GU && A.desc_mode) {
+    have = find_expert_desc(A, a, sl, per);
+  } else {
+    have = A.inline_route ? find_expert_inline(A, a, sl, L) : find_expert_routed<GU>(A, a, sl);
+    if (have) per = waves_per_segment<GU>(A, sl.num_active);
+  }
   if (!have) return;
   if (sl.n_e < A.min_tokens || sl.n_e >= A.max_tokens) return;
 
   const int rows = GU ? A.I : A.H;
-  const int per = waves_per_segment<GU>(A, sl.num_active);
   const int seg = (int)blockIdx.x / per;
   const int c = (int)blockIdx.x - seg * per;
   Chunk ch;
@@ -676,8 +741,13 @@ __global__ __launch_bounds__(kWave) void gemv_kernel(GemvArgs A) {
   ch.n = (int)(((long long)(c + 1) * rows) / per) - ch.first;
   if (ch.n <= 0) return;
   // bitwidth and page-table entry of the block, requested together
-  const int qv = uniform(A.q[2 * sl.e + (GU ? 0 : 1)]);
-  sl.d = A.blocks[2 * sl.e + (GU ? 0 : 1)];
+  int qv;
+  if (!GU && A.desc_mode) {
+    qv = sl.qd;   // the work descriptor carried the entry
+  } else {
+    qv = uniform(A.q[2 * sl.e + (GU ? 0 : 1)]);
+    sl.d = A.blocks[2 * sl.e + (GU ? 0 : 1)];
+  }
   switch (qv) {
     case 3: chunk_by_tokens<3, GU>(A, sl, ch, tabs); break;
     case 4: chunk_by_tokens<4, GU>(A, sl, ch, tabs); break;
@@ -744,6 +814,7 @@ hipError_t launch_gemv_down(const GemvLaunch& g, hipStream_t s) {
   A.inline_route = 0;    // the gate_up kernel or the route kernel published the routing
   A.act = g.h; A.hout = nullptr; A.oout = g.o;
   A.kparts = g.kparts;
+  A.desc_mode = g.inline_route;   // the gate_up kernel published the work descriptors
   hipLaunchKernelGGL(gemv_kernel<false>, dim3(gemv_grid<false>(A)), dim3(kWave), 0, s, A);
   return hipGetLastError();
 }

@@ -63,6 +63,7 @@ struct WsLayout {
   size_t rlogits = 0;       // fp32  [T][E]   router logits
   size_t rids = 0;          // int32 [T*k]    router expert ids (routed forward)
   size_t rw = 0;            // fp32  [T*k]    router weights (routed forward)
+  size_t adesc = 0;         // ActiveDesc [E] down-product work descriptors (calls routed inside gate_up)
   size_t total = 0;
 };
 
@@ -83,11 +84,22 @@ inline WsLayout ws_layout(int H, int I, int E, int k, int T) {
   L.rlogits = off; off = align_up(off + sizeof(float) * (size_t)T * E, kAlign);
   L.rids = off;    off = align_up(off + sizeof(int32_t) * slots, kAlign);
   L.rw = off;      off = align_up(off + sizeof(float) * slots, kAlign);
+  L.adesc = off;   off = align_up(off + 32 * (size_t)E, kAlign);
   L.total = off;
   return L;
 }
 
 // Pointers into one workspace for one call.
+// What a down-product wave needs about the a-th routed expert, in one
+// 32-byte record: written by the gate_up kernel that routes a small batch, so
+// the down kernel reaches its planes after one dependent load.
+struct ActiveDesc {
+  int32_t e, n_e, off_e, q;
+  const uint32_t* planes;
+  const uint16_t* lut_all;
+};
+static_assert(sizeof(ActiveDesc) == 32, "one record per 32 bytes");
+
 struct Route {
   uint32_t* status;
   int32_t* num_active;
@@ -100,6 +112,7 @@ struct Route {
   int32_t* num_mtiles;
   int32_t* mgtiles;       // (expert, first token) per matrix-core GEMV token tile
   int32_t* num_mgtiles;
+  ActiveDesc* adesc;      // [E] down work descriptors by active index (inline routing only)
 };
 
 
