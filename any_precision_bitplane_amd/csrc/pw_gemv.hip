@@ -28,8 +28,9 @@
 //
 // Batches of at most 64 routed slots skip the separate route step: every
 // gate_up wave finds its expert and token slots with ballots over the slot
-// ids, and the first wave publishes the routing (counts, offsets, active list,
-// slot order) for the down and combine kernels that follow on the stream.
+// ids, the first wave publishes the routing (counts, offsets, active list,
+// slot order) for the down and combine kernels that follow on the stream, and
+// the last wave one work descriptor per routed expert for the down kernel.
 #include "pw_device.h"
 #include "pw_internal.h"
 
