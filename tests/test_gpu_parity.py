@@ -288,6 +288,38 @@ def test_invalid_ids_and_bitwidths_flagged_and_zero(torch):
     compare(dev2.y.float().cpu().numpy(), oracle_y(L, q=q), "invalid bitwidth block")
 
 
+def test_gemv_small_call_invalid_down_bitwidth_and_dropped_slots(torch):
+    """Small calls on the GEMV kernels route inside gate_up, and the down kernel
+    takes each routed expert's bitwidth and storage from a work descriptor:
+    an invalid down bitwidth there still reads as zero rows and is flagged,
+    dropped slots add nothing, and the next call on the same workspace is exact."""
+    from any_precision_bitplane_amd.device import DeviceLayer
+    L = layer_for("tiny")
+    opts = B.make_options(path=B.PW_PATH_GEMV)
+    info = B.pw_moe_path_info(B.shape(L.wl.H, L.wl.I, L.wl.E, L.wl.k), L.wl.T, opts)
+    assert info.gemv == 1 and info.inline_route == 1
+    ids = L.ids.copy()
+    ids[1, 0] = -3
+    q = L.q.copy()
+    q[int(L.ids[6, 1]), 1] = 2
+    say("GEMV inline call: invalid down bitwidth and a dropped slot")
+    dev = DeviceLayer(L)
+    dev.ids.copy_(torch.from_numpy(ids))
+    dev.set_q(q)
+    dev.forward(opts)
+    torch.cuda.synchronize()
+    st = dev.status()
+    assert st & B.PW_DEV_BAD_BITWIDTH and st & B.PW_DEV_BAD_EXPERT_ID
+    compare(dev.y.float().cpu().numpy(), oracle_y(L, ids=ids, q=q), "gemv inline, bad down q + dropped slot")
+    say("GEMV inline call: the valid layer on the same workspace")
+    dev.ids.copy_(torch.from_numpy(L.ids))
+    dev.set_q(L.q)
+    dev.forward(opts)
+    torch.cuda.synchronize()
+    assert dev.status() == 0
+    compare(dev.y.float().cpu().numpy(), oracle_y(L), "gemv inline, valid after invalid")
+
+
 def test_duplicate_ids_are_summed(torch):
     from any_precision_bitplane_amd.device import DeviceLayer
     L = layer_for("tiny")
