@@ -46,6 +46,9 @@ PW_STAGE_DOWN = 2
 PW_STAGE_COMBINE = 3
 PW_NUM_STAGES = 4
 
+PW_EVENTS_STAGES = 0
+PW_EVENTS_KERNELS = 1
+
 
 class PwMoeShape(ctypes.Structure):
     _fields_ = [("hidden", c_int32), ("inter", c_int32), ("num_experts", c_int32), ("top_k", c_int32)]
@@ -58,7 +61,7 @@ class PwBlockDesc(ctypes.Structure):
 class PwMoeOptions(ctypes.Structure):
     _fields_ = [("path", c_int32), ("mfma_min_tokens", c_int32),
                 ("stage_events", c_void_p * (PW_NUM_STAGES + 1)),
-                ("mgemv_min_tokens", c_int32), ("reserved", c_int32)]
+                ("mgemv_min_tokens", c_int32), ("event_mode", c_int32)]
 
 
 class PwPageInfo(ctypes.Structure):
@@ -136,7 +139,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
 
 def exported_symbols() -> Sequence[str]:
     return ["pw_abi_version", "pw_status_str", "pw_plane_words", "pw_lut_elems", "pw_lut_offset",
-            "pw_check_shape", "pw_workspace_bytes", "pw_workspace_init", "pw_moe_forward", "pw_moe_path_info",
+            "pw_check_shape", "pw_workspace_bytes", "pw_workspace_init", "pw_moe_forward",
+            "pw_moe_path_info",
             "pw_dequant_block", "pw_get_device_status", "pw_pager_create", "pw_pager_destroy",
             "pw_pager_set_block", "pw_pager_request", "pw_pager_execute", "pw_pager_commit", "pw_pager_info",
             "pw_pager_arena_used", "pw_router_topk", "pw_moe_forward_routed", "pw_plan_bitwidths"]
@@ -203,11 +207,12 @@ def pw_workspace_init(workspace, stream=None) -> None:
 
 
 def make_options(path: int = PW_PATH_AUTO, mfma_min_tokens: int = 0, events=None,
-                 mgemv_min_tokens: int = 0) -> PwMoeOptions:
+                 mgemv_min_tokens: int = 0, event_mode: int = 0) -> PwMoeOptions:
     o = PwMoeOptions()
     o.path = path
     o.mfma_min_tokens = mfma_min_tokens
     o.mgemv_min_tokens = mgemv_min_tokens
+    o.event_mode = event_mode
     if events is not None:
         for i, ev in enumerate(events):
             o.stage_events[i] = ev

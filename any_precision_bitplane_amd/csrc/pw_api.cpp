@@ -100,6 +100,116 @@ pw_status make_plan(const pw_moe_shape* shape, int32_t T, const pw_moe_options* 
 
 }  // namespace
 
+namespace pw {
+
+pw_status check_forward_args(const pw_moe_shape* shape, int32_t T, const uint16_t* x, const int32_t* ids,
+                             const float* w, const pw_block_desc* blocks, const uint8_t* q, uint16_t* y,
+                             const pw_moe_options* opts) {
+  pw_status st = check_shape(shape, T);
+  if (st != PW_OK) return st;
+  if (T == 0) return PW_OK;
+  if (!x || !ids || !w || !blocks || !q || !y) return PW_ERR_INVALID_ARG;
+  const int path = opts ? opts->path : PW_PATH_AUTO;
+  if (path != PW_PATH_AUTO && path != PW_PATH_GEMV && path != PW_PATH_MFMA && path != PW_PATH_MGEMV)
+    return PW_ERR_INVALID_ARG;
+  if (opts && opts->event_mode != PW_EVENTS_STAGES && opts->event_mode != PW_EVENTS_KERNELS)
+    return PW_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ids, 4) || !aligned(w, 4) || !aligned(blocks, 8))
+    return PW_ERR_ALIGNMENT;
+  Plan pl;
+  return make_plan(shape, T, opts, pl);
+}
+
+pw_status forward_on(const pw_moe_shape* shape, int32_t T, const uint16_t* x, const int32_t* ids, const float* w,
+                     const pw_block_desc* blocks, const uint8_t* q, uint16_t* y, uint8_t* ws, uint32_t* status,
+                     const pw_moe_options* opts, hipStream_t s) {
+  const int H = shape->hidden, I = shape->inter, E = shape->num_experts, k = shape->top_k;
+  const WsLayout L = ws_layout(H, I, E, k, T);
+  Plan pl;
+  pw_status st = make_plan(shape, T, opts, pl);
+  if (st != PW_OK) return st;
+  const bool use_gemv = pl.gemv, use_mg = pl.mgemv, use_mfma = pl.mfma;
+  const int b1 = pl.b1, b2 = pl.b2, thresh = pl.b2;
+
+  Route rt;
+  rt.status = status ? status : reinterpret_cast<uint32_t*>(ws + L.status);
+  rt.num_active = reinterpret_cast<int32_t*>(ws + L.num_active);
+  rt.counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  rt.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  rt.active = reinterpret_cast<int32_t*>(ws + L.active);
+  rt.perm = reinterpret_cast<int32_t*>(ws + L.perm);
+  rt.inv = reinterpret_cast<int32_t*>(ws + L.inv);
+  rt.mtiles = reinterpret_cast<int32_t*>(ws + L.mtiles);
+  rt.num_mtiles = reinterpret_cast<int32_t*>(ws + L.num_mtiles);
+  rt.mgtiles = reinterpret_cast<int32_t*>(ws + L.mgtiles);
+  rt.num_mgtiles = reinterpret_cast<int32_t*>(ws + L.num_mgtiles);
+  rt.adesc = reinterpret_cast<ActiveDesc*>(ws + L.adesc);
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
+  float* o = reinterpret_cast<float*>(ws + L.o);
+
+  const bool inline_route = pl.inline_route;
+  ExpertArgs mfma{H, I, E, k, T, blocks, q, rt, thresh == 0 ? 1 : thresh, INT_MAX};
+  ExpertArgs mg{H, I, E, k, T, blocks, q, rt, b1 == 0 ? 1 : b1, b2};
+  GemvLaunch g{};
+  g.H = H; g.I = I; g.E = E; g.k = k; g.T = T;
+  g.blocks = blocks; g.q = q; g.ids = ids; g.rt = rt;
+  g.inline_route = inline_route ? 1 : 0;
+  g.min_tokens = 0;
+  g.max_tokens = b1;
+  g.x = x; g.h = h; g.o = o;
+  // the other families write one K part of o; the GEMV splits K only when it runs alone
+  g.kparts = pl.kparts;
+
+  // Events: at stage boundaries on the stream, or carried by the product
+  // kernels themselves (start on the first kernel of a product, stop on its last).
+  void* const* ev = (opts && opts->stage_events[0]) ? opts->stage_events : nullptr;
+  const bool kernel_ev = ev && opts->event_mode == PW_EVENTS_KERNELS;
+  auto mark = [&](int i) -> hipError_t {
+    return (ev && !kernel_ev) ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess;
+  };
+  // kernel events of one product: `first`/`last` say whether this launch opens / closes the product
+  auto kev = [&](int product, bool first, bool last) {
+    KernelEvents r;
+    if (kernel_ev) {
+      if (first) r.start = (hipEvent_t)ev[2 * product];
+      if (last) r.stop = (hipEvent_t)ev[2 * product + 1];
+    }
+    return r;
+  };
+  const int nfam = (int)use_gemv + (int)use_mg + (int)use_mfma;
+
+  hipError_t e = mark(PW_STAGE_ROUTE);
+  if (e == hipSuccess && !inline_route)
+    e = launch_route(ids, T, k, E, use_mfma ? (thresh == 0 ? 1 : thresh) : INT_MAX, use_mg ? (b1 == 0 ? 1 : b1) : INT_MAX,
+                     use_mg ? b2 : INT_MAX, rt, s);
+  for (int product = 0; product < 2 && e == hipSuccess; ++product) {
+    e = mark(product == 0 ? PW_STAGE_GATE_UP : PW_STAGE_DOWN);
+    int done = 0;
+    if (e == hipSuccess && use_gemv) {
+      const KernelEvents kv = kev(product, done == 0, done + 1 == nfam);
+      e = product == 0 ? launch_gemv_gate_up(g, s, kv) : launch_gemv_down(g, s, kv);
+      ++done;
+    }
+    if (e == hipSuccess && use_mg) {
+      const KernelEvents kv = kev(product, done == 0, done + 1 == nfam);
+      e = product == 0 ? launch_mgemv_gate_up(mg, x, h, s, kv) : launch_mgemv_down(mg, h, o, s, kv);
+      ++done;
+    }
+    if (e == hipSuccess && use_mfma) {
+      const KernelEvents kv = kev(product, done == 0, done + 1 == nfam);
+      e = product == 0 ? launch_mfma_gate_up(mfma, x, h, s, kv) : launch_mfma_down(mfma, h, o, s, kv);
+      ++done;
+    }
+  }
+  if (e == hipSuccess) e = mark(PW_STAGE_COMBINE);
+  if (e == hipSuccess) e = launch_combine(o, w, rt.inv, T, k, H, g.kparts, y, s);
+  if (e == hipSuccess) e = mark(PW_NUM_STAGES);
+  if (e == hipErrorNotSupported) return PW_ERR_UNSUPPORTED;
+  return hip_status(e);
+}
+
+}  // namespace pw
+
 extern "C" {
 
 int32_t pw_abi_version(void) { return PW_ABI_VERSION; }
@@ -147,80 +257,14 @@ pw_status pw_workspace_init(void* workspace, size_t workspace_bytes, void* strea
 pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T, const uint16_t* x, const int32_t* ids,
                          const float* w, const pw_block_desc* blocks, const uint8_t* q, uint16_t* y,
                          void* workspace, size_t workspace_bytes, const pw_moe_options* opts, void* stream) {
-  pw_status st = check_shape(shape, T);
-  if (st != PW_OK) return st;
-  if (T == 0) return PW_OK;
-  if (!x || !ids || !w || !blocks || !q || !y || !workspace) return PW_ERR_INVALID_ARG;
-  const int path = opts ? opts->path : PW_PATH_AUTO;
-  if (path != PW_PATH_AUTO && path != PW_PATH_GEMV && path != PW_PATH_MFMA && path != PW_PATH_MGEMV)
-    return PW_ERR_INVALID_ARG;
-  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ids, 4) || !aligned(w, 4) || !aligned(blocks, 8) ||
-      !aligned(workspace, kAlign))
-    return PW_ERR_ALIGNMENT;
-
-  const int H = shape->hidden, I = shape->inter, E = shape->num_experts, k = shape->top_k;
-  const WsLayout L = ws_layout(H, I, E, k, T);
+  pw_status st = check_forward_args(shape, T, x, ids, w, blocks, q, y, opts);
+  if (st != PW_OK || T == 0) return st;
+  if (!workspace) return PW_ERR_INVALID_ARG;
+  if (!aligned(workspace, kAlign)) return PW_ERR_ALIGNMENT;
+  const WsLayout L = ws_layout(shape->hidden, shape->inter, shape->num_experts, shape->top_k, T);
   if (workspace_bytes < L.total) return PW_ERR_WORKSPACE;
-
-  Plan pl;
-  st = make_plan(shape, T, opts, pl);
-  if (st != PW_OK) return st;
-  const bool use_gemv = pl.gemv, use_mg = pl.mgemv, use_mfma = pl.mfma;
-  const int b1 = pl.b1, b2 = pl.b2, thresh = pl.b2;
-
-  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
-  Route rt;
-  rt.status = reinterpret_cast<uint32_t*>(ws + L.status);
-  rt.num_active = reinterpret_cast<int32_t*>(ws + L.num_active);
-  rt.counts = reinterpret_cast<int32_t*>(ws + L.counts);
-  rt.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
-  rt.active = reinterpret_cast<int32_t*>(ws + L.active);
-  rt.perm = reinterpret_cast<int32_t*>(ws + L.perm);
-  rt.inv = reinterpret_cast<int32_t*>(ws + L.inv);
-  rt.mtiles = reinterpret_cast<int32_t*>(ws + L.mtiles);
-  rt.num_mtiles = reinterpret_cast<int32_t*>(ws + L.num_mtiles);
-  rt.mgtiles = reinterpret_cast<int32_t*>(ws + L.mgtiles);
-  rt.num_mgtiles = reinterpret_cast<int32_t*>(ws + L.num_mgtiles);
-  rt.adesc = reinterpret_cast<ActiveDesc*>(ws + L.adesc);
-  uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
-  float* o = reinterpret_cast<float*>(ws + L.o);
-
-  const bool inline_route = pl.inline_route;
-  ExpertArgs mfma{H, I, E, k, T, blocks, q, rt, thresh == 0 ? 1 : thresh, INT_MAX};
-  ExpertArgs mg{H, I, E, k, T, blocks, q, rt, b1 == 0 ? 1 : b1, b2};
-  GemvLaunch g{};
-  g.H = H; g.I = I; g.E = E; g.k = k; g.T = T;
-  g.blocks = blocks; g.q = q; g.ids = ids; g.rt = rt;
-  g.inline_route = inline_route ? 1 : 0;
-  g.min_tokens = 0;
-  g.max_tokens = b1;
-  g.x = x; g.h = h; g.o = o;
-  // the other families write one K part of o; the GEMV splits K only when it runs alone
-  g.kparts = pl.kparts;
-
-  hipStream_t s = (hipStream_t)stream;
-  void* const* ev = (opts && opts->stage_events[0]) ? opts->stage_events : nullptr;
-  auto mark = [&](int i) -> hipError_t {
-    return ev ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess;
-  };
-
-  hipError_t e = mark(PW_STAGE_ROUTE);
-  if (e == hipSuccess && !inline_route)
-    e = launch_route(ids, T, k, E, use_mfma ? (thresh == 0 ? 1 : thresh) : INT_MAX, use_mg ? (b1 == 0 ? 1 : b1) : INT_MAX,
-                     use_mg ? b2 : INT_MAX, rt, s);
-  if (e == hipSuccess) e = mark(PW_STAGE_GATE_UP);
-  if (e == hipSuccess && use_gemv) e = launch_gemv_gate_up(g, s);
-  if (e == hipSuccess && use_mg) e = launch_mgemv_gate_up(mg, x, h, s);
-  if (e == hipSuccess && use_mfma) e = launch_mfma_gate_up(mfma, x, h, s);
-  if (e == hipSuccess) e = mark(PW_STAGE_DOWN);
-  if (e == hipSuccess && use_gemv) e = launch_gemv_down(g, s);
-  if (e == hipSuccess && use_mg) e = launch_mgemv_down(mg, h, o, s);
-  if (e == hipSuccess && use_mfma) e = launch_mfma_down(mfma, h, o, s);
-  if (e == hipSuccess) e = mark(PW_STAGE_COMBINE);
-  if (e == hipSuccess) e = launch_combine(o, w, rt.inv, T, k, H, g.kparts, y, s);
-  if (e == hipSuccess) e = mark(PW_NUM_STAGES);
-  if (e == hipErrorNotSupported) return PW_ERR_UNSUPPORTED;
-  return hip_status(e);
+  return forward_on(shape, T, x, ids, w, blocks, q, y, reinterpret_cast<uint8_t*>(workspace), nullptr, opts,
+                    (hipStream_t)stream);
 }
 
 pw_status pw_router_topk(const pw_moe_shape* shape, int32_t T, const uint16_t* x, const uint16_t* router_w,

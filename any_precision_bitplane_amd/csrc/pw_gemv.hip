@@ -801,23 +801,21 @@ static int gemv_grid(const GemvArgs& A) {
   return (int)g;
 }
 
-hipError_t launch_gemv_gate_up(const GemvLaunch& g, hipStream_t s) {
+hipError_t launch_gemv_gate_up(const GemvLaunch& g, hipStream_t s, const KernelEvents& ev) {
   GemvArgs A = make_args(g);
   A.inline_route = g.inline_route;
   A.act = g.x; A.hout = g.h; A.oout = nullptr;
   A.kparts = 1;
-  hipLaunchKernelGGL(gemv_kernel<true>, dim3(gemv_grid<true>(A)), dim3(kWave), 0, s, A);
-  return hipGetLastError();
+  return launch_kernel(gemv_kernel<true>, dim3(gemv_grid<true>(A)), dim3(kWave), s, ev, A);
 }
 
-hipError_t launch_gemv_down(const GemvLaunch& g, hipStream_t s) {
+hipError_t launch_gemv_down(const GemvLaunch& g, hipStream_t s, const KernelEvents& ev) {
   GemvArgs A = make_args(g);
   A.inline_route = 0;    // the gate_up kernel or the route kernel published the routing
   A.act = g.h; A.hout = nullptr; A.oout = g.o;
   A.kparts = g.kparts;
   A.desc_mode = g.inline_route;   // the gate_up kernel published the work descriptors
-  hipLaunchKernelGGL(gemv_kernel<false>, dim3(gemv_grid<false>(A)), dim3(kWave), 0, s, A);
-  return hipGetLastError();
+  return launch_kernel(gemv_kernel<false>, dim3(gemv_grid<false>(A)), dim3(kWave), s, ev, A);
 }
 
 }  // namespace pw

@@ -1,6 +1,7 @@
 // Internal interfaces between the C-ABI host layer and the kernel files.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -140,15 +141,36 @@ struct GemvLaunch {
   int kparts;
 };
 
+// Optional start / stop events of one kernel: the library hands them to the
+// launch itself, so they carry the timestamps of that kernel's execution
+// rather than of the stream around it.  Null members are not recorded.
+struct KernelEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+template <typename F, typename... Args>
+inline hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, hipStream_t s, const KernelEvents& ev,
+                                Args... args) {
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  return hipGetLastError();
+}
+
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_route(const int32_t* ids, int T, int k, int E, int mfma_min_tokens, int mg_min_tokens,
                         int mg_max_tokens, const Route& rt, hipStream_t s);
-hipError_t launch_gemv_gate_up(const GemvLaunch& g, hipStream_t s);
-hipError_t launch_gemv_down(const GemvLaunch& g, hipStream_t s);
-hipError_t launch_mfma_gate_up(const ExpertArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s);
-hipError_t launch_mfma_down(const ExpertArgs& a, const uint16_t* h, float* o, hipStream_t s);
-hipError_t launch_mgemv_gate_up(const ExpertArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s);
-hipError_t launch_mgemv_down(const ExpertArgs& a, const uint16_t* h, float* o, hipStream_t s);
+hipError_t launch_gemv_gate_up(const GemvLaunch& g, hipStream_t s, const KernelEvents& ev);
+hipError_t launch_gemv_down(const GemvLaunch& g, hipStream_t s, const KernelEvents& ev);
+hipError_t launch_mfma_gate_up(const ExpertArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s,
+                               const KernelEvents& ev);
+hipError_t launch_mfma_down(const ExpertArgs& a, const uint16_t* h, float* o, hipStream_t s, const KernelEvents& ev);
+hipError_t launch_mgemv_gate_up(const ExpertArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s,
+                                const KernelEvents& ev);
+hipError_t launch_mgemv_down(const ExpertArgs& a, const uint16_t* h, float* o, hipStream_t s,
+                             const KernelEvents& ev);
 hipError_t launch_combine(const float* o, const float* w, const int32_t* inv, int T, int k, int H, int kparts,
                           uint16_t* y, hipStream_t s);
 hipError_t launch_dequant(const uint32_t* planes, const uint16_t* lut_all, int N, int K, int q,
@@ -157,5 +179,18 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, int T, int H, int E, int k, float* logits,
                          int32_t* ids, float* w, uint32_t* count, float* mass, hipStream_t s);
 hipError_t launch_status_clear(uint32_t* status, hipStream_t s);
+
+// The fused layer on a caller-provided scratch area (the workspace, or the
+// allocation-free entry point's static array).  `status`, if non-null,
+// replaces the status word of the scratch header as the place device errors
+// are raised.  Arguments are checked by the caller.
+pw_status forward_on(const pw_moe_shape* shape, int32_t T, const uint16_t* x, const int32_t* ids, const float* w,
+                     const pw_block_desc* blocks, const uint8_t* q, uint16_t* y, uint8_t* scratch,
+                     uint32_t* status, const pw_moe_options* opts, hipStream_t s);
+
+// Host checks shared by the forward entry points (everything but the scratch).
+pw_status check_forward_args(const pw_moe_shape* shape, int32_t T, const uint16_t* x, const int32_t* ids,
+                             const float* w, const pw_block_desc* blocks, const uint8_t* q, uint16_t* y,
+                             const pw_moe_options* opts);
 
 }  // namespace pw

@@ -530,7 +530,8 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_kernel(MfmaArgs A) {
 }
 
 template <bool GU>
-static hipError_t launch_mfma(const ExpertArgs& a, const uint16_t* act, uint16_t* h, float* o, hipStream_t s) {
+static hipError_t launch_mfma(const ExpertArgs& a, const uint16_t* act, uint16_t* h, float* o, hipStream_t s,
+                              const KernelEvents& ev) {
   MfmaArgs A{};
   A.H = a.H; A.I = a.I; A.E = a.E; A.k = a.k; A.T = a.T;
   A.blocks = a.blocks; A.q = a.q; A.rt = a.rt;
@@ -543,16 +544,16 @@ static hipError_t launch_mfma(const ExpertArgs& a, const uint16_t* act, uint16_t
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   A.grid = (int)grid;
-  hipLaunchKernelGGL(mfma_kernel<GU>, dim3((unsigned)grid), dim3(kMfmaThreads), 0, s, A);
-  return hipGetLastError();
+  return launch_kernel(mfma_kernel<GU>, dim3((unsigned)grid), dim3(kMfmaThreads), s, ev, A);
 }
 
-hipError_t launch_mfma_gate_up(const ExpertArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s) {
-  return launch_mfma<true>(a, x, h, nullptr, s);
+hipError_t launch_mfma_gate_up(const ExpertArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s,
+                               const KernelEvents& ev) {
+  return launch_mfma<true>(a, x, h, nullptr, s, ev);
 }
 
-hipError_t launch_mfma_down(const ExpertArgs& a, const uint16_t* h, float* o, hipStream_t s) {
-  return launch_mfma<false>(a, h, nullptr, o, s);
+hipError_t launch_mfma_down(const ExpertArgs& a, const uint16_t* h, float* o, hipStream_t s, const KernelEvents& ev) {
+  return launch_mfma<false>(a, h, nullptr, o, s, ev);
 }
 
 }  // namespace pw

@@ -284,7 +284,8 @@ __global__ __launch_bounds__(kWave) void mgemv_kernel(MgArgs A) {
 }
 
 template <bool GU>
-static hipError_t launch_mg(const ExpertArgs& a, const uint16_t* act, uint16_t* h, float* o, hipStream_t s) {
+static hipError_t launch_mg(const ExpertArgs& a, const uint16_t* act, uint16_t* h, float* o, hipStream_t s,
+                            const KernelEvents& ev) {
   MgArgs A{};
   A.H = a.H; A.I = a.I; A.E = a.E; A.k = a.k; A.T = a.T;
   A.blocks = a.blocks; A.q = a.q; A.rt = a.rt;
@@ -295,18 +296,22 @@ static hipError_t launch_mg(const ExpertArgs& a, const uint16_t* act, uint16_t* 
   A.act_bytes = (uint32_t)act_bytes;
   long long grid = (long long)mgtile_bound(a.E, a.T, a.k) * A.chunks;
   if (grid > 0x7FFFFFFFLL - kMgMaxGrid) return hipErrorInvalidValue;   // the kernel counts items in int
-  if (grid == 0 || a.min_tokens >= a.max_tokens) return hipSuccess;
+  const bool timed = ev.start || ev.stop;
+  if ((grid == 0 || a.min_tokens >= a.max_tokens) && !timed) return hipSuccess;
+  // with events attached an empty band still launches (one workgroup, no items)
+  if (grid == 0) grid = 1;
   if (grid > kMgMaxGrid) grid = kMgMaxGrid;
-  hipLaunchKernelGGL(mgemv_kernel<GU>, dim3((unsigned)grid), dim3(kWave), 0, s, A);
-  return hipGetLastError();
+  return launch_kernel(mgemv_kernel<GU>, dim3((unsigned)grid), dim3(kWave), s, ev, A);
 }
 
-hipError_t launch_mgemv_gate_up(const ExpertArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s) {
-  return launch_mg<true>(a, x, h, nullptr, s);
+hipError_t launch_mgemv_gate_up(const ExpertArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s,
+                                const KernelEvents& ev) {
+  return launch_mg<true>(a, x, h, nullptr, s, ev);
 }
 
-hipError_t launch_mgemv_down(const ExpertArgs& a, const uint16_t* h, float* o, hipStream_t s) {
-  return launch_mg<false>(a, h, nullptr, o, s);
+hipError_t launch_mgemv_down(const ExpertArgs& a, const uint16_t* h, float* o, hipStream_t s,
+                             const KernelEvents& ev) {
+  return launch_mg<false>(a, h, nullptr, o, s, ev);
 }
 
 }  // namespace pw

@@ -74,6 +74,22 @@ class DeviceLayer:
                 desc[e, m, 1] = self.luts[c][e][m].data_ptr()
         return _to_dev(desc.view(np.int64), self.device)
 
+    def set_tokens(self, layer) -> None:
+        """Point the layer at another batch (x, ids, w of ``layer``, which must
+        share this layer's shape and storage); the expert storage stays."""
+        import torch
+        wl = layer.wl
+        assert (wl.H, wl.I, wl.E, wl.k) == (self.wl.H, self.wl.I, self.wl.E, self.wl.k)
+        self.wl = wl
+        self.T = wl.T
+        self.x = torch.from_numpy(layer.x).to(self.device)
+        self.ids = _to_dev(layer.ids, self.device)
+        self.w = _to_dev(layer.w, self.device)
+        self.y = torch.empty((wl.T, wl.H), dtype=torch.float16, device=self.device)
+        self.ws_bytes = binding.pw_workspace_bytes(self.shape, wl.T)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        binding.pw_workspace_init(self.ws)
+
     def set_q(self, q: np.ndarray):
         """Commit new bitwidths: a stream-ordered write of the q table."""
         self.q.copy_(_to_dev(np.asarray(q, dtype=np.uint8), self.device))

@@ -1,21 +1,28 @@
 #!/usr/bin/env python3
 """Benchmark of the fused mixed-precision MoE expert layer on one MI355X.
 
-One step = one pw_moe_forward call (route, gate_up + SwiGLU, down, combine)
-over the Qwen1.5-MoE-A2.7B-shaped decode layer: H=2048, I=1408, E=60 routed
-experts, top-4, T=4 tokens, per-block committed bitwidths uniform in 3..8,
-seeded synthetic weights and activations.  Inputs are resident in HBM before
-the timed region.  The expert storage of the routed experts is kept in R
-copies at different addresses and the steps rotate through them, so weights
-come from HBM and not from the 256 MB last-level cache.
+One step = one pw_moe_forward call (route, gate_up + SwiGLU, down, combine) on
+seeded synthetic inputs resident in HBM.  The reported line is the
+Mixtral-8x7B-shaped decode layer at T = 64 tokens (H=4096, I=14336, E=8,
+top-2, per-block committed bitwidths uniform in 3..8: the largest layer with
+mixed 3-8-bit experts); every other layer shape of the study -- tiny, the
+Qwen1.5-MoE-A2.7B-shaped decode (T=4) and batched (T=256, Zipf) layers,
+Mixtral decode at T = 1 and 8, Mixtral prefill (T=4096) -- gets its own timed
+region under `per_config`.  The routed experts' storage is kept in R copies at
+different addresses (R x the bytes a call reads >= 1 GB) and the steps rotate
+through them, so weights come from HBM and not from the 256 MB last-level cache.
 
-Prints one JSON line.  Optional --workload picks another shape for local
-studies; the default is the reported configuration.
+Roofline of each call's dominant kernel: its algorithmic bytes (or flops) per
+launch over its average duration, taken from start / stop events that the
+library hands to the kernel launch itself (the kernel's own execution).
+
+Prints one JSON line.  --only NAME runs one configuration (for profiling).
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +35,23 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (% peak) at mixed 3–8-bit experts"
 
+# (name, workload, T) of every configuration; the first field names the
+# profile summaries under profiles/ as well.
+CONFIGS = [
+    ("tiny", "tiny", None),
+    ("qwen_decode", "qwen_decode", None),
+    ("qwen_batched", "qwen_batched", None),
+    ("mixtral_decode_T1", "mixtral_decode", 1),
+    ("mixtral_decode_T8", "mixtral_decode", 8),
+    ("mixtral_decode_T64", "mixtral_decode", 64),
+    ("mixtral_prefill", "mixtral_prefill", None),
+]
+HEADLINE = "mixtral_decode_T64"
+
+KERNEL_NAMES = {("gemv", 0): "gemv_kernel<true>", ("gemv", 1): "gemv_kernel<false>",
+                ("mgemv", 0): "mgemv_kernel<true>", ("mgemv", 1): "mgemv_kernel<false>",
+                ("mfma", 0): "mfma_kernel<true>", ("mfma", 1): "mfma_kernel<false>"}
+
 
 class HipEvents:
     """Raw hipEvent_t handles (the library records them on its own stream)."""
@@ -38,14 +62,17 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self):
         ev = ctypes.c_void_p()
         assert self.hip.hipEventCreate(ctypes.byref(ev)) == 0
         return ev.value
 
+    def destroy(self, ev) -> None:
+        self.hip.hipEventDestroy(ctypes.c_void_p(ev))
+
     def record(self, ev, stream) -> None:
-        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         assert self.hip.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream)) == 0
 
     def elapsed_ms(self, a, b) -> float:
@@ -55,51 +82,79 @@ class HipEvents:
         return float(out.value)
 
 
-def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary for this workload, if that summary was taken on the current kernel
-    source (its recorded source hash matches); otherwise None."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", f"traffic_gemv_{workload}.txt")
+def source_hash() -> str:
+    """sha256[:16] over the library's kernel and host sources (a profile summary
+    taken on other sources no longer describes these kernels)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "any_precision_bitplane_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def profile_fields(name: str, kind: str, kernel: str):
+    """Fields of `kernel` in profiles/<kind>_<name>.txt if that summary was taken
+    on the current sources, else None.  kind: "kernels" (rocprofv3 kernel-trace
+    stats: avg_ns) or "traffic" (FETCH_SIZE / WRITE_SIZE: traffic_bytes_per_launch)."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_{name}.txt")
     if not os.path.exists(path):
         return None
-    h = hashlib.sha256()
-    for f in ("any_precision_bitplane_amd/csrc/pw_gemv.hip", "any_precision_bitplane_amd/csrc/pw_device.h"):
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    fields = {}
+    fields, sha = {}, None
     for line in open(path):
         if line.startswith("source_sha256_16:"):
-            fields["sha"] = line.split(":", 1)[1].strip()
+            sha = line.split(":", 1)[1].strip()
         elif line.startswith(kernel + ":"):
             for tok in line.split()[1:]:
                 k, v = tok.split("=")
                 fields[k] = float(v)
-    if fields.get("sha") != h.hexdigest()[:16] or "traffic_bytes_per_launch" not in fields:
+    if sha != source_hash() or not fields:
         return None
-    return fields["traffic_bytes_per_launch"]
+    return fields
 
 
-def cpu_baseline(layer, budget_s: float):
-    """The oracle as it stands, on the host cores, over a bounded sample: whole
-    layer calls on the same workload, repeated until the budget is spent."""
-    import oracle.pagedweight_oracle as orc
+def cpu_info():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         threads = 1
-    T = layer.wl.T
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        orc.moe_forward_layer(layer)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
+    return model, int(threads), os.cpu_count()
+
+
+def cpu_baseline(layer, budget_s: float):
+    """The oracle as it stands, on the host cores, over a bounded sample of the
+    same workload: whole experts (every slot routed to the expert, its two
+    blocks dequantized and its FFN run), in ascending expert id until the
+    budget is spent; the layer's time is the mean per-expert time times the
+    number of routed experts."""
+    import oracle.pagedweight_oracle as orc
+    model, threads, ncpu = cpu_info()
+    routed = [int(e) for e in layer.active_experts()]
+    done, spent = [], 0.0
+    for e in routed:
+        ids_e = np.where(layer.ids == e, layer.ids, -1).astype(np.int32)
+        t0 = time.perf_counter()
+        orc.moe_forward_layer(layer, ids=ids_e)
+        spent += time.perf_counter() - t0
+        done.append(e)
+        if spent >= budget_s:
             break
-    return {"value": n * T / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} whole-layer oracle calls ({n * T} tokens) of the same workload, "
-                      f"{el:.1f} s, fp64 numpy; cores = BLAS threads"}
+    layer_s = spent / len(done) * len(routed)
+    T = layer.wl.T
+    return {"value": T / layer_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"experts {done} of the {len(routed)} routed (all their slots), {spent:.1f} s of fp64 numpy; "
+                      f"layer time = mean per expert x {len(routed)}",
+            "os_cpu_count": ncpu, "blas_threads": threads, "cpu_model": model}
 
 
 def timed_ms(evs, stream, fn, n: int) -> float:
@@ -216,13 +271,172 @@ def next_rows(layer, dev, copies, opts, stream, evs, steps: int):
     return out
 
 
+def build_layers(name, workload, T, cache):
+    """The synthetic layer of one configuration.  The Mixtral decode layers at
+    T = 1, 8 and 64 share one storage draw (same seed; their tokens and routing
+    are prefixes of the same streams)."""
+    from any_precision_bitplane_amd import synth
+    wl = synth.WORKLOADS[workload]
+    if T is not None:
+        wl = wl.with_T(T)
+    if workload == "mixtral_decode":
+        if "mixtral_decode_full" not in cache:
+            cache["mixtral_decode_full"] = synth.make_layer(synth.WORKLOADS[workload].with_T(64))
+        full = cache["mixtral_decode_full"]
+        ids, w = synth.draw_router(wl)
+        return synth.Layer(wl, full.planes, full.luts, synth.draw_q(wl, ids, w), synth.draw_x(wl.seed, wl.T, wl.H),
+                           ids, w)
+    return synth.make_routed_layer(wl)
+
+
+def measure(name, layer, dev, copies, args, evs, stream, opts_kw):
+    """Timed region, repeats, and kernel-event pass of one configuration."""
+    import torch
+    from any_precision_bitplane_amd import binding as B
+    from any_precision_bitplane_amd import roofline as RL
+    wl = layer.wl
+    H, I, E, k, T = wl.H, wl.I, wl.E, wl.k, wl.T
+    routed = [int(e) for e in layer.active_experts()]
+    opts = B.make_options(**opts_kw)
+    info = B.pw_moe_path_info(dev.shape, T, opts)
+    family = [f for f in ("gemv", "mgemv", "mfma") if getattr(info, f)]
+    lbytes = RL.layer_bytes(layer.q, layer.ids, H, I, E, T, k)
+    flops = RL.layer_flops(T, k, H, I)
+
+    for i in range(args.warmup):
+        dev.forward(opts, copy=i % copies, stream=stream)
+    torch.cuda.synchronize()
+
+    # Timed region: exactly K layer calls, bracketed by synchronizations, with a
+    # pair of HIP events on the stream around the loop.
+    ev_a, ev_b = evs.create(), evs.create()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs.record(ev_a, stream.cuda_stream)
+    for i in range(args.steps):
+        dev.forward(opts, copy=i % copies, stream=stream)
+    evs.record(ev_b, stream.cuda_stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_step_ms = evs.elapsed_ms(ev_a, ev_b) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    reps = []
+    for _ in range(5):
+        ra, rb = evs.create(), evs.create()
+        torch.cuda.synchronize()
+        evs.record(ra, stream.cuda_stream)
+        for i in range(args.steps):
+            dev.forward(opts, copy=i % copies, stream=stream)
+        evs.record(rb, stream.cuda_stream)
+        torch.cuda.synchronize()
+        reps.append(evs.elapsed_ms(ra, rb) / args.steps)
+        evs.destroy(ra)
+        evs.destroy(rb)
+
+    # Kernel pass: the same K calls with the product kernels' own start / stop
+    # events (gate_up: events 0/1, down: 2/3).
+    kev = [[evs.create() for _ in range(4)] for _ in range(args.steps)]
+    kopts = [B.make_options(events=kev[i], event_mode=B.PW_EVENTS_KERNELS, **opts_kw) for i in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        dev.forward(kopts[i], copy=i % copies, stream=stream)
+    torch.cuda.synchronize()
+    kern = np.array([[evs.elapsed_ms(kev[i][0], kev[i][1]), evs.elapsed_ms(kev[i][2], kev[i][3])]
+                     for i in range(args.steps)])
+    for row in kev:
+        for e in row:
+            evs.destroy(e)
+    # Stage pass: events between the kernels on the stream (kernel plus launch gap).
+    sev = [[evs.create() for _ in range(B.PW_NUM_STAGES + 1)] for _ in range(args.steps)]
+    sopts = [B.make_options(events=sev[i], **opts_kw) for i in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        dev.forward(sopts[i], copy=i % copies, stream=stream)
+    torch.cuda.synchronize()
+    stage = np.array([[evs.elapsed_ms(sev[i][s], sev[i][s + 1]) for s in range(B.PW_NUM_STAGES)]
+                      for i in range(args.steps)]).mean(axis=0)
+    for row in sev:
+        for e in row:
+            evs.destroy(e)
+    evs.destroy(ev_a)
+    evs.destroy(ev_b)
+
+    kms = kern.mean(axis=0)
+    m = 0 if kms[0] >= kms[1] else 1
+    fam = family[-1] if family else "gemv"
+    kname = KERNEL_NAMES[(fam, m)]
+    dom_bytes = RL.module_bytes(layer.q, layer.ids, H, I, E, T, k, m)
+    dom_flops = RL.module_flops(T, k, H, I, m)
+    bound = RL.bound(dom_flops, dom_bytes)
+
+    def rate(ms):
+        if bound == "mfma":
+            return dom_flops / (ms * 1e-3) / 1e12
+        return dom_bytes / (ms * 1e-3) / 1e9
+    peak = RL.MFMA_FP16_PEAK_TFLOPS if bound == "mfma" else RL.HBM_PEAK_GBS
+    achieved = rate(float(kms[m]))
+    span_ms = float(stage[1 + m])
+    roof = {
+        "kernel": f"{kname} ({['gate_up', 'down'][m]})",
+        "bound": bound,
+        "achieved": achieved,
+        "peak": peak,
+        "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+        "frac": achieved / peak,
+        "traffic": None,
+        "algorithmic_bytes_per_launch": dom_bytes,
+        "algorithmic_flops_per_launch": dom_flops,
+        "avg_kernel_ms": float(kms[m]),
+        "timing": "kernel start/stop events handed to the launch (hipExtLaunchKernelGGL), mean of K launches",
+        "event_span": {"avg_ms": span_ms, "frac": rate(span_ms) / peak,
+                       "what": "events on the stream before and after the product (includes the launch gap)"},
+    }
+    tr = profile_fields(name, "traffic", kname)
+    if tr is not None:
+        roof["traffic"] = tr["traffic_bytes_per_launch"]
+    kt = profile_fields(name, "kernels", kname)
+    if kt is not None:
+        roof["kernel_trace"] = {"avg_ms": kt["avg_ns"] * 1e-6, "frac": rate(kt["avg_ns"] * 1e-6) / peak,
+                                "profile": f"profiles/kernels_{name}.txt"}
+
+    status = dev.status()
+    y = dev.y.float().cpu().numpy()
+    ok = bool(np.all(np.isfinite(y))) and status == 0
+    return {
+        "workload": name,
+        "description": wl.description or wl.name,
+        "H": H, "I": I, "E": E, "top_k": k, "T": T,
+        "routed_experts": len(routed),
+        "mean_q_routed": float(np.mean([layer.q[e] for e in routed])),
+        "kernel_family": family,
+        "storage_copies_rotated": copies,
+        "ms_per_step": ms_per_step,
+        "tokens_per_s": T / (ms_per_step * 1e-3),
+        "gpu_ms_per_step": gpu_step_ms,
+        "repeats_gpu_ms_per_step": reps,
+        "median_gpu_ms_per_step": float(np.median(reps)),
+        "algorithmic_bytes": lbytes,
+        "algorithmic_flops": flops,
+        "hbm_gbs": lbytes / (ms_per_step * 1e-3) / 1e9,
+        "hbm_frac": lbytes / (ms_per_step * 1e-3) / 1e9 / RL.HBM_PEAK_GBS,
+        "tflops": flops / (ms_per_step * 1e-3) / 1e12,
+        "mfma_frac": flops / (ms_per_step * 1e-3) / 1e12 / RL.MFMA_FP16_PEAK_TFLOPS,
+        "kernel_ms": {"gate_up": float(kms[0]), "down": float(kms[1])},
+        "stage_ms": {"route": float(stage[0]), "gate_up": float(stage[1]), "down": float(stage[2]),
+                     "combine": float(stage[3])},
+        "roofline": roof,
+        "output_finite_and_status_clear": ok,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="qwen_decode")
-    ap.add_argument("--T", type=int, default=None)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", default=None, choices=[c[0] for c in CONFIGS],
+                    help="run one configuration and report it as the line")
     ap.add_argument("--copies", type=int, default=0, help="storage copies to rotate (0: auto, >= 1 GB)")
     ap.add_argument("--path", type=int, default=0, help="0 auto, 1 GEMV, 2 MFMA, 3 matrix-core GEMV")
     ap.add_argument("--mfma-min", type=int, default=0, help="AUTO: MFMA from this many tokens (0: library default)")
@@ -255,156 +469,86 @@ def main():
         return
     from any_precision_bitplane_amd import binding as B
     from any_precision_bitplane_amd import roofline as RL
-    from any_precision_bitplane_amd import synth
     from any_precision_bitplane_amd.device import DeviceLayer
 
     B.load()
-    wl = synth.WORKLOADS[args.workload]
-    if args.T is not None:
-        wl = wl.with_T(args.T)
-    layer = synth.make_routed_layer(wl)
-    if args.uniform_q:
-        layer.q[:] = args.uniform_q
-    routed = [int(e) for e in layer.active_experts()]
-    H, I, E, k, T = wl.H, wl.I, wl.E, wl.k, wl.T
-    lbytes = RL.layer_bytes(layer.q, layer.ids, H, I, E, T, k)
-    gu_bytes = RL.module_bytes(layer.q, layer.ids, H, I, E, T, k, 0)
-    dn_bytes = RL.module_bytes(layer.q, layer.ids, H, I, E, T, k, 1)
-    flops = RL.layer_flops(T, k, H, I)
-    copies = args.copies or max(2, int(np.ceil(1.0e9 / max(lbytes, 1))))
-    copies = min(copies, 64)
-
-    dev = DeviceLayer(layer, copies=copies, experts=routed)
-    opts = B.make_options(path=args.path, mfma_min_tokens=args.mfma_min, mgemv_min_tokens=args.mgemv_min)
-    stream = torch.cuda.current_stream()
-
-    for i in range(args.warmup):
-        dev.forward(opts, copy=i % copies)
-    torch.cuda.synchronize()
-
     evs = HipEvents()
-    nst = B.PW_NUM_STAGES + 1
+    stream = torch.cuda.current_stream()
+    opts_kw = dict(path=args.path, mfma_min_tokens=args.mfma_min, mgemv_min_tokens=args.mgemv_min)
+    headline = args.only or HEADLINE
+    run = [c for c in CONFIGS if args.only is None or c[0] == args.only]
 
-    # Timed region: exactly K layer calls, bracketed by synchronizations, with
-    # one pair of HIP events on the stream around the whole loop.
-    ev_a, ev_b = evs.create(), evs.create()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    evs.record(ev_a, stream.cuda_stream)
-    for i in range(args.steps):
-        dev.forward(opts, copy=i % copies, stream=stream)
-    evs.record(ev_b, stream.cuda_stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_step_ms = evs.elapsed_ms(ev_a, ev_b) / args.steps
-    ms_per_step = wall * 1e3 / args.steps
+    results, extras, base_layer = {}, None, None
+    cache = {}
+    dev = None
+    for name, workload, T in run:
+        print(f"[bench] {name}: building", file=sys.stderr, flush=True)
+        layer = build_layers(name, workload, T, cache)
+        if args.uniform_q:
+            layer.q[:] = args.uniform_q
+        lbytes = RL.layer_bytes(layer.q, layer.ids, layer.wl.H, layer.wl.I, layer.wl.E, layer.wl.T, layer.wl.k)
+        copies = args.copies or max(2, int(np.ceil(1.0e9 / max(lbytes, 1))))
+        copies = min(copies, 64)
+        if workload == "mixtral_decode" and dev is not None and getattr(dev, "_shared", None) == "mixtral_decode":
+            dev.set_tokens(layer)
+            dev.set_q(layer.q)
+            copies = dev.copies
+        else:
+            dev = None
+            torch.cuda.empty_cache()
+            routed = [int(e) for e in layer.active_experts()]
+            if workload == "mixtral_decode":
+                routed = list(range(layer.wl.E))   # one device copy serves T = 1, 8, 64
+            dev = DeviceLayer(layer, copies=copies, experts=routed)
+            dev._shared = workload
+            dev.copies = copies
+        print(f"[bench] {name}: timing ({copies} storage copies)", file=sys.stderr, flush=True)
+        results[name] = measure(name, layer, dev, copies, args, evs, stream, opts_kw)
+        if name == headline:
+            base_layer = layer
+        if name == "qwen_decode" and not args.no_extras and not args.uniform_q:
+            print("[bench] qwen_decode: around the layer", file=sys.stderr, flush=True)
+            extras = next_rows(layer, dev, copies, B.make_options(**opts_kw), stream, evs, args.steps)
+        if workload != "mixtral_decode":
+            dev = None
+    dev = None
+    torch.cuda.empty_cache()
 
-    # Repeats: the K-call loop five more times, each between a pair of HIP
-    # events (GPU timeline); the median is the protocol's per-call time, `value`
-    # stays the wall-clock time of the one contract-timed loop above.
-    reps = []
-    for _ in range(5):
-        ra, rb = evs.create(), evs.create()
-        torch.cuda.synchronize()
-        evs.record(ra, stream.cuda_stream)
-        for i in range(args.steps):
-            dev.forward(opts, copy=i % copies, stream=stream)
-        evs.record(rb, stream.cuda_stream)
-        torch.cuda.synchronize()
-        reps.append(evs.elapsed_ms(ra, rb) / args.steps)
-
-    # Stage timing: the same K calls again, with events recorded by the library
-    # on the stream between its kernels (kernel duration plus its launch gap).
-    events = [[evs.create() for _ in range(nst)] for _ in range(args.steps)]
-    step_opts = [B.make_options(path=args.path, events=events[i], mfma_min_tokens=args.mfma_min,
-                                mgemv_min_tokens=args.mgemv_min) for i in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        dev.forward(step_opts[i], copy=i % copies, stream=stream)
-    torch.cuda.synchronize()
-    stage_ms = np.zeros((args.steps, B.PW_NUM_STAGES))
-    for i in range(args.steps):
-        for s in range(B.PW_NUM_STAGES):
-            stage_ms[i, s] = evs.elapsed_ms(events[i][s], events[i][s + 1])
-    stage_avg = stage_ms.mean(axis=0)
-    gu_ms = float(stage_avg[B.PW_STAGE_GATE_UP])
-    dn_ms = float(stage_avg[B.PW_STAGE_DOWN])
-    fwd_ms = gpu_step_ms
-
-    # dominant kernel: the longer of the two expert products; priced against
-    # HBM bandwidth or fp16 MFMA throughput, whichever bounds its work
-    if gu_ms >= dn_ms:
-        dom, dom_bytes, dom_ms, dom_m = "gate_up", gu_bytes, gu_ms, 0
-    else:
-        dom, dom_bytes, dom_ms, dom_m = "down", dn_bytes, dn_ms, 1
-    dom_flops = RL.module_flops(T, k, H, I, dom_m)
-    dom_bound = RL.bound(dom_flops, dom_bytes)
-    if dom_bound == "mfma":
-        achieved, peak, unit = dom_flops / (dom_ms * 1e-3) / 1e12, RL.MFMA_FP16_PEAK_TFLOPS, "TFLOP/s"
-    else:
-        achieved, peak, unit = dom_bytes / (dom_ms * 1e-3) / 1e9, RL.HBM_PEAK_GBS, "GB/s"
-
-    status = dev.status()
-    y = dev.y.float().cpu().numpy()
-    ok = bool(np.all(np.isfinite(y))) and status == 0
-
+    head = results[headline]
     rec = {
         "metric": METRIC,
-        "value": T / (ms_per_step * 1e-3),
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp16",
         "data": "synthetic",
         "config": {
-            "workload": wl.description or wl.name,
-            "H": H, "I": I, "E": E, "top_k": k, "T": T,
-            "routed_experts": len(routed),
-            "mean_q_routed": float(np.mean([layer.q[e] for e in routed])),
-            "storage_copies_rotated": copies,
+            "workload": head["description"],
+            "H": head["H"], "I": head["I"], "E": head["E"], "top_k": head["top_k"], "T": head["T"],
+            "routed_experts": head["routed_experts"],
+            "mean_q_routed": head["mean_q_routed"],
+            "storage_copies_rotated": head["storage_copies_rotated"],
             "path": ["auto", "gemv", "mfma", "mgemv"][args.path],
-            "bitwidths": (f"uniform {args.uniform_q}" if args.uniform_q else
-                          {"uniform38": "per block, uniform in 3..8",
-                           "hot8": "hottest 20% of experts at 8 bits, others uniform in {3,4,5}",
-                           "skewed": "per module a permutation of [8,8,4,4,4,3,3,3]"}.get(wl.qmode, wl.qmode)),
+            "kernel_family": head["kernel_family"],
+            "bitwidths": f"uniform {args.uniform_q}" if args.uniform_q else "per block, uniform in 3..8",
         },
-        "layer": {
-            "algorithmic_bytes": lbytes,
-            "algorithmic_flops": flops,
-            "gpu_ms_per_step": gpu_step_ms,
-            "repeats_gpu_ms_per_step": reps,
-            "median_gpu_ms_per_step": float(np.median(reps)),
-            "stage_ms": {"route": float(stage_avg[0]), "gate_up": gu_ms, "down": dn_ms,
-                         "combine": float(stage_avg[3])},
-            "hbm_gbs_gpu_timeline": lbytes / (fwd_ms * 1e-3) / 1e9,
-            "hbm_frac_gpu_timeline": lbytes / (fwd_ms * 1e-3) / 1e9 / RL.HBM_PEAK_GBS,
-            "hbm_gbs_wall": lbytes / (ms_per_step * 1e-3) / 1e9,
-            "tflops_wall": flops / (ms_per_step * 1e-3) / 1e12,
-            "mfma_frac_wall": flops / (ms_per_step * 1e-3) / 1e12 / RL.MFMA_FP16_PEAK_TFLOPS,
-            "output_finite_and_status_clear": ok,
-        },
-        "roofline": {
-            "kernel": dom,
-            "bound": dom_bound,
-            "achieved": achieved,
-            "peak": peak,
-            "unit": unit,
-            "frac": achieved / peak,
-            "traffic": measured_traffic(dom, args.workload) if not (args.uniform_q or args.T) else None,
-            "algorithmic_bytes_per_launch": dom_bytes,
-            "algorithmic_flops_per_launch": dom_flops,
-            "avg_launch_ms": dom_ms,
-        },
+        "hbm_gbs": head["hbm_gbs"],
+        "hbm_frac_of_peak": head["hbm_frac"],
+        "roofline": head["roofline"],
+        "layer": {k: v for k, v in head.items() if k != "roofline"},
+        "per_config": [results[c[0]] for c in run if c[0] != headline],
     }
-    if not args.no_extras and not args.uniform_q:
-        rec["around_the_layer"] = next_rows(layer, dev, copies, opts, stream, evs, args.steps)
-    if not args.no_cpu:
-        rec["cpu_baseline"] = cpu_baseline(layer, args.cpu_budget)
+    if extras is not None:
+        rec["around_the_layer"] = extras
+    if not args.no_cpu and base_layer is not None:
+        print("[bench] oracle on the host cores", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(base_layer, args.cpu_budget)
     print(json.dumps(rec), flush=True)
 
 

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define PW_ABI_VERSION 2
+#define PW_ABI_VERSION 3
 
 typedef int32_t pw_status;
 #define PW_OK                     0
@@ -109,18 +109,29 @@ typedef struct {
 #define PW_STAGE_COMBINE 3
 #define PW_NUM_STAGES    4
 
+/* What the optional events of pw_moe_options record. */
+#define PW_EVENTS_STAGES  0  /* stage_events[s] recorded on the stream right
+                                before stage s, stage_events[PW_NUM_STAGES]
+                                after the last stage (kernel time plus the
+                                launch gaps between them)                      */
+#define PW_EVENTS_KERNELS 1  /* stage_events[0] / [1]: start / stop of the
+                                gate_up product's kernel(s), [2] / [3]: start /
+                                stop of the down product's kernel(s), taken by
+                                the launches themselves (the kernels' own
+                                execution, no launch gap); [4] unused.  A NULL
+                                entry is not recorded                          */
+
 typedef struct {
   int32_t path;              /* PW_PATH_*                                     */
   int32_t mfma_min_tokens;   /* AUTO bands: MFMA from this many tokens per
                                 expert; <= 0: per-call rule or default 256    */
-  /* Optional hipEvent_t handles (as void*).  If stage_events[0] is non-NULL,
-   * event s is recorded on `stream` right before stage s and event
-   * PW_NUM_STAGES after the last stage, so the caller can time each stage. */
+  /* Optional hipEvent_t handles (as void*), used if stage_events[0] is
+   * non-NULL; what they record is set by event_mode. */
   void* stage_events[PW_NUM_STAGES + 1];
   int32_t mgemv_min_tokens;  /* AUTO bands: matrix-core GEMV from this many
                                 tokens per expert (below mfma_min_tokens);
                                 <= 0: per-call rule or default 1              */
-  int32_t reserved;
+  int32_t event_mode;        /* PW_EVENTS_* (other values: PW_ERR_INVALID_ARG) */
 } pw_moe_options;
 
 /* ABI version of the loaded library (PW_ABI_VERSION). */

@@ -39,7 +39,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert B.pw_abi_version() == 2
+    assert B.pw_abi_version() == 3
     for s in (B.PW_OK, B.PW_ERR_INVALID_ARG, B.PW_ERR_UNSUPPORTED_SHAPE, B.PW_ERR_BITWIDTH,
               B.PW_ERR_WORKSPACE, B.PW_ERR_ALIGNMENT, B.PW_ERR_HIP, B.PW_ERR_UNSUPPORTED, 12345):
         assert isinstance(B.pw_status_str(s), str) and B.pw_status_str(s)

@@ -99,15 +99,30 @@ def test_dequant_bit_exact_tiny_all_blocks(torch):
                 _dequant_check(torch, L.planes[e][m], L.luts[e][m], q, f"tiny e{e} m{m}")
 
 
-def test_dequant_bit_exact_qwen_blocks(torch):
+@pytest.mark.parametrize("group", range(6))
+def test_dequant_bit_exact_qwen_every_block(torch, group):
+    """Every block of the Qwen-shaped layer (60 experts x 2 modules, ten experts
+    per group) at every bitwidth 3..8."""
     wl = synth.WORKLOADS["qwen_decode"]
-    for e in (0, 37):
+    for e in range(10 * group, 10 * group + 10):
         for m in (0, 1):
             N, K = wl.block_shape(m)
             planes = synth.draw_planes(wl.seed, e, m, N, K)
             lut = synth.draw_lut(wl.seed, e, m, N)
             for q in range(3, 9):
                 _dequant_check(torch, planes, lut, q, f"qwen e{e} m{m}")
+
+
+@pytest.mark.parametrize("m", [0, 1])
+def test_dequant_bit_exact_mixtral_full_block(torch, m):
+    """One full-size Mixtral-shaped block per module (gate_up 28672 x 4096,
+    down 4096 x 14336) at every bitwidth 3..8."""
+    wl = synth.WORKLOADS["mixtral_prefill"]
+    N, K = wl.block_shape(m)
+    planes = synth.draw_planes(wl.seed, 5, m, N, K)
+    lut = synth.draw_lut(wl.seed, 5, m, N)
+    for q in range(3, 9):
+        _dequant_check(torch, planes, lut, q, f"mixtral e5 m{m}")
 
 
 def test_dequant_ragged_shapes(torch):
@@ -370,21 +385,102 @@ def test_forward_qwen_batched_auto_mixes_paths(torch):
     compare(y2, ref, "qwen_batched gemv")
 
 
-def test_forward_mixtral_prefill_sampled(torch):
-    """Full-size prefill call (T=4096, skewed bitwidths, all experts on MFMA);
-    the oracle checks a sample of tokens one by one."""
-    L = layer_for("mixtral_prefill", routed_only=False)
-    say("forward mixtral_prefill T=4096 AUTO")
-    _, y = run_forward(torch, L, B.PW_PATH_AUTO)
+# Full-size prefill (T = 4096, E = 8, top-2, skewed bitwidths).  Every expert
+# gets about 1000 slots, i.e. four or five 256-slot MFMA tiles, the last one
+# partial (fewer than 128 slots takes the direct-activation variant).  Each pair
+# test drops every slot outside two experts (ids -> -1): those experts' slots,
+# their order and hence their MFMA tiles stay exactly as in the full call, and
+# every token routed to them is compared with the oracle over the same ids, so
+# all 16 blocks are checked at full K on all of their tiles.  The oracle
+# dequantizes two experts per test, which bounds its time and memory.  The full
+# call is then checked on stratified tokens: for every expert, tokens of its
+# first and of its last tile, against the sum of the four pairs' references.
+_C4 = {}
+_C4_PAIRS = [(0, 1), (2, 3), (4, 5), (6, 7)]
+
+
+def _c4_layer():
+    if "layer" not in _C4:
+        _C4["layer"] = layer_for("mixtral_prefill", routed_only=False)
+    return _C4["layer"]
+
+
+def _c4_device(torch):
+    if "dev" not in _C4:
+        from any_precision_bitplane_amd.device import DeviceLayer
+        _C4["dev"] = DeviceLayer(_c4_layer())
+    return _C4["dev"]
+
+
+def _c4_pair_ids(a, b):
+    ids = _c4_layer().ids.copy()
+    ids[(ids != a) & (ids != b)] = -1
+    return ids
+
+
+def _c4_pair_ref(a, b):
+    """Oracle y for all tokens with only experts a and b routed."""
+    key = ("ref", a, b)
+    if key not in _C4:
+        L = _c4_layer()
+        _C4[key] = orc.moe_forward_layer(L, ids=_c4_pair_ids(a, b))
+    return _C4[key]
+
+
+@pytest.mark.parametrize("pair", _C4_PAIRS)
+def test_forward_mixtral_prefill_expert_pairs_all_tokens(torch, pair):
+    a, b = pair
+    L = _c4_layer()
+    dev = _c4_device(torch)
+    ids = _c4_pair_ids(a, b)
+    say(f"forward mixtral_prefill T=4096 AUTO, only experts {a},{b} routed "
+        f"(q gate_up {L.q[a][0]},{L.q[b][0]}; q down {L.q[a][1]},{L.q[b][1]})")
+    dev.ids.copy_(torch.from_numpy(ids))
+    dev.forward(B.make_options(path=B.PW_PATH_AUTO))
+    torch.cuda.synchronize()
+    y = dev.y.float().cpu().numpy()
+    dev.ids.copy_(torch.from_numpy(L.ids))
+    assert dev.status() == B.PW_DEV_BAD_EXPERT_ID     # the dropped slots, nothing else
+    rows = np.nonzero((ids >= 0).any(axis=1))[0]
+    assert len(rows) > 1500
+    assert not np.any(y[np.setdiff1d(np.arange(L.wl.T), rows)])
+    ref = _c4_pair_ref(a, b)
+    compare(y[rows], ref[rows], f"mixtral_prefill experts {a},{b}: all {len(rows)} tokens")
+
+
+def _c4_strata():
+    """For every expert: 4 tokens from its first 256-slot tile and 4 from its last."""
+    L = _c4_layer()
+    flat = L.ids.reshape(-1)
+    toks = set()
+    for e in range(L.wl.E):
+        slots = np.nonzero(flat == e)[0]          # slot order = the expert's sorted order
+        ntile = (len(slots) + 255) // 256
+        first = slots[:256] // L.wl.k
+        last = slots[256 * (ntile - 1):] // L.wl.k
+        for part in (first, last):
+            pick = np.unique(part)
+            toks.update(int(t) for t in pick[np.linspace(0, len(pick) - 1, 4).astype(int)])
+    return sorted(toks)
+
+
+def test_forward_mixtral_prefill_full_call_stratified(torch):
+    """The full-size call with every expert routed, compared on tokens drawn
+    from the first and the last MFMA tile of every expert."""
+    L = _c4_layer()
+    dev = _c4_device(torch)
+    say("forward mixtral_prefill T=4096 AUTO, all experts")
+    dev.forward(B.make_options(path=B.PW_PATH_AUTO))
+    torch.cuda.synchronize()
+    assert dev.status() == 0
+    y = dev.y.float().cpu().numpy()
     assert np.all(np.isfinite(y))
-    # tokens whose two experts lie in a small subset keep the oracle's work bounded
-    rng = np.random.default_rng(5)
-    subset = {0, 1, 2}
-    cand = [t for t in range(L.wl.T) if set(int(e) for e in L.ids[t]) <= subset]
-    toks = sorted(rng.choice(cand, size=min(12, len(cand)), replace=False).tolist()) + [0, L.wl.T - 1]
-    toks = sorted(set(toks))
-    ref = oracle_y(L, tokens=toks)
-    compare(y[toks], ref, f"mixtral_prefill sampled tokens {toks}")
+    toks = _c4_strata()
+    per = {e: sum(1 for t in toks if e in set(int(v) for v in L.ids[t])) for e in range(L.wl.E)}
+    assert min(per.values()) >= 8, per
+    ref = sum(_c4_pair_ref(a, b)[toks] for a, b in _C4_PAIRS)
+    compare(y[toks], ref, f"mixtral_prefill full call, {len(toks)} stratified tokens")
+    _C4.clear()
 
 
 # ---------------------------------------------------------------------------
