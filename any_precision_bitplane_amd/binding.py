@@ -109,6 +109,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "pw_workspace_init": (c_int32, [c_void_p, c_size_t, c_void_p]),
         "pw_moe_forward": (c_int32, [POINTER(PwMoeShape), c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_void_p, c_void_p, c_size_t, POINTER(PwMoeOptions), c_void_p]),
+        "pw_moe_forward_noalloc": (c_int32, [POINTER(PwMoeShape), c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                             c_void_p, c_void_p, c_void_p, POINTER(PwMoeOptions), c_void_p]),
         "pw_moe_path_info": (c_int32, [POINTER(PwMoeShape), c_int32, POINTER(PwMoeOptions), POINTER(PwPathInfo)]),
         "pw_dequant_block": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
         "pw_get_device_status": (c_int32, [c_void_p, POINTER(c_uint32), c_void_p]),
@@ -139,7 +141,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
 
 def exported_symbols() -> Sequence[str]:
     return ["pw_abi_version", "pw_status_str", "pw_plane_words", "pw_lut_elems", "pw_lut_offset",
-            "pw_check_shape", "pw_workspace_bytes", "pw_workspace_init", "pw_moe_forward",
+            "pw_check_shape", "pw_workspace_bytes", "pw_workspace_init", "pw_moe_forward", "pw_moe_forward_noalloc",
             "pw_moe_path_info",
             "pw_dequant_block", "pw_get_device_status", "pw_pager_create", "pw_pager_destroy",
             "pw_pager_set_block", "pw_pager_request", "pw_pager_execute", "pw_pager_commit", "pw_pager_info",
@@ -227,6 +229,19 @@ def pw_moe_forward(shp: PwMoeShape, T: int, x, ids, w, blocks, q, y, workspace,
                                ctypes.byref(opts) if opts is not None else None, _stream(stream))
     if check:
         _check(st, "pw_moe_forward")
+    return st
+
+
+PW_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def pw_moe_forward_noalloc(shp: PwMoeShape, T: int, x, ids, w, blocks, q, y, status=None,
+                           opts: Optional[PwMoeOptions] = None, stream=None, check: bool = True) -> int:
+    st = load().pw_moe_forward_noalloc(ctypes.byref(shp), T, _ptr(x), _ptr(ids), _ptr(w), _ptr(blocks), _ptr(q),
+                                       _ptr(y), _ptr(status), ctypes.byref(opts) if opts is not None else None,
+                                       _stream(stream))
+    if check:
+        _check(st, "pw_moe_forward_noalloc")
     return st
 
 

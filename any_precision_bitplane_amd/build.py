@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedweight.so")
-SOURCES = ["pw_api.cpp", "pw_pager.cpp", "pw_route.hip", "pw_gemv.hip", "pw_mfma.hip", "pw_misc.hip", "pw_router.hip", "pw_planner.cpp", "pw_mgemv.hip"]
+SOURCES = ["pw_api.cpp", "pw_pager.cpp", "pw_route.hip", "pw_gemv.hip", "pw_mfma.hip", "pw_misc.hip", "pw_router.hip", "pw_planner.cpp", "pw_mgemv.hip", "pw_noalloc.hip"]
 ARCH = "gfx950"
 
 

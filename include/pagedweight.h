@@ -175,6 +175,26 @@ pw_status pw_moe_forward(const pw_moe_shape* shape, int32_t T,
                          uint16_t* y, void* workspace, size_t workspace_bytes,
                          const pw_moe_options* opts, void* stream);
 
+/* Allocation-free variant of pw_moe_forward, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same computation, kernels and results
+ * as pw_moe_forward; the scratch the workspace would hold lives in a static
+ * device array of PW_NOALLOC_SCRATCH_BYTES per GPU, kept until the process
+ * ends.  The call allocates nothing.
+ *   shape, T, x, ids, w, blocks, q, y, opts, stream: as for pw_moe_forward
+ *   status  device uint32, may be NULL: device errors (PW_DEV_* bits) are OR-ed
+ *           into it; the caller clears and reads it.  With NULL they are not
+ *           reported.
+ * Errors: those of pw_moe_forward; PW_ERR_WORKSPACE if the call needs more
+ * than PW_NOALLOC_SCRATCH_BYTES (pw_workspace_bytes(shape, T) bytes);
+ * PW_ERR_HIP if the scratch address cannot be found.  All calls on one GPU
+ * share its scratch array: calls that overlap in time on one GPU race.  Each
+ * call overwrites what it reads, so nothing needs clearing between calls. */
+#define PW_NOALLOC_SCRATCH_BYTES (64u << 20)
+pw_status pw_moe_forward_noalloc(const pw_moe_shape* shape, int32_t T, const uint16_t* x, const int32_t* ids,
+                                 const float* w, const pw_block_desc* blocks, const uint8_t* q, uint16_t* y,
+                                 uint32_t* status, const pw_moe_options* opts, void* stream);
+
 /* The kernel families a pw_moe_forward call with this shape, T and options
  * runs (the fused kernel's dispatch between its decode, moderate-batch and
  * prefill forms, Core components 3), without touching the GPU.  Host only;
