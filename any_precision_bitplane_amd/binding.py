@@ -112,7 +112,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "pw_moe_forward_noalloc": (c_int32, [POINTER(PwMoeShape), c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                              c_void_p, c_void_p, c_void_p, POINTER(PwMoeOptions), c_void_p]),
         "pw_moe_path_info": (c_int32, [POINTER(PwMoeShape), c_int32, POINTER(PwMoeOptions), POINTER(PwPathInfo)]),
-        "pw_dequant_block": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
+        "pw_planes_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
+        "pw_pack_planes": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
+        "pw_dequant_block": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p,
+                                       c_void_p]),
         "pw_get_device_status": (c_int32, [c_void_p, POINTER(c_uint32), c_void_p]),
         "pw_router_topk": (c_int32, [POINTER(PwMoeShape), c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
@@ -143,7 +146,7 @@ def exported_symbols() -> Sequence[str]:
     return ["pw_abi_version", "pw_status_str", "pw_plane_words", "pw_lut_elems", "pw_lut_offset",
             "pw_check_shape", "pw_workspace_bytes", "pw_workspace_init", "pw_moe_forward", "pw_moe_forward_noalloc",
             "pw_moe_path_info",
-            "pw_dequant_block", "pw_get_device_status", "pw_pager_create", "pw_pager_destroy",
+            "pw_dequant_block", "pw_planes_bytes", "pw_pack_planes", "pw_get_device_status", "pw_pager_create", "pw_pager_destroy",
             "pw_pager_set_block", "pw_pager_request", "pw_pager_execute", "pw_pager_commit", "pw_pager_info",
             "pw_pager_arena_used", "pw_router_topk", "pw_moe_forward_routed", "pw_plan_bitwidths"]
 
@@ -252,8 +255,21 @@ def pw_moe_path_info(shp: PwMoeShape, T: int, opts: Optional[PwMoeOptions] = Non
     return info
 
 
-def pw_dequant_block(planes, lut_all, N: int, K: int, q: int, w_out, stream=None, check: bool = True) -> int:
-    st = load().pw_dequant_block(_ptr(planes), _ptr(lut_all), N, K, q, _ptr(w_out), _stream(stream))
+def pw_planes_bytes(N: int, K: int, nplanes: int) -> int:
+    return load().pw_planes_bytes(N, K, nplanes)
+
+
+def pw_pack_planes(canon, N: int, K: int, nplanes: int, module: int, dev_layout, stream=None,
+                   check: bool = True) -> int:
+    st = load().pw_pack_planes(_ptr(canon), N, K, nplanes, module, _ptr(dev_layout), _stream(stream))
+    if check:
+        _check(st, "pw_pack_planes")
+    return st
+
+
+def pw_dequant_block(planes, lut_all, N: int, K: int, q: int, w_out, module: int = 0, stream=None,
+                     check: bool = True) -> int:
+    st = load().pw_dequant_block(_ptr(planes), _ptr(lut_all), N, K, q, module, _ptr(w_out), _stream(stream))
     if check:
         _check(st, "pw_dequant_block")
     return st

@@ -331,13 +331,30 @@ pw_status pw_moe_forward_routed(const pw_moe_shape* shape, int32_t T, const uint
   return pw_moe_forward(shape, T, x, ids, w, blocks, q, y, workspace, workspace_bytes, opts, stream);
 }
 
+size_t pw_planes_bytes(int32_t N, int32_t K, int32_t nplanes) {
+  if (N <= 0 || K <= 0 || K % 32 || N % 16 || nplanes < 1 || nplanes > kMaxBits) return 0;
+  return (size_t)nplanes * (size_t)N * (size_t)(K / 32) * 4u;
+}
+
+pw_status pw_pack_planes(const uint32_t* canon, int32_t N, int32_t K, int32_t nplanes, int32_t module,
+                         uint32_t* dev_layout, void* stream) {
+  if (!canon || !dev_layout || N <= 0 || K <= 0 || nplanes < 1 || nplanes > kMaxBits) return PW_ERR_INVALID_ARG;
+  if (module != 0 && module != 1) return PW_ERR_INVALID_ARG;
+  if (K % 32 || N % 16) return PW_ERR_UNSUPPORTED_SHAPE;
+  if ((size_t)N * (size_t)(K / 32) * (size_t)nplanes > 0xFFFFFFFFull) return PW_ERR_UNSUPPORTED_SHAPE;
+  if (!aligned(canon, 4) || !aligned(dev_layout, 16)) return PW_ERR_ALIGNMENT;
+  if ((const void*)canon == (const void*)dev_layout) return PW_ERR_INVALID_ARG;   // not in place
+  return hip_status(launch_pack(canon, N, K, nplanes, module, dev_layout, (hipStream_t)stream));
+}
+
 pw_status pw_dequant_block(const uint32_t* planes, const uint16_t* lut_all, int32_t N, int32_t K, int32_t q,
-                           uint16_t* w_out, void* stream) {
+                           int32_t module, uint16_t* w_out, void* stream) {
   if (!planes || !lut_all || !w_out || N <= 0 || K <= 0) return PW_ERR_INVALID_ARG;
-  if (K % 32) return PW_ERR_UNSUPPORTED_SHAPE;
+  if (module != 0 && module != 1) return PW_ERR_INVALID_ARG;
+  if (K % 32 || N % 16) return PW_ERR_UNSUPPORTED_SHAPE;
   if (q < kMinBits || q > kMaxBits) return PW_ERR_BITWIDTH;
   if (!aligned(planes, 4) || !aligned(lut_all, 16) || !aligned(w_out, 16)) return PW_ERR_ALIGNMENT;
-  return hip_status(launch_dequant(planes, lut_all, N, K, q, w_out, (hipStream_t)stream));
+  return hip_status(launch_dequant(planes, lut_all, N, K, q, module, w_out, (hipStream_t)stream));
 }
 
 pw_status pw_get_device_status(void* workspace, uint32_t* flags, void* stream) {

@@ -1,10 +1,11 @@
 // Device-side building blocks shared by the libpagedweight kernels (gfx950).
 //
-// Storage format of a block (N rows, K columns, W = K/32 words per row):
-// plane-major uint32 [8][N][W]; bit j of word [p][n][c] is plane p (plane 0 =
-// most significant) of weight (n, 32c + j).  The code of a weight at bitwidth
-// q is the value of its first q planes; its weight is the row's fp16 table
-// entry for that code ("Technical summary: PagedWeight", Core components 1).
+// Bit planes of a block (N rows, K columns, W = K/32 words per row): bit j of
+// word (p, n, c) is plane p (plane 0 = most significant) of weight
+// (n, 32c + j).  The code of a weight at bitwidth q is the value of its first
+// q planes; its weight is the row's fp16 table entry for that code
+// ("Technical summary: PagedWeight", Core components 1).  The kernels read the
+// device layout described below (written by pw_pack_planes).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -20,6 +21,50 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 constexpr int kWave = 64;
 
 __host__ __device__ constexpr int lut_offset(int N, int b) { return N * ((1 << b) - 8); }
+
+// ---------------------------------------------------------------------------
+// Device plane layout.
+//
+// Planes stay outermost, so a block at bitwidth q is the prefix of its first
+// q planes, and a plane holds exactly N W words.  Inside a plane the words
+// sit in tiles of 16 device rows by 16 words, tile-row-major; inside a tile
+// the 16 rows follow each other, each holding the tile's words (16, or
+// W mod 16 in the last column tile):
+//   word (d, c) -> (d >> 4) 16 W + (c >> 4) 256 + (d & 15) wct(c) + (c & 15),
+//   wct(c) = min(16, W - (c & ~15)).
+// So 16 rows x 16 words (512 weights per row) are one contiguous 1 KB piece,
+// and the 16 words of one row are 64 contiguous bytes.  In a gate_up block
+// (N = 2I) the device rows interleave gate and up: tile t holds gate rows
+// 8t .. 8t+7 and then the matching up rows I + 8t .. I + 8t + 7, so every
+// tile carries both halves SwiGLU needs.  Down blocks keep their row order.
+// Requires N % 16 == 0 and, for gate_up, I % 8 == 0.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline int dev_row_of_gate(int i) { return ((i >> 3) << 4) + (i & 7); }
+__host__ __device__ inline int dev_row_of_up(int i) { return ((i >> 3) << 4) + 8 + (i & 7); }
+
+// canonical row n of a block -> device row (gu: gate_up block with I = N / 2)
+__host__ __device__ inline int dev_row(int n, int I, bool gu) {
+  return !gu ? n : (n < I ? dev_row_of_gate(n) : dev_row_of_up(n - I));
+}
+
+// device row d -> canonical row
+__host__ __device__ inline int canon_row(int d, int I, bool gu) {
+  if (!gu) return d;
+  const int t = d >> 4, r = d & 15;
+  return r < 8 ? 8 * t + r : I + 8 * t + (r - 8);
+}
+
+// words per row in the column tile of word c
+__host__ __device__ inline uint32_t tile_width(int c, int W) {
+  const int rest = W - (c & ~15);
+  return (uint32_t)(rest < 16 ? rest : 16);
+}
+
+// word offset of (device row d, word c) inside one plane
+__host__ __device__ inline uint32_t dev_word(int d, int c, int W) {
+  return (uint32_t)(d >> 4) * 16u * (uint32_t)W + (uint32_t)(c >> 4) * 256u + (uint32_t)(d & 15) * tile_width(c, W) +
+         (uint32_t)(c & 15);
+}
 
 // ---------------------------------------------------------------------------
 // Bit-plane -> code fields.

@@ -489,8 +489,9 @@ __device__ __forceinline__ int slot_of(const GemvArgs& A, const Slots& sl, int r
 // A chunk: gate_up pairs [first, first + n) (n <= 8; chunk row r < 8 is gate
 // row first + r, chunk row 8 + r the matching up row), or down rows
 // [first, first + n) (n <= 16) of K part kpart.  Chunk rows past n are masked.
-// Rows of one row group are consecutive rows of the block, so each plane load
-// of a group reads one contiguous 1 KB run (K = 2048).
+// Rows of one row group are consecutive rows of the block; in the device
+// layout a row's 16-word runs of consecutive rows sit next to each other, so
+// the four loads of a group touch the same 256-byte spans.
 struct Chunk {
   int first, n, kpart;
 };
@@ -504,6 +505,13 @@ __device__ __forceinline__ int chunk_row(const Chunk& ch, int r, int I) {
 template <bool GU>
 __device__ __forceinline__ bool chunk_row_valid(const Chunk& ch, int r) {
   return GU ? (r & 7) < ch.n : r < ch.n;
+}
+
+// Device-layout row of chunk row r (gate_up rows are interleaved per tile).
+template <bool GU>
+__device__ __forceinline__ int chunk_dev_row(const Chunk& ch, int r) {
+  if constexpr (GU) return r < 8 ? dev_row_of_gate(ch.first + r) : dev_row_of_up(ch.first + (r & 7));
+  else return ch.first + r;
 }
 
 template <int Q, int NT, bool GU>
@@ -587,7 +595,7 @@ __device__ __forceinline__ void chunk_body(const GemvArgs& A, const Slots& sl, c
 #pragma unroll
       for (int r = 0; r < G; ++r) {
         const uint32_t voff = (wc < W && chunk_row_valid<GU>(ch, g * G + r))
-                                  ? ((uint32_t)chunk_row<GU>(ch, g * G + r, I) * (uint32_t)W + (uint32_t)wc) * 4u
+                                  ? dev_word(chunk_dev_row<GU>(ch, g * G + r), wc, W) * 4u
                                   : kOutOfRange;
 #pragma unroll
         for (int p = 0; p < Q; ++p) P[r][p] = buf_load_u32(prs, voff, (uint32_t)p * pstride);

@@ -173,8 +173,9 @@ hipError_t launch_mgemv_down(const ExpertArgs& a, const uint16_t* h, float* o, h
                              const KernelEvents& ev);
 hipError_t launch_combine(const float* o, const float* w, const int32_t* inv, int T, int k, int H, int kparts,
                           uint16_t* y, hipStream_t s);
-hipError_t launch_dequant(const uint32_t* planes, const uint16_t* lut_all, int N, int K, int q,
+hipError_t launch_dequant(const uint32_t* planes, const uint16_t* lut_all, int N, int K, int q, int module,
                           uint16_t* out, hipStream_t s);
+hipError_t launch_pack(const uint32_t* canon, int N, int K, int nplanes, int module, uint32_t* out, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, int T, int H, int E, int k, float* logits,
                          int32_t* ids, float* w, uint32_t* count, float* mass, hipStream_t s);

@@ -125,7 +125,7 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& A, int e, int n_e, int
   // of that word (the two threads of a pair load the same plane words).
   const int dr = tid >> 2, dw = (tid >> 1) & 1, dh = tid & 1;
   const bool dr_ok = mrow_ok<GU>(nt, dr, I, H);
-  const uint32_t drow = (uint32_t)mrow<GU>(nt, dr, I);
+  const int ddev = dev_row(mrow<GU>(nt, dr, I), I, GU);   // device-layout row
   const uint32_t tab_base = lds_addr(tabs) + (uint32_t)(dr * TAB);
   // Activation job (all waves): token row xr, columns [32 xh, +32) of each K step.
   const int xr = tid >> 1, xh = tid & 1;
@@ -142,7 +142,7 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& A, int e, int n_e, int
   auto prefetch_planes = [&](uint32_t (&P)[Q], int step) {
     if (step >= nk) return;
     const int wc = ((step * kTK) >> 5) + dw;
-    const uint32_t voff = (dr_ok && wc < W) ? (drow * (uint32_t)W + (uint32_t)wc) * 4u : kOutOfRange;
+    const uint32_t voff = (dr_ok && wc < W) ? dev_word(ddev, wc, W) * 4u : kOutOfRange;
 #pragma unroll
     for (int p = 0; p < Q; ++p) P[p] = buf_load_u32(prs, voff, (uint32_t)p * pstride);
   };
@@ -327,7 +327,7 @@ __device__ __forceinline__ void mfma_tile_direct(const MfmaArgs& A, int e, int n
   // of that word (the two threads of a pair load the same plane words).
   const int dr = tid >> 2, dw = (tid >> 1) & 1, dh = tid & 1;
   const bool dr_ok = mrow_ok<GU>(nt, dr, I, H);
-  const uint32_t drow = (uint32_t)mrow<GU>(nt, dr, I);
+  const int ddev = dev_row(mrow<GU>(nt, dr, I), I, GU);   // device-layout row
   const uint32_t tab_base = lds_addr(tabs) + (uint32_t)(dr * TAB);
   uint32_t Pa[Q], Pb[Q];
 
@@ -335,7 +335,7 @@ __device__ __forceinline__ void mfma_tile_direct(const MfmaArgs& A, int e, int n
   auto prefetch_planes = [&](uint32_t (&P)[Q], int step) {
     if (step >= nk) return;
     const int wc = ((step * kTK) >> 5) + dw;
-    const uint32_t voff = (dr_ok && wc < W) ? (drow * (uint32_t)W + (uint32_t)wc) * 4u : kOutOfRange;
+    const uint32_t voff = (dr_ok && wc < W) ? dev_word(ddev, wc, W) * 4u : kOutOfRange;
 #pragma unroll
     for (int p = 0; p < Q; ++p) P[p] = buf_load_u32(prs, voff, (uint32_t)p * pstride);
   };

@@ -79,19 +79,20 @@ __device__ __forceinline__ void mg_chunk(const MgArgs& A, int e, int n_e, int of
   bool row_ok;
   const int row = mg_row<GU>(ch, n, I, H, row_ok);
 
-  // K is walked in 512-wide super-chunks: lane group g reads plane words
-  // 16 C + 4 g .. +4 of its row (64 contiguous bytes per row and plane across
-  // the four groups, one line), and word 16 C + 4 g + i feeds sub-chunk i.
-  // Rows start on 16-byte boundaries when W % 4 == 0 (one 16-byte load per
-  // plane); otherwise four 4-byte loads.  Words past the row's end belong to
-  // the next row (or read as zero past the buffer); their activations read as
-  // zero, so they add nothing.
+  // K is walked in 512-wide super-chunks C: lane group g reads plane words
+  // 16 C + 4 g .. +4 of its row, and word 16 C + 4 g + i feeds sub-chunk i.
+  // The item's 16 rows are device tile ch (gate_up: 8 gate rows and their 8
+  // up rows), so the wave's load of one plane is the tile's contiguous 1 KB
+  // piece (less in a narrower last column tile).  With W % 4 == 0 a lane's
+  // four words are one aligned 16-byte load; otherwise four 4-byte loads.
+  // Words past the row's end are not read and count as zero.
   const int ns = (W + 15) >> 4;
   const bool vec = (W & 3) == 0;
+  const int drow = 16 * ch + n;
   auto load_planes = [&](uint32_t (&P)[Q][4], int C) {
     const int wd = 16 * C + 4 * g;
-    const uint32_t voff = (row_ok && C < ns && wd < W) ? ((uint32_t)row * (uint32_t)W + (uint32_t)wd) * 4u
-                                                       : kOutOfRange;
+    const bool live = row_ok && C < ns && wd < W;
+    const uint32_t voff = live ? dev_word(drow, wd, W) * 4u : kOutOfRange;
     if (vec) {
 #pragma unroll
       for (int p = 0; p < Q; ++p) {
@@ -104,7 +105,8 @@ __device__ __forceinline__ void mg_chunk(const MgArgs& A, int e, int n_e, int of
       for (int p = 0; p < Q; ++p)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          P[p][i] = buf_load_u32(prs, voff == kOutOfRange ? kOutOfRange : voff + 4u * i, (uint32_t)p * pstride);
+          P[p][i] = buf_load_u32(prs, (live && wd + i < W) ? dev_word(drow, wd + i, W) * 4u : kOutOfRange,
+                                 (uint32_t)p * pstride);
     }
   };
   uint32_t P0[Q][4], P1[Q][4];

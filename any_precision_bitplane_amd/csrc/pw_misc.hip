@@ -67,17 +67,59 @@ hipError_t launch_combine(const float* o, const float* w, const int32_t* inv, in
   return hipGetLastError();
 }
 
+// Canonical planes [nplanes][N][W] -> device layout (see pw_device.h).  One
+// thread per destination word, in destination order, so the stores are
+// contiguous; the loads gather along rows.  A pure permutation of words.
+__global__ __launch_bounds__(256) void pack_kernel(const uint32_t* __restrict__ src, int N, int W, size_t total,
+                                                   int I_gu, uint32_t* __restrict__ dst) {
+  const size_t plane = (size_t)N * W;
+  const uint32_t tile_row = 16u * (uint32_t)W;
+  const int nfull = W >> 4;                 // full 16-word column tiles
+  const int wlast = W - 16 * nfull;         // width of the last, partial one (0: none)
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t p = i / plane;
+    const uint32_t off = (uint32_t)(i - p * plane);
+    const uint32_t rt = off / tile_row;
+    const uint32_t rem = off - rt * tile_row;
+    int r, c;
+    if (rem < 256u * (uint32_t)nfull) {
+      const uint32_t ct = rem >> 8, within = rem & 255u;
+      r = (int)(within >> 4);
+      c = (int)(16u * ct + (within & 15u));
+    } else {
+      const uint32_t within = rem - 256u * (uint32_t)nfull;
+      r = (int)(within / (uint32_t)wlast);
+      c = 16 * nfull + (int)(within - (uint32_t)r * (uint32_t)wlast);
+    }
+    const int d = (int)(16u * rt) + r;
+    const int n = I_gu > 0 ? canon_row(d, I_gu, true) : d;
+    dst[i] = src[p * plane + (size_t)n * W + c];
+  }
+}
+
+hipError_t launch_pack(const uint32_t* canon, int N, int K, int nplanes, int module, uint32_t* out, hipStream_t s) {
+  const int W = K >> 5;
+  const size_t total = (size_t)nplanes * N * W;
+  size_t blocks = (total + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, canon, N, W, total,
+                     module == 0 ? N / 2 : 0, out);
+  return hipGetLastError();
+}
+
 // Dequantize one block at bitwidth Q: out[n][c] = table_Q[n][code_Q(n, c)]
-// ("Technical summary: PagedWeight", Core components 1).  Same decode as the
-// GEMV kernels: a wave owns 8 rows, lanes own plane-word columns, the row
-// tables sit in LDS.
+// ("Technical summary: PagedWeight", Core components 1), rows in canonical
+// order, planes read from the device layout.  Same decode as the GEMV
+// kernels: a wave owns 8 rows, lanes own plane-word columns, the row tables
+// sit in LDS.
 constexpr int kDqThreads = 256;
 constexpr int kDqRowsPerWave = 8;
 
 template <int Q>
 __global__ __launch_bounds__(kDqThreads) void dequant_kernel(const uint32_t* __restrict__ planes,
                                                             const uint16_t* __restrict__ lut_all, int N, int K,
-                                                            uint16_t* __restrict__ out) {
+                                                            int I_gu, uint16_t* __restrict__ out) {
   constexpr int TAB = (1 << Q) * 2;
   constexpr int CH = TAB / 16;
   __shared__ __align__(16) uint8_t lds[(kDqThreads / kWave) * kDqRowsPerWave * TAB];
@@ -107,9 +149,10 @@ __global__ __launch_bounds__(kDqThreads) void dequant_kernel(const uint32_t* __r
     for (int r = 0; r < kDqRowsPerWave; ++r) {
       const int row = row0 + r;
       if (row >= N) continue;
+      const size_t src = dev_word(I_gu > 0 ? dev_row(row, I_gu, true) : row, wc, W);
       uint32_t P[Q];
 #pragma unroll
-      for (int pp = 0; pp < Q; ++pp) P[pp] = planes[pp * pstride + (size_t)row * W + wc];
+      for (int pp = 0; pp < Q; ++pp) P[pp] = planes[pp * pstride + src];
       uint32_t R[8];
       planes_to_fields<Q>(P, R);
       uint32_t packed[16];
@@ -122,17 +165,18 @@ __global__ __launch_bounds__(kDqThreads) void dequant_kernel(const uint32_t* __r
   }
 }
 
-hipError_t launch_dequant(const uint32_t* planes, const uint16_t* lut_all, int N, int K, int q, uint16_t* out,
-                          hipStream_t s) {
+hipError_t launch_dequant(const uint32_t* planes, const uint16_t* lut_all, int N, int K, int q, int module,
+                          uint16_t* out, hipStream_t s) {
   const int rows_per_block = (kDqThreads / kWave) * kDqRowsPerWave;
   dim3 grid((N + rows_per_block - 1) / rows_per_block);
+  const int I_gu = module == 0 ? N / 2 : 0;
   switch (q) {
-    case 3: hipLaunchKernelGGL(dequant_kernel<3>, grid, dim3(kDqThreads), 0, s, planes, lut_all, N, K, out); break;
-    case 4: hipLaunchKernelGGL(dequant_kernel<4>, grid, dim3(kDqThreads), 0, s, planes, lut_all, N, K, out); break;
-    case 5: hipLaunchKernelGGL(dequant_kernel<5>, grid, dim3(kDqThreads), 0, s, planes, lut_all, N, K, out); break;
-    case 6: hipLaunchKernelGGL(dequant_kernel<6>, grid, dim3(kDqThreads), 0, s, planes, lut_all, N, K, out); break;
-    case 7: hipLaunchKernelGGL(dequant_kernel<7>, grid, dim3(kDqThreads), 0, s, planes, lut_all, N, K, out); break;
-    case 8: hipLaunchKernelGGL(dequant_kernel<8>, grid, dim3(kDqThreads), 0, s, planes, lut_all, N, K, out); break;
+    case 3: hipLaunchKernelGGL(dequant_kernel<3>, grid, dim3(kDqThreads), 0, s, planes, lut_all, N, K, I_gu, out); break;
+    case 4: hipLaunchKernelGGL(dequant_kernel<4>, grid, dim3(kDqThreads), 0, s, planes, lut_all, N, K, I_gu, out); break;
+    case 5: hipLaunchKernelGGL(dequant_kernel<5>, grid, dim3(kDqThreads), 0, s, planes, lut_all, N, K, I_gu, out); break;
+    case 6: hipLaunchKernelGGL(dequant_kernel<6>, grid, dim3(kDqThreads), 0, s, planes, lut_all, N, K, I_gu, out); break;
+    case 7: hipLaunchKernelGGL(dequant_kernel<7>, grid, dim3(kDqThreads), 0, s, planes, lut_all, N, K, I_gu, out); break;
+    case 8: hipLaunchKernelGGL(dequant_kernel<8>, grid, dim3(kDqThreads), 0, s, planes, lut_all, N, K, I_gu, out); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -13,6 +13,27 @@ import numpy as np
 from . import binding
 
 
+def pack_to_device(planes: np.ndarray, module: int, device, nplanes: int = 8):
+    """Canonical planes uint32 [8][N][K/32] (host) -> the device layout the
+    kernels read (a torch int32 tensor of pw_planes_bytes(N, K, nplanes)
+    bytes), through pw_pack_planes on the GPU."""
+    import torch
+    _, N, W = planes.shape
+    canon = _to_dev(np.ascontiguousarray(planes[:nplanes]), device)
+    out = torch.empty(binding.pw_planes_bytes(N, 32 * W, nplanes) // 4, dtype=torch.int32, device=device)
+    binding.pw_pack_planes(canon, N, 32 * W, nplanes, module, out)
+    return out
+
+
+def pack_to_host(planes: np.ndarray, module: int, device) -> np.ndarray:
+    """Canonical planes -> device layout, returned as a host uint32 array of
+    the same shape (for pinned host copies the pager reloads from)."""
+    import torch
+    dev = pack_to_device(planes, module, device)
+    torch.cuda.synchronize()
+    return dev.cpu().numpy().view(np.uint32).reshape(planes.shape)
+
+
 def _to_dev(a: np.ndarray, device):
     import torch
     if a.dtype == np.uint32:
@@ -43,7 +64,7 @@ class DeviceLayer:
         self.luts = [[[None, None] for _ in range(wl.E)] for _ in range(copies)]
         for e in range(wl.E):
             for m in (0, 1):
-                self.planes[0][e][m] = _to_dev(layer.planes[e][m], device)
+                self.planes[0][e][m] = pack_to_device(layer.planes[e][m], m, device)
                 self.luts[0][e][m] = _to_dev(layer.luts[e][m], device)
         sel = set(range(wl.E)) if experts is None else set(experts)
         for c in range(1, copies):
@@ -126,7 +147,7 @@ class PagedLayer:
         self.luts = []
         for e in range(wl.E):
             for m in (0, 1):
-                src = torch.from_numpy(np.ascontiguousarray(layer.planes[e][m]).view(np.int32))
+                src = torch.from_numpy(pack_to_host(layer.planes[e][m], m, device).view(np.int32))
                 hp = torch.empty(src.shape, dtype=torch.int32, pin_memory=True)
                 hp.copy_(src)
                 self.host_planes.append(hp)

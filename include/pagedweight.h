@@ -17,14 +17,23 @@
  * with W[n][c] = LUT_{q}[n][code_q(n, c)] and code_q the value of the first q
  * planes (plane 0 = most significant bit).
  *
- * Storage format of one block with N rows and K columns (K % 32 == 0):
- *   planes : uint32 [8][N][K/32], plane-major.  Bit j (LSB = 0) of word
- *            [p][n][c] is plane p of weight (n, 32c + j).  Only planes 0..q-1
- *            are read, so a block committed at q needs only that prefix to be
- *            resident (a shorter allocation is fine).
+ * Storage of one block with N rows and K columns (K % 32 == 0, N % 16 == 0).
+ * Canonical planes (what pw_pack_planes takes): uint32 [8][N][K/32],
+ * plane-major; bit j (LSB = 0) of word [p][n][c] is plane p of weight
+ * (n, 32c + j).  The forward and pw_dequant_block read the DEVICE layout that
+ * pw_pack_planes writes from them:
+ *   planes : device layout, pw_planes_bytes(N, K, nplanes) bytes.  Planes stay
+ *            outermost and each takes N * K / 8 bytes, so a block committed at
+ *            q needs only its first q planes resident (a shorter allocation is
+ *            fine).  Inside a plane the words sit in tiles of 16 rows by 16
+ *            words, tile-row-major; inside a tile the 16 rows follow each
+ *            other, each holding the tile's words (16, or (K/32) mod 16 in the
+ *            last column tile).  Rows of a gate_up block are interleaved: tile
+ *            t holds gate rows 8t..8t+7, then up rows I+8t..I+8t+7.
  *   lut_all: fp16 bits [504 * N], the per-row tables for b = 3..8 laid one
- *            after another; the table of bitwidth b starts at element
- *            N * (2^b - 8) and is [N][2^b].  Only the table of q is read.
+ *            after another in canonical row order; the table of bitwidth b
+ *            starts at element N * (2^b - 8) and is [N][2^b].  Only the table
+ *            of q is read.
  *
  * Conventions of every entry point.
  *   - Pointers are DEVICE pointers unless the comment says host.  The caller
@@ -140,7 +149,7 @@ int32_t pw_abi_version(void);
 /* Static, never-NULL text for a status code. */
 const char* pw_status_str(pw_status status);
 
-/* Element counts of one block's storage (see the storage format above). */
+/* Element counts of one block's canonical storage (see the storage format above). */
 size_t pw_plane_words(int32_t N, int32_t K);   /* 8 * N * K / 32, 0 if invalid */
 size_t pw_lut_elems(int32_t N);                /* 504 * N                      */
 size_t pw_lut_offset(int32_t N, int32_t b);    /* N * (2^b - 8)                */
@@ -220,11 +229,32 @@ typedef struct {
 pw_status pw_moe_path_info(const pw_moe_shape* shape, int32_t T, const pw_moe_options* opts,
                            pw_path_info* info);
 
+/* Bytes of `nplanes` planes (1..8) of an N x K block in the device layout:
+ * nplanes * N * K / 8 (0 if N % 16, K % 32 or nplanes is invalid).  The
+ * bitplane packing layout of Core components 1 ("Technical summary:
+ * PagedWeight": overlaid Any-Precision bit planes with lookup tables). */
+size_t pw_planes_bytes(int32_t N, int32_t K, int32_t nplanes);
+
+/* Write planes 0..nplanes-1 of one block in the device layout the kernels read
+ * (see the storage format above): a lossless permutation of the words of the
+ * canonical planes.  module 0 (gate_up, N = 2I) interleaves gate and up rows
+ * per 16-row tile, module 1 (down) keeps the row order.
+ *   canon       device uint32 [nplanes][N][K/32] (4-byte aligned), not modified
+ *   dev_layout  device, pw_planes_bytes(N, K, nplanes) bytes, 16-byte aligned,
+ *               distinct from canon (no in-place packing); overwritten
+ * Errors: PW_ERR_INVALID_ARG (null, nplanes outside 1..8, module not 0/1,
+ * in place), PW_ERR_UNSUPPORTED_SHAPE (N % 16, K % 32), PW_ERR_ALIGNMENT.
+ * Enqueued on `stream`; one kernel. */
+pw_status pw_pack_planes(const uint32_t* canon, int32_t N, int32_t K, int32_t nplanes, int32_t module,
+                         uint32_t* dev_layout, void* stream);
+
 /* Dequantize one block at bitwidth q (host value, 3..8): w_out fp16 bits
- * [N][K] = LUT_q[n][code_q(n, c)].  The same device decode the forward uses;
- * bit-exact by definition (a table copy).  Core components 1. */
+ * [N][K] in canonical row order, = LUT_q[n][code_q(n, c)].  planes in the
+ * device layout (pw_pack_planes, same module), at least q planes.  The same
+ * device decode the forward uses; bit-exact by definition (a table copy).
+ * Core components 1.  Errors as pw_pack_planes, PW_ERR_BITWIDTH for q. */
 pw_status pw_dequant_block(const uint32_t* planes, const uint16_t* lut_all,
-                           int32_t N, int32_t K, int32_t q,
+                           int32_t N, int32_t K, int32_t q, int32_t module,
                            uint16_t* w_out, void* stream);
 
 /* Wait for `stream`, copy the workspace status word to *flags (host), then
@@ -360,7 +390,9 @@ pw_status pw_pager_create(int32_t num_blocks, const int32_t* rows /* host */, co
 pw_status pw_pager_destroy(pw_pager* pager);
 
 /* Register block b's storage before its first commit: host_planes is pinned
- * host memory holding all 8 planes [8][N][K/32]; lut_all is the device table
+ * host memory holding all 8 planes in the device layout (pw_pack_planes of the
+ * block's module, pw_planes_bytes(N, K, 8) bytes; plane p starts at byte
+ * p * N * K / 8, which is what the pager copies); lut_all is the device table
  * block [504 N] (fp16 bits, 16-byte aligned), which stays resident. */
 pw_status pw_pager_set_block(pw_pager* pager, int32_t b, const uint32_t* host_planes /* pinned host */,
                              const uint16_t* lut_all);

@@ -102,12 +102,39 @@ def test_forward_rejects_bad_arguments_before_launch(lib):
 def test_dequant_rejects_bad_arguments_before_launch(lib):
     f = lib.pw_dequant_block
     p = 1 << 20
-    assert f(None, p, 8, 32, 4, p, None) == B.PW_ERR_INVALID_ARG
-    assert f(p, p, 8, 30, 4, p, None) == B.PW_ERR_UNSUPPORTED_SHAPE
-    assert f(p, p, 8, 32, 2, p, None) == B.PW_ERR_BITWIDTH
-    assert f(p, p, 8, 32, 9, p, None) == B.PW_ERR_BITWIDTH
-    assert f(p, p + 2, 8, 32, 4, p, None) == B.PW_ERR_ALIGNMENT
-    assert f(p, p, 0, 32, 4, p, None) == B.PW_ERR_INVALID_ARG
+    assert f(None, p, 16, 32, 4, 0, p, None) == B.PW_ERR_INVALID_ARG
+    assert f(p, p, 16, 30, 4, 0, p, None) == B.PW_ERR_UNSUPPORTED_SHAPE
+    assert f(p, p, 8, 32, 4, 1, p, None) == B.PW_ERR_UNSUPPORTED_SHAPE     # rows come in 16-row tiles
+    assert f(p, p, 16, 32, 2, 0, p, None) == B.PW_ERR_BITWIDTH
+    assert f(p, p, 16, 32, 9, 1, p, None) == B.PW_ERR_BITWIDTH
+    assert f(p, p + 2, 16, 32, 4, 0, p, None) == B.PW_ERR_ALIGNMENT
+    assert f(p, p, 0, 32, 4, 0, p, None) == B.PW_ERR_INVALID_ARG
+    assert f(p, p, 16, 32, 4, 2, p, None) == B.PW_ERR_INVALID_ARG          # module 0 or 1
+
+
+def test_device_layout_sizes(lib):
+    # a plane of the device layout holds exactly the canonical plane's words
+    for N, K in [(16, 32), (2816, 2048), (2048, 1408), (28672, 4096), (4096, 14336)]:
+        for n in range(1, 9):
+            assert B.pw_planes_bytes(N, K, n) == n * N * K // 8
+    assert B.pw_planes_bytes(24, 32, 8) == 0        # N % 16
+    assert B.pw_planes_bytes(16, 48, 8) == 0        # K % 32
+    assert B.pw_planes_bytes(16, 32, 0) == 0 and B.pw_planes_bytes(16, 32, 9) == 0
+
+
+def test_pack_rejects_bad_arguments_before_launch(lib):
+    f = lib.pw_pack_planes
+    p, q = 1 << 20, 1 << 24
+    assert f(None, 16, 32, 8, 0, q, None) == B.PW_ERR_INVALID_ARG
+    assert f(p, 16, 32, 8, 0, None, None) == B.PW_ERR_INVALID_ARG
+    assert f(p, 16, 32, 0, 0, q, None) == B.PW_ERR_INVALID_ARG
+    assert f(p, 16, 32, 9, 0, q, None) == B.PW_ERR_INVALID_ARG
+    assert f(p, 16, 32, 8, 3, q, None) == B.PW_ERR_INVALID_ARG
+    assert f(p, 16, 32, 8, 1, p, None) == B.PW_ERR_INVALID_ARG              # not in place
+    assert f(p, 24, 32, 8, 1, q, None) == B.PW_ERR_UNSUPPORTED_SHAPE
+    assert f(p, 16, 40, 8, 1, q, None) == B.PW_ERR_UNSUPPORTED_SHAPE
+    assert f(p + 2, 16, 32, 8, 1, q, None) == B.PW_ERR_ALIGNMENT
+    assert f(p, 16, 32, 8, 1, q + 4, None) == B.PW_ERR_ALIGNMENT
 
 
 def test_status_and_init_reject_bad_arguments(lib):

@@ -78,25 +78,36 @@ def run_forward(torch, L, path=B.PW_PATH_AUTO, mfma_min_tokens=0, dev=None):
 # ---------------------------------------------------------------------------
 # dequantization: bit-exact
 # ---------------------------------------------------------------------------
-def _dequant_check(torch, planes, lut, q, what):
+def _pack(torch, planes, module, nplanes=8):
+    """Canonical planes -> device layout on the GPU (pw_pack_planes)."""
+    N, W = planes.shape[1], planes.shape[2]
+    src = torch.from_numpy(np.ascontiguousarray(planes[:nplanes]).view(np.int32)).cuda()
+    out = torch.empty(B.pw_planes_bytes(N, 32 * W, nplanes) // 4, dtype=torch.int32, device="cuda")
+    B.pw_pack_planes(src, N, 32 * W, nplanes, module, out)
+    return out
+
+
+def _dequant_checks(torch, planes, lut, module, what, qs=range(3, 9)):
+    """Pack the canonical planes, dequantize on the GPU at each q, compare bit
+    for bit with the oracle's dequantization of the canonical planes."""
     N, K = planes.shape[1], planes.shape[2] * 32
-    say(f"dequant {what} N={N} K={K} q={q}")
-    p = torch.from_numpy(planes.view(np.int32)).cuda()
+    p = _pack(torch, planes, module)
     l = torch.from_numpy(lut.view(np.int16)).cuda()
     out = torch.empty((N, K), dtype=torch.int16, device="cuda")
-    B.pw_dequant_block(p, l, N, K, q, out)
-    torch.cuda.synchronize()
-    got = out.cpu().numpy().view(np.uint16)
-    ref = orc.dequant_block(planes, lut, q)
-    assert np.array_equal(got, ref), f"{what} q={q}: {np.count_nonzero(got != ref)} mismatches"
+    for q in qs:
+        say(f"dequant {what} N={N} K={K} module={module} q={q}")
+        B.pw_dequant_block(p, l, N, K, q, out, module=module)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().view(np.uint16)
+        ref = orc.dequant_block(planes, lut, q)
+        assert np.array_equal(got, ref), f"{what} q={q}: {np.count_nonzero(got != ref)} mismatches"
 
 
 def test_dequant_bit_exact_tiny_all_blocks(torch):
     L = layer_for("tiny", routed_only=False)
     for e in range(L.wl.E):
         for m in (0, 1):
-            for q in range(3, 9):
-                _dequant_check(torch, L.planes[e][m], L.luts[e][m], q, f"tiny e{e} m{m}")
+            _dequant_checks(torch, L.planes[e][m], L.luts[e][m], m, f"tiny e{e} m{m}")
 
 
 @pytest.mark.parametrize("group", range(6))
@@ -109,8 +120,7 @@ def test_dequant_bit_exact_qwen_every_block(torch, group):
             N, K = wl.block_shape(m)
             planes = synth.draw_planes(wl.seed, e, m, N, K)
             lut = synth.draw_lut(wl.seed, e, m, N)
-            for q in range(3, 9):
-                _dequant_check(torch, planes, lut, q, f"qwen e{e} m{m}")
+            _dequant_checks(torch, planes, lut, m, f"qwen e{e} m{m}")
 
 
 @pytest.mark.parametrize("m", [0, 1])
@@ -121,17 +131,53 @@ def test_dequant_bit_exact_mixtral_full_block(torch, m):
     N, K = wl.block_shape(m)
     planes = synth.draw_planes(wl.seed, 5, m, N, K)
     lut = synth.draw_lut(wl.seed, 5, m, N)
-    for q in range(3, 9):
-        _dequant_check(torch, planes, lut, q, f"mixtral e5 m{m}")
+    _dequant_checks(torch, planes, lut, m, f"mixtral e5 m{m}")
 
 
 def test_dequant_ragged_shapes(torch):
+    # K/32 below one 16-word tile, not a multiple of 16 (a narrower last column
+    # tile: 44 and 65 words), not a multiple of 4; both row orders
     rng = np.random.default_rng(11)
-    for N, K in [(1, 32), (7, 96), (13, 2080), (33, 4128)]:
+    for N, K in [(16, 32), (32, 96), (48, 2080), (32, 4128), (64, 1408), (16, 544)]:
         planes = rng.integers(0, 2 ** 32, (8, N, K // 32), dtype=np.uint32)
         lut = synth.draw_lut(5, 0, 0, N)
-        for q in (3, 5, 8):
-            _dequant_check(torch, planes, lut, q, f"ragged")
+        for m in (0, 1):
+            _dequant_checks(torch, planes, lut, m, "ragged", qs=(3, 5, 8))
+
+
+def _layout_ref(canon, module):
+    """The device layout written out element by element from its definition
+    (16-row x 16-word tiles, tile-row-major, rows inside a tile, the last
+    column tile W mod 16 wide; gate_up rows interleaved 8 gate / 8 up)."""
+    P, N, W = canon.shape
+    I = N // 2
+    d = np.arange(N)[:, None]
+    c = np.arange(W)[None, :]
+    n_of_d = np.where((d & 15) < 8, 8 * (d >> 4) + (d & 15), I + 8 * (d >> 4) + (d & 15) - 8) if module == 0 else d
+    width = np.minimum(16, W - (c & ~15))
+    off = (d >> 4) * 16 * W + (c >> 4) * 256 + (d & 15) * width + (c & 15)
+    out = np.zeros(P * N * W, dtype=np.uint32)
+    for p in range(P):
+        out[p * N * W + off] = canon[p][np.broadcast_to(n_of_d, off.shape), np.broadcast_to(c, off.shape)]
+    return out
+
+
+@pytest.mark.parametrize("module", [0, 1])
+def test_pack_planes_layout(torch, module):
+    """pw_pack_planes writes every word where the layout puts it (bit-exact),
+    for full and partial column tiles and plane counts below 8; the result is
+    a permutation of the input words."""
+    rng = np.random.default_rng(12 + module)
+    for N, K, nplanes in [(16, 32, 8), (32, 96, 3), (48, 1408, 8), (64, 2080, 5), (2816, 2048, 8), (256, 512, 6)]:
+        say(f"pack N={N} K={K} nplanes={nplanes} module={module}")
+        canon = rng.integers(0, 2 ** 32, (8, N, K // 32), dtype=np.uint32)
+        assert B.pw_planes_bytes(N, K, nplanes) == nplanes * N * K // 8
+        got = _pack(torch, canon, module, nplanes)
+        torch.cuda.synchronize()
+        got = got.cpu().numpy().view(np.uint32)
+        ref = _layout_ref(canon[:nplanes], module)
+        assert np.array_equal(got, ref)
+        assert np.array_equal(np.sort(got), np.sort(canon[:nplanes].reshape(-1)))
 
 
 # ---------------------------------------------------------------------------
