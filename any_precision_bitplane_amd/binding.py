@@ -122,6 +122,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "pw_moe_forward_routed": (c_int32, [POINTER(PwMoeShape), c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                             c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                             POINTER(PwMoeOptions), c_void_p]),
+        "pw_moe_forward_layers": (c_int32, [POINTER(PwMoeShape), c_int32, c_int32, c_void_p, c_void_p, c_void_p,
+                                            c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                            POINTER(PwMoeOptions), c_void_p]),
         "pw_plan_bitwidths": (c_int32, [POINTER(PwPlanProblem), c_void_p, ctypes.c_int64, c_void_p,
                                         POINTER(ctypes.c_int64), POINTER(c_int32)]),
         "pw_pager_create": (c_int32, [c_int32, POINTER(c_int32), POINTER(c_int32), c_void_p, c_size_t, c_void_p,
@@ -148,7 +151,8 @@ def exported_symbols() -> Sequence[str]:
             "pw_moe_path_info",
             "pw_dequant_block", "pw_planes_bytes", "pw_pack_planes", "pw_get_device_status", "pw_pager_create", "pw_pager_destroy",
             "pw_pager_set_block", "pw_pager_request", "pw_pager_execute", "pw_pager_commit", "pw_pager_info",
-            "pw_pager_arena_used", "pw_router_topk", "pw_moe_forward_routed", "pw_plan_bitwidths"]
+            "pw_pager_arena_used", "pw_router_topk", "pw_moe_forward_routed", "pw_moe_forward_layers",
+            "pw_plan_bitwidths"]
 
 
 # ---------------------------------------------------------------------------
@@ -301,6 +305,20 @@ def pw_moe_forward_routed(shp: PwMoeShape, T: int, x, router_w, blocks, q, y, st
                                       ctypes.byref(opts) if opts is not None else None, _stream(stream))
     if check:
         _check(st, "pw_moe_forward_routed")
+    return st
+
+
+def pw_moe_forward_layers(shp: PwMoeShape, T: int, x, router_ws, blocks, qs, y, stat_count, stat_mass, workspace,
+                          opts: Optional[PwMoeOptions] = None, stream=None, check: bool = True) -> int:
+    """router_ws, blocks, qs: sequences of device tensors, one per layer."""
+    L = len(router_ws)
+    arr = lambda ts: (c_void_p * L)(*[_ptr(t) for t in ts])
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = load().pw_moe_forward_layers(ctypes.byref(shp), L, T, _ptr(x), arr(router_ws), arr(blocks), arr(qs), _ptr(y),
+                                      _ptr(stat_count), _ptr(stat_mass), _ptr(workspace), ws_bytes,
+                                      ctypes.byref(opts) if opts is not None else None, _stream(stream))
+    if check:
+        _check(st, "pw_moe_forward_layers")
     return st
 
 

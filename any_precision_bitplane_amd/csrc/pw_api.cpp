@@ -122,7 +122,7 @@ pw_status check_forward_args(const pw_moe_shape* shape, int32_t T, const uint16_
 
 pw_status forward_on(const pw_moe_shape* shape, int32_t T, const uint16_t* x, const int32_t* ids, const float* w,
                      const pw_block_desc* blocks, const uint8_t* q, uint16_t* y, uint8_t* ws, uint32_t* status,
-                     const pw_moe_options* opts, hipStream_t s) {
+                     const pw_moe_options* opts, hipStream_t s, bool combine) {
   const int H = shape->hidden, I = shape->inter, E = shape->num_experts, k = shape->top_k;
   const WsLayout L = ws_layout(H, I, E, k, T);
   Plan pl;
@@ -202,7 +202,7 @@ pw_status forward_on(const pw_moe_shape* shape, int32_t T, const uint16_t* x, co
     }
   }
   if (e == hipSuccess) e = mark(PW_STAGE_COMBINE);
-  if (e == hipSuccess) e = launch_combine(o, w, rt.inv, T, k, H, g.kparts, y, s);
+  if (e == hipSuccess && combine) e = launch_combine(o, w, rt.inv, T, k, H, g.kparts, y, s);
   if (e == hipSuccess) e = mark(PW_NUM_STAGES);
   if (e == hipErrorNotSupported) return PW_ERR_UNSUPPORTED;
   return hip_status(e);
@@ -280,8 +280,7 @@ pw_status pw_router_topk(const pw_moe_shape* shape, int32_t T, const uint16_t* x
     return PW_ERR_ALIGNMENT;
   const WsLayout L = ws_layout(shape->hidden, shape->inter, shape->num_experts, shape->top_k, T);
   if (workspace_bytes < L.total) return PW_ERR_WORKSPACE;
-  float* logits = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + L.rlogits);
-  return hip_status(launch_router(x, router_w, T, shape->hidden, shape->num_experts, shape->top_k, logits, ids, w,
+  return hip_status(launch_router(x, router_w, T, shape->hidden, shape->num_experts, shape->top_k, ids, w,
                                   stat_count, stat_mass, (hipStream_t)stream));
 }
 
@@ -345,6 +344,55 @@ pw_status pw_pack_planes(const uint32_t* canon, int32_t N, int32_t K, int32_t np
   if (!aligned(canon, 4) || !aligned(dev_layout, 16)) return PW_ERR_ALIGNMENT;
   if ((const void*)canon == (const void*)dev_layout) return PW_ERR_INVALID_ARG;   // not in place
   return hip_status(launch_pack(canon, N, K, nplanes, module, dev_layout, (hipStream_t)stream));
+}
+
+pw_status pw_moe_forward_layers(const pw_moe_shape* shape, int32_t L, int32_t T, const uint16_t* x,
+                                const uint16_t* const* router_w, const pw_block_desc* const* blocks,
+                                const uint8_t* const* q, uint16_t* y, uint32_t* stat_count, float* stat_mass,
+                                void* workspace, size_t workspace_bytes, const pw_moe_options* opts, void* stream) {
+  pw_status st = check_shape(shape, T);
+  if (st != PW_OK) return st;
+  if (L < 1 || !router_w || !blocks || !q) return PW_ERR_INVALID_ARG;
+  if (shape->top_k > kMaxRouterTopK || shape->hidden > kMaxRouterHidden) return PW_ERR_UNSUPPORTED_SHAPE;
+  if (opts && opts->stage_events[0]) return PW_ERR_UNSUPPORTED;   // events time one layer
+  for (int l = 0; l < L; ++l) {
+    if (!router_w[l] || !blocks[l] || !q[l]) return PW_ERR_INVALID_ARG;
+    if (!aligned(router_w[l], 16) || !aligned(blocks[l], 8)) return PW_ERR_ALIGNMENT;
+  }
+  if (!aligned(stat_count, 4) || !aligned(stat_mass, 4)) return PW_ERR_ALIGNMENT;
+  // the forward's checks, with stand-ins for the ids / weights the routers write
+  st = check_forward_args(shape, T, x, reinterpret_cast<const int32_t*>(workspace),
+                          reinterpret_cast<const float*>(workspace), blocks[0], q[0], y, opts);
+  if (st != PW_OK || T == 0) return st;
+  if (!workspace) return PW_ERR_INVALID_ARG;
+  if (!aligned(workspace, kAlign)) return PW_ERR_ALIGNMENT;
+  const int H = shape->hidden, I = shape->inter, E = shape->num_experts, k = shape->top_k;
+  const WsLayout W = ws_layout(H, I, E, k, T);
+  if (workspace_bytes < W.total) return PW_ERR_WORKSPACE;
+  Plan pl;
+  st = make_plan(shape, T, opts, pl);
+  if (st != PW_OK) return st;
+
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  int32_t* ids = reinterpret_cast<int32_t*>(ws + W.rids);
+  float* w = reinterpret_cast<float*>(ws + W.rw);
+  const float* o = reinterpret_cast<const float*>(ws + W.o);
+  const int32_t* inv = reinterpret_cast<const int32_t*>(ws + W.inv);
+  uint16_t* xl[2] = {reinterpret_cast<uint16_t*>(ws + W.xl), reinterpret_cast<uint16_t*>(ws + W.xl) + (size_t)T * H};
+  hipStream_t s = (hipStream_t)stream;
+  auto cnt = [&](int l) { return stat_count ? stat_count + (size_t)l * E : nullptr; };
+  auto mss = [&](int l) { return stat_mass ? stat_mass + (size_t)l * E : nullptr; };
+
+  hipError_t e = launch_router(x, router_w[0], T, H, E, k, ids, w, cnt(0), mss(0), s);
+  if (e != hipSuccess) return PW_ERR_HIP;
+  st = forward_on(shape, T, x, ids, w, blocks[0], q[0], y, ws, nullptr, opts, s, L == 1);
+  for (int l = 1; l < L && st == PW_OK; ++l) {
+    uint16_t* xin = xl[(l - 1) & 1];
+    e = launch_combine_router(o, w, inv, pl.kparts, xin, router_w[l], T, H, E, k, ids, w, cnt(l), mss(l), s);
+    if (e != hipSuccess) return PW_ERR_HIP;
+    st = forward_on(shape, T, xin, ids, w, blocks[l], q[l], y, ws, nullptr, opts, s, l == L - 1);
+  }
+  return st;
 }
 
 pw_status pw_dequant_block(const uint32_t* planes, const uint16_t* lut_all, int32_t N, int32_t K, int32_t q,

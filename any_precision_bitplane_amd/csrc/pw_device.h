@@ -214,6 +214,41 @@ __device__ __forceinline__ half2_t lookup_pair(const uint32_t (&R)[8], uint32_t 
   return __builtin_bit_cast(half2_t, lo | (hi << 16));
 }
 
+// Row tables kept at a 256-byte LDS stride (512 for q = 8): for q <= 7 the
+// field byte is 2 * code, so an entry's address is the table base with its
+// low byte replaced by the field (one v_perm_b32); for q = 8 the field is the
+// code and the address is base + 2 * code.
+template <int Q>
+constexpr int kTabStride = Q == 8 ? 512 : 256;
+
+template <int Q>
+__device__ __forceinline__ uint32_t tab_entry(const uint32_t (&R)[8], uint32_t base, int j) {
+  const uint32_t f = R[j & 7];
+  const int b = j >> 3;
+  if constexpr (Q == 8) return base + (((f >> (8 * b)) & 0xFFu) << 1);
+  else return __builtin_amdgcn_perm(base, f, 0x07060500u | (uint32_t)b);
+}
+
+// The 32 weights of one group (fields R, row table at `base`, kTabStride
+// aligned) as 16 packed fp16 pairs: pair p = weights (2p, 2p + 1).  The
+// lookups go out in batches of eight (one sub-step's weights 8b .. 8b + 7)
+// ahead of the packing, so the wave waits on LDS about once per batch.
+template <int Q>
+__device__ __forceinline__ void decode_group(const uint32_t (&R)[8], uint32_t base, uint32_t (&packed)[16]) {
+  uint32_t v[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) v[j] = lds_u16_at(tab_entry<Q>(R, base, j));
+#pragma unroll
+  for (int p = 0; p < 16; ++p) packed[p] = v[2 * p] | (v[2 * p + 1] << 16);
+  constexpr int kValu = 0x002, kDsRead = 0x100;
+  constexpr int kAddrOps = Q == 8 ? 2 : 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kValu, 8 * kAddrOps, 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 8, 0);
+  }
+}
+
 // Decode of one row's 32-weight group into 16 fp16 pairs.
 template <int Q, int J>
 struct GroupDecode {
@@ -240,6 +275,57 @@ __device__ __forceinline__ uint32_t buf_load_u32(__amdgpu_buffer_rsrc_t r, uint3
 constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset that reads as zero
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+
+// Weighted top-k combine of token t at hidden positions n .. n+3:
+// sum over j < k, ascending, of w[t][j] * o[t k + j][n ..] (each o row the sum
+// of its K parts), fp32 fused multiply-adds; dropped slots (inv < 0) add
+// nothing.  Every loaded value of a group of eight slots is requested before
+// any is used.  The one definition every kernel that combines uses, so their
+// results agree bit for bit.
+__device__ __forceinline__ floatx4 combine4(const float* __restrict__ o, const float* __restrict__ w,
+                                            const int32_t* __restrict__ inv, int t, int k, int H, int kparts,
+                                            size_t part_stride, int n) {
+  constexpr int G = 8;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  for (int j0 = 0; j0 < k; j0 += G) {
+    bool ok[G];
+    float wj[G];
+    floatx4 v[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int j = j0 + i;
+      ok[i] = false;
+      wj[i] = 0.f;
+      v[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (j < k) {
+        const size_t slot = (size_t)t * k + j;
+        ok[i] = inv[slot] >= 0;
+        wj[i] = w[slot];
+        v[i] = *reinterpret_cast<const floatx4*>(o + slot * H + n);
+        for (int kp = 1; kp < kparts; ++kp)
+          v[i] += *reinterpret_cast<const floatx4*>(o + kp * part_stride + slot * H + n);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (!ok[i]) continue;
+      a0 = __builtin_fmaf(wj[i], v[i][0], a0);
+      a1 = __builtin_fmaf(wj[i], v[i][1], a1);
+      a2 = __builtin_fmaf(wj[i], v[i][2], a2);
+      a3 = __builtin_fmaf(wj[i], v[i][3], a3);
+    }
+  }
+  return floatx4{a0, a1, a2, a3};
+}
+
+// Four fp32 values rounded to fp16 (nearest even), packed little-endian.
+__device__ __forceinline__ uint2 pack_half4(floatx4 a) {
+  const _Float16 h0 = (_Float16)a[0], h1 = (_Float16)a[1], h2 = (_Float16)a[2], h3 = (_Float16)a[3];
+  uint2 p;
+  p.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+  p.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+  return p;
+}
 
 // Values the kernels load from memory at a wave-uniform address are the same
 // in every lane, but the compiler cannot always prove it (it must use a vector

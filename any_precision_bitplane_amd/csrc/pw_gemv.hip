@@ -166,14 +166,8 @@ __device__ __forceinline__ int wave_excl_scan(int v) {
 // base + 2*code.
 // ---------------------------------------------------------------------------
 template <int Q>
-constexpr int kTabStride = Q == 8 ? 512 : 256;
-
-template <int Q>
 __device__ __forceinline__ uint32_t row_entry(const uint32_t (&R)[8], uint32_t base, int j) {
-  const uint32_t f = R[j & 7];
-  const int b = j >> 3;
-  if constexpr (Q == 8) return base + (((f >> (8 * b)) & 0xFFu) << 1);
-  else return __builtin_amdgcn_perm(base, f, 0x07060500u | (uint32_t)b);
+  return tab_entry<Q>(R, base, j);
 }
 
 // acc[t] += sum_j W[j] * x[t][j] over the row's 32 weights.  The 32 lookups

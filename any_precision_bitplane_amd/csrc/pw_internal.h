@@ -19,6 +19,7 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 constexpr int kMfmaTileM = 256;   // tokens per MFMA tile
 constexpr int kMaxRouterTopK = 64; // the router's top-k kernel keeps slot j in lane j
+constexpr int kMaxRouterHidden = 16384;   // a multi-layer call's router keeps one token's x in LDS
 
 inline int mtile_bound(int E, int T, int k) {
   const int slots = T * k;
@@ -61,7 +62,7 @@ struct WsLayout {
   size_t mgtiles = 0;       // int32 [2 * mgtile_bound] matrix-core GEMV token tiles
   size_t h = 0;             // fp16  [T*k][I] activations between the products
   size_t o = 0;             // fp32  [kparts][T*k][H] expert outputs by slot (t*k + j), before the combine
-  size_t rlogits = 0;       // fp32  [T][E]   router logits
+  size_t xl = 0;            // fp16  [2][T][H] layer inputs of a multi-layer call (ping-pong)
   size_t rids = 0;          // int32 [T*k]    router expert ids (routed forward)
   size_t rw = 0;            // fp32  [T*k]    router weights (routed forward)
   size_t adesc = 0;         // ActiveDesc [E] down-product work descriptors (calls routed inside gate_up)
@@ -82,7 +83,7 @@ inline WsLayout ws_layout(int H, int I, int E, int k, int T) {
   L.mgtiles = off; off = align_up(off + sizeof(int32_t) * 2 * mgtile_bound(E, T, k), kAlign);
   L.h = off;       off = align_up(off + sizeof(uint16_t) * slots * I, kAlign);
   L.o = off;       off = align_up(off + sizeof(float) * kp * slots * H, kAlign);
-  L.rlogits = off; off = align_up(off + sizeof(float) * (size_t)T * E, kAlign);
+  L.xl = off;      off = align_up(off + sizeof(uint16_t) * 2 * (size_t)T * H, kAlign);
   L.rids = off;    off = align_up(off + sizeof(int32_t) * slots, kAlign);
   L.rw = off;      off = align_up(off + sizeof(float) * slots, kAlign);
   L.adesc = off;   off = align_up(off + 32 * (size_t)E, kAlign);
@@ -177,8 +178,13 @@ hipError_t launch_dequant(const uint32_t* planes, const uint16_t* lut_all, int N
                           uint16_t* out, hipStream_t s);
 hipError_t launch_pack(const uint32_t* canon, int N, int K, int nplanes, int module, uint32_t* out, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
-hipError_t launch_router(const uint16_t* x, const uint16_t* wr, int T, int H, int E, int k, float* logits,
-                         int32_t* ids, float* w, uint32_t* count, float* mass, hipStream_t s);
+hipError_t launch_router(const uint16_t* x, const uint16_t* wr, int T, int H, int E, int k, int32_t* ids, float* w,
+                         uint32_t* count, float* mass, hipStream_t s);
+// The previous layer's weighted combine (o, w_prev, inv, kparts as the
+// combine kernel takes them) written to x_out, then the router on it.
+hipError_t launch_combine_router(const float* o, const float* w_prev, const int32_t* inv, int kparts,
+                                 uint16_t* x_out, const uint16_t* wr, int T, int H, int E, int k, int32_t* ids,
+                                 float* w, uint32_t* count, float* mass, hipStream_t s);
 hipError_t launch_status_clear(uint32_t* status, hipStream_t s);
 
 // The fused layer on a caller-provided scratch area (the workspace, or the
@@ -187,7 +193,7 @@ hipError_t launch_status_clear(uint32_t* status, hipStream_t s);
 // are raised.  Arguments are checked by the caller.
 pw_status forward_on(const pw_moe_shape* shape, int32_t T, const uint16_t* x, const int32_t* ids, const float* w,
                      const pw_block_desc* blocks, const uint8_t* q, uint16_t* y, uint8_t* scratch,
-                     uint32_t* status, const pw_moe_options* opts, hipStream_t s);
+                     uint32_t* status, const pw_moe_options* opts, hipStream_t s, bool combine = true);
 
 // Host checks shared by the forward entry points (everything but the scratch).
 pw_status check_forward_args(const pw_moe_shape* shape, int32_t T, const uint16_t* x, const int32_t* ids,

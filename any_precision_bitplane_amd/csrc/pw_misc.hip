@@ -8,11 +8,9 @@ namespace pw {
 // is indexed by slot and is the sum of its K parts (the down product may split
 // K across waves).  The router weights are used as given; a slot the routing
 // dropped (expert id out of range) has inv = -1 and adds nothing (its o row is
-// never written).  Every load of a group of up to eight slots is issued before
-// any is used, so a call waits for one memory round trip per group.  Fixed j
-// order and no atomics, so the result is deterministic.
+// never written).  Fixed j order and no atomics, so the result is
+// deterministic (combine4 in pw_device.h).
 constexpr int kCombineThreads = 256;
-constexpr int kCombineGroup = 8;
 
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ o,
                                                                   const float* __restrict__ w,
@@ -22,40 +20,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
   const int t = blockIdx.y;
   const int n = (blockIdx.x * kCombineThreads + threadIdx.x) * 4;
   if (n >= H) return;
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  for (int j0 = 0; j0 < k; j0 += kCombineGroup) {
-    bool ok[kCombineGroup];
-    float wj[kCombineGroup];
-    floatx4 v[kCombineGroup];
-#pragma unroll
-    for (int i = 0; i < kCombineGroup; ++i) {
-      const int j = j0 + i;
-      ok[i] = false;
-      wj[i] = 0.f;
-      v[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (j < k) {
-        const size_t slot = (size_t)t * k + j;
-        ok[i] = inv[slot] >= 0;
-        wj[i] = w[slot];
-        v[i] = *reinterpret_cast<const floatx4*>(o + slot * H + n);
-        for (int kp = 1; kp < kparts; ++kp)
-          v[i] += *reinterpret_cast<const floatx4*>(o + kp * part_stride + slot * H + n);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kCombineGroup; ++i) {
-      if (!ok[i]) continue;
-      a0 = __builtin_fmaf(wj[i], v[i][0], a0);
-      a1 = __builtin_fmaf(wj[i], v[i][1], a1);
-      a2 = __builtin_fmaf(wj[i], v[i][2], a2);
-      a3 = __builtin_fmaf(wj[i], v[i][3], a3);
-    }
-  }
-  const _Float16 h0 = (_Float16)a0, h1 = (_Float16)a1, h2 = (_Float16)a2, h3 = (_Float16)a3;
-  uint2 packed;
-  packed.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-  packed.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
-  *reinterpret_cast<uint2*>(y + (size_t)t * H + n) = packed;
+  const floatx4 a = combine4(o, w, inv, t, k, H, kparts, part_stride, n);
+  *reinterpret_cast<uint2*>(y + (size_t)t * H + n) = pack_half4(a);
 }
 
 hipError_t launch_combine(const float* o, const float* w, const int32_t* inv, int T, int k, int H, int kparts,

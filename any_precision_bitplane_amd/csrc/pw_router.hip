@@ -7,17 +7,17 @@
 // logits in descending order (lower expert id first on equal logits), weights
 // = softmax over the selected logits.
 //
-// Two launches (a single-workgroup variant for decode batches, logits in LDS,
-// took 17.6 us instead of 9.2 on the Qwen-shaped decode layer: its 32 serial
-// wave sums cost more than the second launch):
-//   logits_kernel  one wave per (expert, tile of 4 tokens): lanes stride over H
-//                  in 8-element chunks, fp16 pairs multiplied into fp32 with
-//                  v_dot2, one butterfly sum per token; logits fp32 [T][E].
-//   topk_kernel    one wave per token: k rounds of a wave-wide (value desc,
-//                  id asc) butterfly arg-max; lane j keeps slot j; softmax
-//                  with the device exp; lane j writes slot j and adds it to
-//                  the routing statistics (count exact, mass an fp32 atomic
-//                  sum whose order varies between runs).
+// One launch: a workgroup of four waves takes TT tokens (1 for batches of up
+// to 256 tokens, 4 above, so larger batches share each router row read), the
+// waves split the experts, each wave's lanes stride over H in 8-element chunks
+// (fp16 pairs multiplied into fp32 with v_dot2, one butterfly sum per token
+// and expert), and the logits meet in LDS; then wave t selects the top-k of
+// token t: k rounds of a wave-wide (value desc, id asc) butterfly arg-max, lane
+// j keeping slot j, softmax with the device exp, lane j writing slot j and its
+// statistics (count exact, mass an fp32 atomic sum whose order varies between
+// runs).  An earlier form used two launches (logits, then top-k through global
+// memory); on the Qwen-shaped decode layer the second launch and its gap cost
+// about as much as the work.
 #include <limits.h>
 
 #include "pw_device.h"
@@ -25,45 +25,13 @@
 
 namespace pw {
 
-constexpr int kRouterTokens = 4;     // tokens per wave in the logits kernel
-constexpr int kRouterWaves = 4;      // waves per workgroup (both kernels)
+constexpr int kRouterTokens = 4;     // tokens per workgroup for batches above 256 tokens
+constexpr int kRouterWaves = 16;     // waves per workgroup
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
   return v;
-}
-
-__global__ __launch_bounds__(kRouterWaves * kWave) void logits_kernel(const uint16_t* __restrict__ x,
-                                                                       const uint16_t* __restrict__ wr, int T, int H,
-                                                                       int E, float* __restrict__ logits) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int e = blockIdx.y * kRouterWaves + (int)(threadIdx.x / kWave);
-  const int t0 = blockIdx.x * kRouterTokens;
-  if (e >= E) return;
-  const int nt = T - t0 < kRouterTokens ? T - t0 : kRouterTokens;
-  float acc[kRouterTokens];
-#pragma unroll
-  for (int t = 0; t < kRouterTokens; ++t) acc[t] = 0.f;
-  const uint16_t* wrow = wr + (size_t)e * H;
-  for (int h = lane * 8; h < H; h += kWave * 8) {
-    const half8_t wv = *reinterpret_cast<const half8_t*>(wrow + h);
-#pragma unroll
-    for (int t = 0; t < kRouterTokens; ++t) {
-      if (t >= nt) continue;
-      const half8_t xv = *reinterpret_cast<const half8_t*>(x + (size_t)(t0 + t) * H + h);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[t] = __builtin_amdgcn_fdot2(half2_t{wv[2 * i], wv[2 * i + 1]}, half2_t{xv[2 * i], xv[2 * i + 1]}, acc[t],
-                                        false);
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < kRouterTokens; ++t) {
-    if (t >= nt) continue;
-    const float s = wave_sum(acc[t]);
-    if (lane == 0) logits[(size_t)(t0 + t) * E + e] = s;
-  }
 }
 
 // Selection and softmax of token t from its logits l[e] (e < E; lane owns
@@ -123,25 +91,134 @@ __device__ __forceinline__ void select_topk(const float* l, int E, int k, int t,
   }
 }
 
-// One wave per token over logits fp32 [T][E] in global memory.
-__global__ __launch_bounds__(kRouterWaves * kWave) void topk_kernel(const float* __restrict__ logits, int T, int E,
-                                                                     int k, int32_t* __restrict__ ids,
-                                                                     float* __restrict__ w,
-                                                                     uint32_t* __restrict__ count,
-                                                                     float* __restrict__ mass) {
-  const int t = blockIdx.x * kRouterWaves + (int)(threadIdx.x / kWave);
-  if (t >= T) return;
-  select_topk(logits + (size_t)t * E, E, k, t, ids, w, count, mass);
+// Logits of the tile's tokens from x rows (global memory, or LDS), into lg.
+// Wave w takes experts w, w + 16, w + 32, ... in groups of four whose router
+// rows are read together, lanes striding over H in 8-element chunks; the
+// four experts' (and TT tokens') butterfly sums run as independent chains.
+constexpr int kRtGroup = 4;
+template <int TT>
+__device__ __forceinline__ void router_logits(const uint16_t* x, size_t x_stride, const uint16_t* __restrict__ wr,
+                                              int nt, int H, int E, float (&lg)[TT][kMaxExperts]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  for (int e0 = wave; e0 < E; e0 += kRouterWaves * kRtGroup) {
+    float acc[kRtGroup][TT];
+#pragma unroll
+    for (int g = 0; g < kRtGroup; ++g)
+#pragma unroll
+      for (int t = 0; t < TT; ++t) acc[g][t] = 0.f;
+    // U 512-element chunks per pass, every load of a pass issued before any
+    // arithmetic (one memory round trip per pass instead of one per chunk)
+    constexpr int U = 4 / TT;
+    for (int hb = 0; hb < H; hb += U * kWave * 8) {
+      half8_t xv[U][TT], wv[U][kRtGroup];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int h = hb + u * kWave * 8 + lane * 8;
+        if (h >= H) continue;
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+          if (t < nt) xv[u][t] = *reinterpret_cast<const half8_t*>(x + (size_t)t * x_stride + h);
+#pragma unroll
+        for (int g = 0; g < kRtGroup; ++g) {
+          const int e = e0 + g * kRouterWaves;
+          if (e < E) wv[u][g] = *reinterpret_cast<const half8_t*>(wr + (size_t)e * H + h);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int h = hb + u * kWave * 8 + lane * 8;
+        if (h >= H) continue;
+#pragma unroll
+        for (int g = 0; g < kRtGroup; ++g) {
+          if (e0 + g * kRouterWaves >= E) continue;
+#pragma unroll
+          for (int t = 0; t < TT; ++t) {
+            if (t >= nt) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[g][t] = __builtin_amdgcn_fdot2(half2_t{wv[u][g][2 * i], wv[u][g][2 * i + 1]},
+                                                 half2_t{xv[u][t][2 * i], xv[u][t][2 * i + 1]}, acc[g][t], false);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+      for (int g = 0; g < kRtGroup; ++g)
+#pragma unroll
+        for (int t = 0; t < TT; ++t) acc[g][t] += __shfl_xor(acc[g][t], off, kWave);
+    if (lane == 0) {
+#pragma unroll
+      for (int g = 0; g < kRtGroup; ++g) {
+        const int e = e0 + g * kRouterWaves;
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+          if (e < E && t < nt) lg[t][e] = acc[g][t];
+      }
+    }
+  }
 }
 
-hipError_t launch_router(const uint16_t* x, const uint16_t* wr, int T, int H, int E, int k, float* logits,
-                         int32_t* ids, float* w, uint32_t* count, float* mass, hipStream_t s) {
-  dim3 g1((T + kRouterTokens - 1) / kRouterTokens, (E + kRouterWaves - 1) / kRouterWaves);
-  hipLaunchKernelGGL(logits_kernel, g1, dim3(kRouterWaves * kWave), 0, s, x, wr, T, H, E, logits);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  dim3 g2((T + kRouterWaves - 1) / kRouterWaves);
-  hipLaunchKernelGGL(topk_kernel, g2, dim3(kRouterWaves * kWave), 0, s, logits, T, E, k, ids, w, count, mass);
+template <int TT>
+__global__ __launch_bounds__(kRouterWaves * kWave) void router_kernel(const uint16_t* __restrict__ x,
+                                                                       const uint16_t* __restrict__ wr, int T, int H,
+                                                                       int E, int k, int32_t* __restrict__ ids,
+                                                                       float* __restrict__ w,
+                                                                       uint32_t* __restrict__ count,
+                                                                       float* __restrict__ mass) {
+  __shared__ float lg[TT][kMaxExperts];
+  const int wave = threadIdx.x / kWave;
+  const int t0 = blockIdx.x * TT;
+  const int nt = T - t0 < TT ? T - t0 : TT;
+  router_logits<TT>(x + (size_t)t0 * H, (size_t)H, wr, nt, H, E, lg);
+  __syncthreads();
+  if (wave < nt) select_topk(lg[wave], E, k, t0 + wave, ids, w, count, mass);
+}
+
+// Layer boundary of a multi-layer call: token t's weighted combine of the
+// previous layer (the combine kernel's arithmetic, combine4) is written to
+// x_out and kept in LDS, then routed for the next layer.  w may alias w_prev:
+// every read of w_prev precedes the barrier, every write of w follows it.
+__global__ __launch_bounds__(kRouterWaves * kWave) void combine_router_kernel(
+    const float* __restrict__ o, const float* w_prev, const int32_t* __restrict__ inv, int kparts, size_t part_stride,
+    uint16_t* __restrict__ x_out, const uint16_t* __restrict__ wr, int H, int E, int k, int32_t* __restrict__ ids,
+    float* w, uint32_t* __restrict__ count, float* __restrict__ mass) {
+  __shared__ float lg[1][kMaxExperts];
+  __shared__ __align__(16) uint16_t xs[kMaxRouterHidden];
+  const int t = blockIdx.x;
+  for (int n = 4 * (int)threadIdx.x; n < H; n += 4 * kRouterWaves * kWave) {
+    const uint2 p = pack_half4(combine4(o, w_prev, inv, t, k, H, kparts, part_stride, n));
+    *reinterpret_cast<uint2*>(x_out + (size_t)t * H + n) = p;
+    *reinterpret_cast<uint2*>(xs + n) = p;
+  }
+  __syncthreads();
+  router_logits<1>(xs, (size_t)H, wr, 1, H, E, lg);
+  __syncthreads();
+  if (threadIdx.x < kWave) select_topk(lg[0], E, k, t, ids, w, count, mass);
+}
+
+hipError_t launch_router(const uint16_t* x, const uint16_t* wr, int T, int H, int E, int k, int32_t* ids, float* w,
+                         uint32_t* count, float* mass, hipStream_t s) {
+  if (T <= 256) {
+    hipLaunchKernelGGL(router_kernel<1>, dim3(T), dim3(kRouterWaves * kWave), 0, s, x, wr, T, H, E, k, ids, w, count,
+                       mass);
+  } else {
+    static_assert(kRouterTokens <= kRouterWaves, "one selecting wave per token of the tile");
+    hipLaunchKernelGGL(router_kernel<kRouterTokens>, dim3((T + kRouterTokens - 1) / kRouterTokens),
+                       dim3(kRouterWaves * kWave), 0, s, x, wr, T, H, E, k, ids, w, count, mass);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_router(const float* o, const float* w_prev, const int32_t* inv, int kparts,
+                                 uint16_t* x_out, const uint16_t* wr, int T, int H, int E, int k, int32_t* ids,
+                                 float* w, uint32_t* count, float* mass, hipStream_t s) {
+  if (H > kMaxRouterHidden) return hipErrorInvalidValue;
+  const size_t part_stride = (size_t)T * k * H;
+  hipLaunchKernelGGL(combine_router_kernel, dim3(T), dim3(kRouterWaves * kWave), 0, s, o, w_prev, inv, kparts,
+                     part_stride, x_out, wr, H, E, k, ids, w, count, mass);
   return hipGetLastError();
 }
 

@@ -192,6 +192,13 @@ def next_rows(layer, dev, copies, opts, stream, evs, steps: int):
     torch.cuda.synchronize()
     out["router_us"] = 1e3 * timed_ms(evs, stream, route, steps)
     out["routed_layer_us"] = 1e3 * timed_ms(evs, stream, routed, steps)
+    # the layer alone on the router's own routing (which routes other experts
+    # than the synthetic ids the plain layer call uses), for a like-for-like
+    # cost of the router inside the routed call
+    route(0)
+    same = lambda i: B.pw_moe_forward(dev.shape, wl.T, dev.x, ids, w, dev.blocks[i % copies], dev.q, y2, dev.ws,
+                                      opts=opts, stream=stream)
+    out["layer_on_router_ids_us"] = 1e3 * timed_ms(evs, stream, same, steps)
     torch.cuda.synchronize()
     # HIP graph of G consecutive layer calls (rotating storage copies), replayed
     G = 16
@@ -258,6 +265,7 @@ def next_rows(layer, dev, copies, opts, stream, evs, steps: int):
                     "layer_us_alone_q3": alone_us, "layer_us_during_reload": during_us,
                     "layer_calls_during_reload": n_during}
     paged.close()
+    out["layers"] = multi_layer_rows(layer, opts, stream, evs, steps)
     # planner: host time for 24 layers of this shape
     nb = 24 * 2 * wl.E
     sens = synth.draw_sensitivity(wl.seed, nb)
@@ -428,6 +436,90 @@ def measure(name, layer, dev, copies, args, evs, stream, opts_kw):
         "roofline": roof,
         "output_finite_and_status_clear": ok,
     }
+
+
+def multi_layer_rows(layer, opts, stream, evs, steps: int, nlayers: int = 8):
+    """Decode step through `nlayers` layers of this shape, each with its own
+    device storage (copies of one full draw) and its own router, chained in
+    one pw_moe_forward_layers call: per-layer time eager and as a replayed HIP
+    graph, against one routed layer call and one unrouted layer call."""
+    import torch
+    from any_precision_bitplane_amd import binding as B
+    from any_precision_bitplane_amd import synth
+    from any_precision_bitplane_amd.device import DeviceLayer
+    wl = layer.wl
+    full = synth.make_layer(wl)
+    devs = [DeviceLayer(full) for _ in range(nlayers)]
+    wrs = [torch.from_numpy(synth.draw_router_weights(wl.seed + 17 * l, wl.E, wl.H)).cuda() for l in range(nlayers)]
+    shp = devs[0].shape
+    ws = torch.empty(B.pw_workspace_bytes(shp, wl.T), dtype=torch.uint8, device="cuda")
+    B.pw_workspace_init(ws)
+    x0 = devs[0].x
+    y = torch.empty((wl.T, wl.H), dtype=torch.float16, device="cuda")
+    blocks = [d.blocks[0] for d in devs]
+    qs = [d.q for d in devs]
+    # A chain of SwiGLU layers without a residual path is quadratic in the
+    # activation scale; each layer's down tables are scaled so that its output
+    # on its actual input has unit RMS, so every layer routes O(1) inputs (with
+    # vanishing inputs every token would pick the same experts).
+    x = x0
+    for l in range(nlayers):
+        B.pw_moe_forward_routed(shp, wl.T, x, wrs[l], blocks[l], qs[l], y, None, None, ws)
+        torch.cuda.synchronize()
+        rms = float(y.float().pow(2).mean().sqrt())
+        for e in range(wl.E):
+            devs[l].luts[0][e][1].view(torch.float16).mul_(1.0 / max(rms, 1e-6))
+        x_next = torch.empty_like(y)
+        B.pw_moe_forward_routed(shp, wl.T, x, wrs[l], blocks[l], qs[l], x_next, None, None, ws)
+        x = x_next
+    torch.cuda.synchronize()
+    call = lambda i: B.pw_moe_forward_layers(shp, wl.T, x0, wrs, blocks, qs, y, None, None, ws, opts=opts,
+                                             stream=stream)
+    routed = lambda i: B.pw_moe_forward_routed(shp, wl.T, x0, wrs[i % nlayers], blocks[i % nlayers], qs[i % nlayers],
+                                               y, None, None, ws, opts=opts, stream=stream)
+    plain = lambda i: devs[i % nlayers].forward(opts, stream=stream)
+    for i in range(5):
+        call(i)
+        routed(i)
+        plain(i)
+    torch.cuda.synchronize()
+    n = max(4, steps // 4)
+    res = {"layers": nlayers,
+           "eager_us_per_layer": 1e3 * timed_ms(evs, stream, call, n) / nlayers,
+           "routed_single_layer_us": 1e3 * timed_ms(evs, stream, routed, steps),
+           "unrouted_single_layer_us": 1e3 * timed_ms(evs, stream, plain, steps)}
+    # each layer alone on the ids its router gives for its input in the chain
+    xin, ids, w = x0, [], []
+    for l in range(nlayers):
+        i_l = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
+        w_l = torch.empty((wl.T, wl.k), dtype=torch.float32, device="cuda")
+        B.pw_router_topk(shp, wl.T, xin, wrs[l], i_l, w_l, None, None, ws)
+        x_next = torch.empty_like(y)
+        B.pw_moe_forward(shp, wl.T, xin, i_l, w_l, blocks[l], qs[l], x_next, ws)
+        ids.append(i_l)
+        w.append(w_l)
+        xin = x_next
+    torch.cuda.synchronize()
+    same = lambda i: B.pw_moe_forward(shp, wl.T, x0, ids[i % nlayers], w[i % nlayers], blocks[i % nlayers],
+                                      qs[i % nlayers], y, ws, opts=opts, stream=stream)
+    res["layers_alone_on_their_routing_us"] = 1e3 * timed_ms(evs, stream, same, steps)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        B.pw_moe_forward_layers(shp, wl.T, x0, wrs, blocks, qs, y, None, None, ws, opts=opts)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        B.pw_moe_forward_layers(shp, wl.T, x0, wrs, blocks, qs, y, None, None, ws, opts=opts)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    res["graph_us_per_layer"] = 1e3 * timed_ms(evs, stream, lambda i: g.replay(), n) / nlayers
+    del g
+    torch.cuda.synchronize()
+    return res
 
 
 def main():

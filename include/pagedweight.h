@@ -275,8 +275,9 @@ pw_status pw_get_device_status(void* workspace, uint32_t* flags /* host */, void
  * depend on the order the slots arrive in).
  *   x fp16 [T][H], router_w fp16 [E][H] (both 16-byte aligned);
  *   ids int32 [T][k], w fp32 [T][k] outputs; k <= 64 (else
- *   PW_ERR_UNSUPPORTED_SHAPE); workspace as for pw_moe_forward (the logits
- *   live in it).  T == 0 returns PW_OK and enqueues nothing.  Two launches. */
+ *   PW_ERR_UNSUPPORTED_SHAPE); workspace as for pw_moe_forward (not used by
+ *   the router itself).  T == 0 returns PW_OK and enqueues nothing.  One
+ *   launch. */
 pw_status pw_router_topk(const pw_moe_shape* shape /* host */, int32_t T, const uint16_t* x,
                          const uint16_t* router_w, int32_t* ids, float* w, uint32_t* stat_count,
                          float* stat_mass, void* workspace, size_t workspace_bytes, void* stream);
@@ -288,6 +289,37 @@ pw_status pw_moe_forward_routed(const pw_moe_shape* shape /* host */, int32_t T,
                                 const uint16_t* router_w, const pw_block_desc* blocks, const uint8_t* q,
                                 uint16_t* y, uint32_t* stat_count, float* stat_mass, void* workspace,
                                 size_t workspace_bytes, const pw_moe_options* opts, void* stream);
+
+/* L chained layers of one decode step: layer l routes its input with its own
+ * top-k softmax router (as pw_router_topk), runs the fused mixed-precision
+ * layer on its own page table (as pw_moe_forward), and its output is layer
+ * l + 1's input; y receives the last layer's output.  "Technical summary:
+ * PagedWeight", Core components 3 (the fused kernel, which reduces overhead;
+ * committed bitwidths read on the device, so a pager commit between two calls,
+ * or two replays of a captured graph of one call, takes effect without new
+ * launch arguments) and Core components 2 (routing statistics per layer).
+ * Each layer's weighted combine is computed inside the next layer's router
+ * kernel, so a layer takes the router and the expert products (three launches
+ * for decode batches) and only the last layer launches a combine.  Results are
+ * bit-identical to L chained pw_moe_forward_routed calls.
+ *   shape        host, the same for every layer; k <= 64, H <= 16384
+ *   x            fp16 [T][H], layer 0's input;  y  fp16 [T][H], overwritten
+ *   router_w     host array [L] of device fp16 [E][H] router matrices
+ *   blocks, q    host arrays [L] of device page tables [E][2] and bitwidths [E][2]
+ *   stat_count, stat_mass  device uint32 / fp32 [L][E] or NULL: routing
+ *                statistics accumulated per layer, as pw_router_topk
+ *   workspace    as for pw_moe_forward with the same T (intermediate layer
+ *                inputs live in it)
+ *   opts         as for pw_moe_forward; events are not supported
+ *                (PW_ERR_UNSUPPORTED)
+ * Errors: those of pw_moe_forward and pw_router_topk; PW_ERR_INVALID_ARG for
+ * L < 1 or a NULL entry. */
+pw_status pw_moe_forward_layers(const pw_moe_shape* shape /* host */, int32_t L, int32_t T, const uint16_t* x,
+                                const uint16_t* const* router_w /* host [L] */,
+                                const pw_block_desc* const* blocks /* host [L] */,
+                                const uint8_t* const* q /* host [L] */, uint16_t* y, uint32_t* stat_count,
+                                float* stat_mass, void* workspace, size_t workspace_bytes,
+                                const pw_moe_options* opts, void* stream);
 
 /* ------------------------------------------------------------------------
  * Quality-aware bitwidth planner (host code; "Technical summary: PagedWeight",

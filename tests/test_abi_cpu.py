@@ -226,3 +226,30 @@ def test_path_info_rejects_what_the_forward_rejects(lib):
     with pytest.raises(B.PwError):                                     # 32-bit activation offsets
         B.pw_moe_path_info(B.shape(4096, 14336, 8, 2), 40000, B.make_options(path=B.PW_PATH_MGEMV))
     assert lib.pw_moe_path_info(ctypes.byref(s), 4, None, None) == B.PW_ERR_INVALID_ARG
+
+
+def test_multi_layer_call_rejects_bad_arguments_before_launch(lib):
+    p = 1 << 20
+    shp = B.shape(256, 512, 8, 2)
+    arr = lambda *v: (ctypes.c_void_p * len(v))(*v)
+
+    def call(L, T=4, wr=None, bl=None, q=None, x=p, y=p, ws=p, ws_bytes=1 << 40, opts=None):
+        wr = wr if wr is not None else arr(*([p] * max(L, 1)))
+        bl = bl if bl is not None else arr(*([p] * max(L, 1)))
+        q = q if q is not None else arr(*([p] * max(L, 1)))
+        return lib.pw_moe_forward_layers(ctypes.byref(shp), L, T, x, wr, bl, q, y, None, None, ws, ws_bytes,
+                                         ctypes.byref(opts) if opts is not None else None, None)
+
+    assert call(0) == B.PW_ERR_INVALID_ARG
+    assert call(2, wr=arr(p, None)) == B.PW_ERR_INVALID_ARG
+    assert call(2, q=arr(None, p)) == B.PW_ERR_INVALID_ARG
+    assert call(2, bl=arr(p, p + 4)) == B.PW_ERR_ALIGNMENT
+    assert call(2, x=None) == B.PW_ERR_INVALID_ARG
+    assert call(2, ws=None) == B.PW_ERR_INVALID_ARG
+    assert call(2, ws_bytes=16) == B.PW_ERR_WORKSPACE
+    assert call(2, T=0) == B.PW_OK
+    ev = B.make_options(events=[p, p, p, p, p])
+    assert call(2, opts=ev) == B.PW_ERR_UNSUPPORTED
+    big = B.shape(32768, 64, 8, 2)
+    assert lib.pw_moe_forward_layers(ctypes.byref(big), 2, 4, p, arr(p, p), arr(p, p), arr(p, p), p, None, None, p,
+                                     1 << 40, None, None) == B.PW_ERR_UNSUPPORTED_SHAPE
