@@ -97,7 +97,7 @@ __device__ __forceinline__ constexpr uint32_t level_mask() {
 // One swap level on rows r and r+S (r & S == 0), with compile-time knowledge of
 // which rows are still all-zero (bit r of Z).  Returns the new zero set.
 template <int S, unsigned Z>
-__device__ __forceinline__ constexpr unsigned level_zero_after() {
+__host__ __device__ constexpr unsigned level_zero_after() {
   unsigned z = Z;
   for (int r = 0; r < 8; ++r)
     if ((r & S) == 0) {
@@ -129,8 +129,22 @@ __device__ __forceinline__ void swap_level(uint32_t (&R)[8]) {
   }
 }
 
+// planes_to_fields in its parts: the inputs placed (fields_init), then swap
+// level LV = 0, 1, 2 (fields_level), so a caller can spread the levels over
+// other work.  Same instructions, same result.
 template <int Q>
-__device__ __forceinline__ void planes_to_fields(const uint32_t (&P)[Q], uint32_t (&R)[8]) {
+struct FieldsPlan {
+  static constexpr unsigned Z0 = Q == 8 ? 0u : (0xFFu & ~(((1u << Q) - 1u) << 1));
+  // level orders with the fewest instructions for each zero pattern
+  static constexpr int L0 = (Q == 3) ? 2 : (Q == 5) ? 1 : (Q == 4) ? 2 : 4;
+  static constexpr int L1 = (Q == 3) ? 1 : (Q == 5) ? 4 : (Q == 4) ? 1 : 2;
+  static constexpr int L2 = (Q == 3) ? 4 : (Q == 5) ? 2 : (Q == 4) ? 4 : 1;
+  static constexpr unsigned Z1 = level_zero_after<L0, Z0>();
+  static constexpr unsigned Z2 = level_zero_after<L1, Z1>();
+};
+
+template <int Q>
+__device__ __forceinline__ void fields_init(const uint32_t (&P)[Q], uint32_t (&R)[8]) {
 #pragma unroll
   for (int r = 0; r < 8; ++r) R[r] = 0u;
 #pragma unroll
@@ -138,16 +152,22 @@ __device__ __forceinline__ void planes_to_fields(const uint32_t (&P)[Q], uint32_
     if constexpr (Q == 8) R[7 - p] = P[p];
     else R[Q - p] = P[p];
   }
-  constexpr unsigned Z0 = Q == 8 ? 0u : (0xFFu & ~(((1u << Q) - 1u) << 1));
-  // level orders with the fewest instructions for each zero pattern
-  constexpr int L0 = (Q == 3) ? 2 : (Q == 5) ? 1 : (Q == 4) ? 2 : 4;
-  constexpr int L1 = (Q == 3) ? 1 : (Q == 5) ? 4 : (Q == 4) ? 1 : 2;
-  constexpr int L2 = (Q == 3) ? 4 : (Q == 5) ? 2 : (Q == 4) ? 4 : 1;
-  constexpr unsigned Z1 = level_zero_after<L0, Z0>();
-  constexpr unsigned Z2 = level_zero_after<L1, Z1>();
-  swap_level<L0, Z0>(R);
-  swap_level<L1, Z1>(R);
-  swap_level<L2, Z2>(R);
+}
+
+template <int Q, int LV>
+__device__ __forceinline__ void fields_level(uint32_t (&R)[8]) {
+  using F = FieldsPlan<Q>;
+  if constexpr (LV == 0) swap_level<F::L0, F::Z0>(R);
+  else if constexpr (LV == 1) swap_level<F::L1, F::Z1>(R);
+  else swap_level<F::L2, F::Z2>(R);
+}
+
+template <int Q>
+__device__ __forceinline__ void planes_to_fields(const uint32_t (&P)[Q], uint32_t (&R)[8]) {
+  fields_init<Q>(P, R);
+  fields_level<Q, 0>(R);
+  fields_level<Q, 1>(R);
+  fields_level<Q, 2>(R);
 }
 
 // Byte B of r added to base (one SDWA instruction).

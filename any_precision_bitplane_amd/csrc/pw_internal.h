@@ -17,7 +17,7 @@ constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-constexpr int kMfmaTileM = 256;   // tokens per MFMA tile
+constexpr int kMfmaTileM = 512;   // tokens per MFMA tile
 constexpr int kMaxRouterTopK = 64; // the router's top-k kernel keeps slot j in lane j
 constexpr int kMaxRouterHidden = 16384;   // a multi-layer call's router keeps one token's x in LDS
 

@@ -5,40 +5,70 @@
 // GEMV, because with hundreds of tokens per expert the product is a dense
 // contraction.
 //
-// Tile: 256 tokens x 128 weight rows per 8-wave workgroup, K step 64.
-//   * every wave decodes: a pair of threads turns one 32-weight group (the
-//     first q plane words of one row) into fp16 through the row's table in
-//     LDS, each thread half of it with its lookups issued together, and
-//     writes it to a double-buffered weight tile;
-//   * all waves stage the gathered activation tile (half a token row each);
-//   * every wave multiplies a 64 x 64 sub-tile with v_mfma_f32_16x16x32_f16
-//     (fp32 accumulation).
-// Plane words are prefetched into registers two K steps ahead and
-// activations one step ahead, and the decode of step k+1 is issued while the
-// matrix cores work on step k.  gate_up tiles take 64 gate rows and the
-// matching 64 up rows; each wave holds matching gate and up columns, so SwiGLU
-// runs on the accumulators and h leaves as fp16.  Token tiles less than half
-// full take a variant that feeds the matrix cores' activation operand from
-// registers loaded straight from memory (no LDS activation tile).
+// Tile: 512 tokens x 128 device rows (eight 16-row tiles of the device
+// layout) per workgroup of four waves, one per SIMD; each wave multiplies
+// 128 tokens by all 128 rows (a 128 x 128 fp32 accumulator, 256 registers,
+// v_mfma_f32_16x16x32_f16), so every weight decoded into LDS feeds 512
+// tokens and every LDS byte of it feeds 128 tokens of one wave.
+//   * Weights: every thread decodes one 32-weight plane word per K step (its
+//     q plane words transposed into code fields, looked up in the row's table
+//     in LDS) into a double-buffered fp16 B tile in LDS; the decode of step
+//     k + 1 runs while the matrix cores work on step k.
+//   * Activations: a wave's token rows are read only by that wave, so they
+//     go straight from memory into the A operand registers, one 32-wide
+//     sub-step ahead; no LDS, and LDS bandwidth is left to the decode and the
+//     B operand.
+// K order.  A K step is two plane words per row; which K positions a step
+// holds is free as long as the A and B operands agree.  Thread (row r, half
+// h) loads plane words 8 Q + 4 h .. +4 of its row for a quad Q of four steps
+// (one 16-byte load per plane: the device layout keeps a row's 16-word run
+// contiguous) and decodes word 8 Q + 4 h + j at step j of the quad into slot
+// h of the B tile; sub-step h of the step multiplies slot h with the
+// activations of the same word.
+// gate_up tiles hold 8 gate rows and their 8 up rows per 16-row tile (the
+// device layout's interleave), so SwiGLU pairs MFMA columns n and n + 8.
 //
 // Work items are (token tile, row tile) pairs; token tiles come from the route
 // kernel's list.  Consecutive items on one XCD (workgroups are dealt to the 8
-// XCDs round-robin) sweep the row tiles of one token tile, so the activation
+// XCDs round-robin) sweep the row tiles of one token tile, so its activation
 // rows stay in that XCD's L2.
+#include <type_traits>
+
 #include "pw_device.h"
 #include "pw_internal.h"
 
 namespace pw {
 
-constexpr int kMfmaThreads = 512;
-constexpr int kTM = kMfmaTileM;        // 256 tokens
-constexpr int kTN = 128;               // weight rows
-constexpr int kTK = 64;                // reduction step
-constexpr int kTileStride = kTK + 8;   // fp16 elements per LDS tile row (padding against bank conflicts)
+constexpr int kPfWaves = 4;
+constexpr int kPfThreads = kPfWaves * kWave;
+constexpr int kPfTM = kMfmaTileM;        // tokens per tile
+constexpr int kPfWM = kPfTM / kPfWaves;  // tokens per wave
+static_assert(kPfWM == 128, "eight 16-token groups per wave");
+constexpr int kPfTN = 128;               // device rows per tile
+constexpr int kPfTG = kPfWM / 16;        // token groups per wave
+constexpr int kPfRG = kPfTN / 16;        // row groups
+constexpr int kPfBStride = 2 * 64 + 16;  // bytes per B-tile row: 64 fp16 of one step + pad (conflict-free reads)
+constexpr int kPfBBytes = kPfTN * kPfBStride;
+constexpr int kPfTabBytes = kPfTN * 512; // row tables: 256-byte slots (q <= 7) or 512 (q = 8)
+constexpr int kPfLds = kPfTabBytes + 2 * kPfBBytes;
 constexpr int kXcds = 8;
 
 typedef _Float16 half8v __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(3))) u32x4v* lds_u4c;
+typedef __attribute__((address_space(3))) u32x4v* lds_u4;
+typedef const __attribute__((address_space(3))) _Float16* lds_f16c;
+
+__device__ __forceinline__ _Float16 lds_f16_at(uint32_t addr) { return *(lds_f16c)(size_t)addr; }
+
+// True, but the compiler cannot see it: code under `if (always_true())` is a
+// basic block of its own, and the compiler schedules within basic blocks.
+__device__ __forceinline__ bool always_true() {
+  int v = 1;
+  asm volatile("" : "+s"(v));
+  return v != 0;
+}
 
 struct MfmaArgs {
   int H, I, E, k, T;
@@ -50,49 +80,13 @@ struct MfmaArgs {
   float* oout;           // down output
   int ntiles;            // row tiles per block
   int grid;              // launched workgroups (multiple of 8)
-  int direct_ok;         // activations addressable with 32-bit offsets (variant for partial tiles)
-};
-
-// Row of the block held at tile-local row r (0..127).
-template <bool GU>
-__device__ __forceinline__ int mrow(int nt, int r, int I) {
-  if constexpr (GU) return (r < 64 ? 0 : I) + nt * 64 + (r & 63);
-  else return nt * kTN + r;
-}
-
-template <bool GU>
-__device__ __forceinline__ bool mrow_ok(int nt, int r, int I, int H) {
-  if constexpr (GU) return nt * 64 + (r & 63) < I;
-  else return nt * kTN + r < H;
-}
-
-constexpr int kLdsTabs = kTN * (1 << kMaxBits) * 2;              // 64 KB
-constexpr int kLdsW = kTN * kTileStride * 2;                     // one weight tile
-constexpr int kLdsX = kTM * kTileStride * 2;                     // activation tile
-constexpr int kMfmaLds = kLdsTabs + 2 * kLdsW + kLdsX;
-
-// Sixteen weights of a group: fields of weights j (0..15) in byte j >> 3 of
-// F[j & 7]; all sixteen lookups are issued before any is packed.
-template <int Q>
-struct HalfGroupDecode {
-  __device__ static __forceinline__ void run(const uint32_t (&F)[8], uint32_t base, uint32_t (&out)[8]) {
-    uint32_t v[16];
-    lookups<0>(F, base, v);
-#pragma unroll
-    for (int p = 0; p < 8; ++p) out[p] = v[2 * p] | (v[2 * p + 1] << 16);
-  }
-  template <int J>
-  __device__ static __forceinline__ void lookups(const uint32_t (&F)[8], uint32_t base, uint32_t (&v)[16]) {
-    if constexpr (J < 16) {
-      v[J] = lds_u16_at(entry_addr<Q, J>(F, base));
-      lookups<J + 1>(F, base, v);
-    }
-  }
+  uint32_t act_bytes;    // activation bytes (< 2^31): out-of-range offsets read zero
 };
 
 template <int Q, bool GU>
-__device__ __forceinline__ void mfma_tile(const MfmaArgs& A, int e, int n_e, int off_e, int m0, int nt, uint8_t* lds) {
+__device__ __forceinline__ void pf_tile(const MfmaArgs& A, int e, int n_e, int off_e, int m0, int nt, uint8_t* lds) {
   constexpr int TAB = (1 << Q) * 2;
+  constexpr int TSTRIDE = kTabStride<Q>;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -100,401 +94,316 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& A, int e, int n_e, int
   const int N = GU ? 2 * I : H;
   const int K = GU ? H : I;
   const int W = K >> 5;
-  const int nk = (K + kTK - 1) / kTK;
+  const int nq = (W + 7) >> 3;             // quads of four K steps
+  const int nsteps = 4 * nq;
+  const int nm = n_e - m0 < kPfTM ? n_e - m0 : kPfTM;
 
   uint8_t* tabs = lds;
-  _Float16* wt0 = reinterpret_cast<_Float16*>(lds + kLdsTabs);
-  _Float16* wt1 = wt0 + kTN * kTileStride;
-  _Float16* xt = wt1 + kTN * kTileStride;
+  uint8_t* btile = lds + kPfTabBytes;
 
   const pw_block_desc d = A.blocks[2 * e + (GU ? 0 : 1)];
   const uint32_t pstride = (uint32_t)N * (uint32_t)W * 4u;
   const __amdgpu_buffer_rsrc_t prs = make_rsrc(uniform_ptr(d.planes), pstride * (uint32_t)Q);
   const uint16_t* __restrict__ lut = uniform_ptr(d.lut_all) + lut_offset(N, Q);
 
-  // Row tables -> LDS (uint4 chunks; rows outside the block read as zero).
-  for (int c = tid; c < kTN * TAB / 16; c += kMfmaThreads) {
-    const int r = c / (TAB / 16), cc = c % (TAB / 16);
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (mrow_ok<GU>(nt, r, I, H))
-      v = *reinterpret_cast<const uint4*>(lut + (size_t)mrow<GU>(nt, r, I) * (1 << Q) + cc * 8);
-    *reinterpret_cast<uint4*>(tabs + c * 16) = v;
+  // Row tables -> LDS: tile row r in a TSTRIDE slot; a table smaller than its
+  // slot sits at byte offset skew(r) = TAB * r mod 256 of it, applied as an
+  // XOR (entry c at byte 2c ^ skew(r)), which spreads the 16 rows of a
+  // half-wave's lookups over the LDS banks.  Direct buffer-to-LDS loads.
+  auto skew_of = [&](int r) -> uint32_t { return TAB < 256 ? (uint32_t)((TAB * r) & 255) : 0u; };
+  {
+    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(lut, (uint32_t)N * (uint32_t)TAB);
+    constexpr int NI = kPfTN * TSTRIDE / 1024;
+#pragma unroll
+    for (int i0 = 0; i0 < NI; i0 += kPfWaves) {
+      const int i = i0 + wave;
+      const int pos = 1024 * i + 16 * lane;
+      const int r = pos / TSTRIDE;
+      const int chunk = (pos % TSTRIDE) / 16 ^ (int)(skew_of(r) >> 4);
+      const int crow = canon_row(kPfTN * nt + r, I, GU);
+      const uint32_t voff =
+          (16 * chunk < TAB && crow < N) ? (uint32_t)crow * (uint32_t)TAB + 16u * (uint32_t)chunk : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (__attribute__((address_space(3))) void*)(tabs + 1024 * i), 16,
+                                               voff, 0, 0, 0);
+    }
   }
 
-  // Decode job: row dr, word dw of each K step, weights [16 dh, 16 dh + 16)
-  // of that word (the two threads of a pair load the same plane words).
-  const int dr = tid >> 2, dw = (tid >> 1) & 1, dh = tid & 1;
-  const bool dr_ok = mrow_ok<GU>(nt, dr, I, H);
-  const int ddev = dev_row(mrow<GU>(nt, dr, I), I, GU);   // device-layout row
-  const uint32_t tab_base = lds_addr(tabs) + (uint32_t)(dr * TAB);
-  // Activation job (all waves): token row xr, columns [32 xh, +32) of each K step.
-  const int xr = tid >> 1, xh = tid & 1;
-  const uint16_t* xsrc = nullptr;
-  if (xr < n_e - m0) {
-    const int pos = off_e + m0 + xr;
-    xsrc = GU ? A.act + (size_t)(A.rt.perm[pos] / A.k) * H : A.act + (size_t)pos * I;
-  }
-
-  uint32_t Pa[Q], Pb[Q];
-  uint4 X[4];
-
-  // plane words of a K step, two steps ahead
-  auto prefetch_planes = [&](uint32_t (&P)[Q], int step) {
-    if (step >= nk) return;
-    const int wc = ((step * kTK) >> 5) + dw;
-    const uint32_t voff = (dr_ok && wc < W) ? dev_word(ddev, wc, W) * 4u : kOutOfRange;
+  // Decode job: tile row r, half h.
+  const int r = tid >> 1, h = tid & 1;
+  const int drow = kPfTN * nt + r;
+  const uint32_t tbase = lds_addr(tabs) + (uint32_t)(r * TSTRIDE);
+  const uint32_t skew4 = skew_of(r) * 0x01010101u;
+  const bool vec = (W & 3) == 0;
+  auto load_quad = [&](uint32_t (&P)[Q][4], int qd) {
+    const int wd = 8 * qd + 4 * h;
+    const bool live = qd < nq && wd < W && drow < N;
+    const uint32_t voff = live ? dev_word(drow, wd, W) * 4u : kOutOfRange;
+    if (vec) {
 #pragma unroll
-    for (int p = 0; p < Q; ++p) P[p] = buf_load_u32(prs, voff, (uint32_t)p * pstride);
-  };
-  // activations of a K step (everyone), one step ahead (they hit L2)
-  auto prefetch_x = [&](int step) {
-    if (step >= nk) return;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int c = step * kTK + 32 * xh + 8 * v;
-      X[v] = make_uint4(0u, 0u, 0u, 0u);
-      if (xsrc != nullptr && c < K) X[v] = *reinterpret_cast<const uint4*>(xsrc + c);
-    }
-  };
-  auto decode = [&](uint32_t (&P)[Q], _Float16* wt) {
-    uint32_t R[8];
-    planes_to_fields<Q>(P, R);
-    // this thread's half: fields of weights 16 dh + j sit in bytes 2 dh, 2 dh + 1 of R[j & 7]
-    uint32_t F[8];
-    const uint32_t sel = dh ? 0x0c0c0302u : 0x0c0c0100u;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) F[i] = __builtin_amdgcn_perm(0u, R[i], sel);
-    uint32_t packed[8];
-    HalfGroupDecode<Q>::run(F, tab_base, packed);
-    uint4* dst = reinterpret_cast<uint4*>(wt + dr * kTileStride + dw * 32 + dh * 16);
-    dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-  };
-  auto stage_x = [&]() {
-    uint4* dst = reinterpret_cast<uint4*>(xt + xr * kTileStride + 32 * xh);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) dst[v] = X[v];
-  };
-
-  // Wave sub-tile: tokens [64 wm, +64); rows: gate_up -> gate [32 wn, +32) and
-  // up [64 + 32 wn, +32); down -> [64 wn, +64).
-  const int wm = wave & 3, wn = wave >> 2;
-  int ncol[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) ncol[j] = GU ? ((j < 2 ? 0 : 64) + 32 * wn + 16 * (j & 1)) : (64 * wn + 16 * j);
-
-  float4v acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
-
-  auto mma = [&](const _Float16* wt) {
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      __builtin_amdgcn_sched_barrier(0);   // keep the two K halves' fragments from being live together
-      half8v af[4], bf[4];
-      const int kk = kh * 32 + 8 * (lane >> 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const half8v*>(xt + (64 * wm + 16 * i + (lane & 15)) * kTileStride + kk);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bf[j] = *reinterpret_cast<const half8v*>(wt + (ncol[j] + (lane & 15)) * kTileStride + kk);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  // Prologue: planes of steps 0 and 1 and activations of step 0 in flight;
-  // stage step 0; activations of step 1 in flight.
-  prefetch_planes(Pa, 0);
-  prefetch_planes(Pb, 1);
-  prefetch_x(0);
-  __syncthreads();                        // tables in LDS
-  decode(Pa, wt0);
-  stage_x();
-  prefetch_planes(Pa, 2);
-  prefetch_x(1);
-  __syncthreads();
-
-  // Step k: matrix cores on (xt, wt[k&1]); meanwhile decode step k+1 into the
-  // other weight buffer; then stage the activations of step k+1.
-  for (int k = 0; k < nk; k += 2) {
-    // even step k: weights in wt0; planes of step k+1 in Pb
-    mma(wt0);
-    if (k + 1 < nk) {
-      decode(Pb, wt1);
-      prefetch_planes(Pb, k + 3);
-    }
-    __syncthreads();
-    if (k + 1 < nk) {
-      stage_x();
-      prefetch_x(k + 2);
-    }
-    __syncthreads();
-    if (k + 1 >= nk) break;
-    // odd step k+1: weights in wt1; planes of step k+2 in Pa
-    mma(wt1);
-    if (k + 2 < nk) {
-      decode(Pa, wt0);
-      prefetch_planes(Pa, k + 4);
-    }
-    __syncthreads();
-    if (k + 2 < nk) {
-      stage_x();
-      prefetch_x(k + 3);
-    }
-    __syncthreads();
-  }
-
-  // Epilogue.  acc[i][j] element v: token 64 wm + 16 i + 4 (lane >> 4) + v,
-  // tile column ncol[j] + (lane & 15).
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = 64 * wm + 16 * i + 4 * (lane >> 4) + v;
-      if (m >= n_e - m0) continue;
-      const size_t pos = (size_t)(off_e + m0 + m);
-      if constexpr (GU) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int r = ncol[j] + (lane & 15);          // gate row (tile-local < 64)
-          if (!mrow_ok<GU>(nt, r, I, H)) continue;
-          const float g = acc[i][j][v], u = acc[i][j + 2][v];
-          const _Float16 hh = (_Float16)(silu_f32(g) * u);
-          A.hout[pos * I + nt * 64 + r] = __builtin_bit_cast(uint16_t, hh);
-        }
-      } else {
-        const size_t slot = (size_t)A.rt.perm[pos];   // o rows are indexed by slot
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = ncol[j] + (lane & 15);
-          if (!mrow_ok<GU>(nt, r, I, H)) continue;
-          A.oout[slot * H + nt * kTN + r] = acc[i][j][v];
-        }
+      for (int p = 0; p < Q; ++p) {
+        const uint4 v = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(prs, (int)voff, (int)((uint32_t)p * pstride), 0));
+        P[p][0] = v.x; P[p][1] = v.y; P[p][2] = v.z; P[p][3] = v.w;
       }
-    }
-  }
-}
-
-// Variant for token tiles less than half full (moderate batches): the
-// matrix-core A operand is loaded straight from the activation rows into
-// registers, one K step ahead, instead of being staged in LDS, so a step needs
-// one barrier instead of two and absent tokens cost no loads; waves whose
-// tokens are all absent skip the matrix-core work.  With full tiles the
-// LDS-staged kernel above hides the activation latency better (measured on
-// the Mixtral-shaped prefill layer: 9.1 ms staged, 10.2 ms direct); with 16
-// tokens per expert (Mixtral-shaped layer, T = 64) the call takes 1.43 ms
-// instead of 1.98, the batched Qwen-shaped call 0.68 ms instead of 0.81.  The
-// switch point (fewer than 128 tokens) was the fastest of 64/128/192/256 on
-// the prefill layer; the other two calls did not depend on it.
-constexpr int kDirectBelow = 128;
-template <int Q, bool GU>
-__device__ __forceinline__ void mfma_tile_direct(const MfmaArgs& A, int e, int n_e, int off_e, int m0, int nt, uint8_t* lds) {
-  constexpr int TAB = (1 << Q) * 2;
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int H = A.H, I = A.I;
-  const int N = GU ? 2 * I : H;
-  const int K = GU ? H : I;
-  const int W = K >> 5;
-  const int nk = (K + kTK - 1) / kTK;
-
-  uint8_t* tabs = lds;
-  _Float16* wt0 = reinterpret_cast<_Float16*>(lds + kLdsTabs);
-  _Float16* wt1 = wt0 + kTN * kTileStride;   // (the activation tile's LDS is unused here)
-
-  const pw_block_desc d = A.blocks[2 * e + (GU ? 0 : 1)];
-  const uint32_t pstride = (uint32_t)N * (uint32_t)W * 4u;
-  const __amdgpu_buffer_rsrc_t prs = make_rsrc(uniform_ptr(d.planes), pstride * (uint32_t)Q);
-  const uint16_t* __restrict__ lut = uniform_ptr(d.lut_all) + lut_offset(N, Q);
-
-  // Row tables -> LDS (uint4 chunks; rows outside the block read as zero).
-  for (int c = tid; c < kTN * TAB / 16; c += kMfmaThreads) {
-    const int r = c / (TAB / 16), cc = c % (TAB / 16);
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (mrow_ok<GU>(nt, r, I, H))
-      v = *reinterpret_cast<const uint4*>(lut + (size_t)mrow<GU>(nt, r, I) * (1 << Q) + cc * 8);
-    *reinterpret_cast<uint4*>(tabs + c * 16) = v;
-  }
-
-  // Decode job: row dr, word dw of each K step, weights [16 dh, 16 dh + 16)
-  // of that word (the two threads of a pair load the same plane words).
-  const int dr = tid >> 2, dw = (tid >> 1) & 1, dh = tid & 1;
-  const bool dr_ok = mrow_ok<GU>(nt, dr, I, H);
-  const int ddev = dev_row(mrow<GU>(nt, dr, I), I, GU);   // device-layout row
-  const uint32_t tab_base = lds_addr(tabs) + (uint32_t)(dr * TAB);
-  uint32_t Pa[Q], Pb[Q];
-
-  // plane words of a K step, two steps ahead
-  auto prefetch_planes = [&](uint32_t (&P)[Q], int step) {
-    if (step >= nk) return;
-    const int wc = ((step * kTK) >> 5) + dw;
-    const uint32_t voff = (dr_ok && wc < W) ? dev_word(ddev, wc, W) * 4u : kOutOfRange;
-#pragma unroll
-    for (int p = 0; p < Q; ++p) P[p] = buf_load_u32(prs, voff, (uint32_t)p * pstride);
-  };
-  auto decode = [&](uint32_t (&P)[Q], _Float16* wt) {
-    uint32_t R[8];
-    planes_to_fields<Q>(P, R);
-    // this thread's half: fields of weights 16 dh + j sit in bytes 2 dh, 2 dh + 1 of R[j & 7]
-    uint32_t F[8];
-    const uint32_t sel = dh ? 0x0c0c0302u : 0x0c0c0100u;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) F[i] = __builtin_amdgcn_perm(0u, R[i], sel);
-    uint32_t packed[8];
-    HalfGroupDecode<Q>::run(F, tab_base, packed);
-    uint4* dst = reinterpret_cast<uint4*>(wt + dr * kTileStride + dw * 32 + dh * 16);
-    dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-  };
-  // Wave sub-tile: tokens [64 wm, +64); rows: gate_up -> gate [32 wn, +32) and
-  // up [64 + 32 wn, +32); down -> [64 wn, +64).
-  const int wm = wave & 3, wn = wave >> 2;
-  // Matrix-core A operand straight from the activation rows (no LDS stage):
-  // for token block i the lane holds token 64 wm + 16 i + (lane & 15),
-  // columns 8 (lane >> 4) .. +8 of each 32-column half of a K step.
-  const uint32_t abytes = (uint32_t)((GU ? (size_t)A.T * H : (size_t)A.T * A.k * I) * 2u);
-  const __amdgpu_buffer_rsrc_t ars = make_rsrc(A.act, abytes);
-  uint32_t aoff[4];   // byte offset of the lane's token row (out of range: reads zero)
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = 64 * wm + 16 * i + (lane & 15);
-    aoff[i] = kOutOfRange;
-    if (m < n_e - m0) {
-      const int pos = off_e + m0 + m;
-      aoff[i] = GU ? (uint32_t)(A.rt.perm[pos] / A.k) * (uint32_t)H * 2u : (uint32_t)pos * (uint32_t)I * 2u;
-    }
-  }
-  int ncol[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) ncol[j] = GU ? ((j < 2 ? 0 : 64) + 32 * wn + 16 * (j & 1)) : (64 * wn + 16 * j);
-
-  float4v acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
-
-  uint4 Ar[2][4];
-  auto load_a = [&](uint4 (&Ar)[2][4], int step) {
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const int c = step * kTK + kh * 32 + 8 * (lane >> 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t voff = c < K ? aoff[i] + 2u * (uint32_t)c : kOutOfRange;
-        Ar[kh][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ars, (int)voff, 0, 0));
-      }
-    }
-  };
-  // a wave whose 64 tokens all lie past the expert's last one has nothing to multiply
-  const bool wave_live = 64 * wm < n_e - m0;
-  auto mma = [&](const _Float16* wt, const uint4 (&Ar)[2][4]) {
-    if (!wave_live) return;
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      __builtin_amdgcn_sched_barrier(0);   // keep the two K halves' fragments from being live together
-      half8v af[4], bf[4];
-      const int kk = kh * 32 + 8 * (lane >> 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = __builtin_bit_cast(half8v, Ar[kh][i]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bf[j] = *reinterpret_cast<const half8v*>(wt + (ncol[j] + (lane & 15)) * kTileStride + kk);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  // Prologue: planes of steps 0 and 1 and activations of step 0 in flight;
-  // decode step 0.
-  load_a(Ar, 0);
-  prefetch_planes(Pa, 0);
-  prefetch_planes(Pb, 1);
-  __syncthreads();                        // tables in LDS
-  decode(Pa, wt0);
-  prefetch_planes(Pa, 2);
-  __syncthreads();
-
-  // Step k: matrix cores on wt[k&1] with the activations in registers; then
-  // request the activations of step k+1 and decode step k+1 into the other
-  // weight buffer.  One barrier per step: after it the decoded tile is
-  // complete and nobody reads the buffer the next decode overwrites.
-  for (int k = 0; k < nk; k += 2) {
-    mma(wt0, Ar);
-    if (k + 1 < nk) {
-      load_a(Ar, k + 1);
-      decode(Pb, wt1);
-      prefetch_planes(Pb, k + 3);
-    }
-    __syncthreads();
-    if (k + 1 >= nk) break;
-    mma(wt1, Ar);
-    if (k + 2 < nk) {
-      load_a(Ar, k + 2);
-      decode(Pa, wt0);
-      prefetch_planes(Pa, k + 4);
-    }
-    __syncthreads();
-  }
-
-  // Epilogue.  acc[i][j] element v: token 64 wm + 16 i + 4 (lane >> 4) + v,
-  // tile column ncol[j] + (lane & 15).
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = 64 * wm + 16 * i + 4 * (lane >> 4) + v;
-      if (m >= n_e - m0) continue;
-      const size_t pos = (size_t)(off_e + m0 + m);
-      if constexpr (GU) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int r = ncol[j] + (lane & 15);          // gate row (tile-local < 64)
-          if (!mrow_ok<GU>(nt, r, I, H)) continue;
-          const float g = acc[i][j][v], u = acc[i][j + 2][v];
-          const _Float16 hh = (_Float16)(silu_f32(g) * u);
-          A.hout[pos * I + nt * 64 + r] = __builtin_bit_cast(uint16_t, hh);
-        }
-      } else {
-        const size_t slot = (size_t)A.rt.perm[pos];   // o rows are indexed by slot
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = ncol[j] + (lane & 15);
-          if (!mrow_ok<GU>(nt, r, I, H)) continue;
-          A.oout[slot * H + nt * kTN + r] = acc[i][j][v];
-        }
-      }
-    }
-  }
-}
-
-template <bool GU>
-__device__ __forceinline__ void mfma_zero_tile(const MfmaArgs& A, int n_e, int off_e, int m0, int nt) {
-  for (int i = threadIdx.x; i < kTM * kTN; i += kMfmaThreads) {
-    const int m = i / kTN, r = i % kTN;
-    if (m >= n_e - m0) continue;
-    const size_t pos = (size_t)(off_e + m0 + m);
-    if constexpr (GU) {
-      if (r < 64 && mrow_ok<GU>(nt, r, A.I, A.H)) A.hout[pos * A.I + nt * 64 + r] = 0;
     } else {
-      if (mrow_ok<GU>(nt, r, A.I, A.H)) A.oout[(size_t)A.rt.perm[pos] * A.H + nt * kTN + r] = 0.0f;
+#pragma unroll
+      for (int p = 0; p < Q; ++p)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          P[p][i] = buf_load_u32(prs, (live && wd + i < W) ? dev_word(drow, wd + i, W) * 4u : kOutOfRange,
+                                 (uint32_t)p * pstride);
+    }
+  };
+  // Decode of one plane word into B-tile buffer `buf`, slot h, in parts that
+  // the steps spread over their pieces: the fields (inputs placed, three
+  // swap levels, the bank skew); the LDS addresses of the eight lookups of
+  // byte b of every field (weights 8 b .. 8 b + 7); those lookups; packing
+  // them into fp16 pairs 4 b .. 4 b + 3; the stores.
+  uint32_t R[8];
+  uint32_t la[8];
+  uint32_t lv[4][8];
+  uint32_t pk[16];
+  auto fields_in = [&](const uint32_t (&P)[Q][4], auto Jc) {
+    constexpr int J = decltype(Jc)::value;
+    uint32_t W8[Q];
+#pragma unroll
+    for (int p = 0; p < Q; ++p) W8[p] = P[p][J];
+    fields_init<Q>(W8, R);
+    fields_level<Q, 0>(R);
+  };
+  auto fields_out = [&]() {
+    fields_level<Q, 2>(R);
+    if constexpr (TAB < 256) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) R[c] ^= skew4;
+    }
+  };
+  auto lookup_addrs = [&](int bb) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) la[c] = tab_entry<Q>(R, tbase, 8 * bb + c);
+  };
+  auto lookups = [&](int bb) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) lv[bb][c] = lds_u16_at(la[c]);
+  };
+  auto pack = [&](int bb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pk[4 * bb + i] = lv[bb][2 * i] | (lv[bb][2 * i + 1] << 16);
+  };
+  auto store_b = [&](int buf) {
+    const uint32_t dst = lds_addr(btile + buf * kPfBBytes + r * kPfBStride + h * 64);
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      *(lds_u4)(size_t)(dst + 16u * v) = u32x4v{pk[4 * v], pk[4 * v + 1], pk[4 * v + 2], pk[4 * v + 3]};
+  };
+  auto decode_all = [&](const uint32_t (&P)[Q][4], auto Jc, int buf) {
+    fields_in(P, Jc);
+    fields_level<Q, 1>(R);
+    fields_out();
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+      lookup_addrs(bb);
+      lookups(bb);
+      pack(bb);
+    }
+    store_b(buf);
+  };
+
+  // A operand: lane (m = lane & 15, g = lane >> 4) holds token 16 tg + m of
+  // the wave's 128, K slots 8 g .. +8 of the sub-step's word.  Tokens past
+  // the tile's end read row 0 (their accumulator rows are never stored);
+  // words past the row's end read through an empty buffer (zeros).  The
+  // word's offset is a scalar, so an activation load costs no vector
+  // instruction.
+  const int m = lane & 15, g = lane >> 4;
+  const __amdgpu_buffer_rsrc_t ars = make_rsrc(A.act, A.act_bytes);
+  const __amdgpu_buffer_rsrc_t ars0 = make_rsrc(A.act, 0u);
+  uint32_t arow[kPfTG];
+#pragma unroll
+  for (int tg = 0; tg < kPfTG; ++tg) {
+    const int mt = kPfWM * wave + 16 * tg + m;
+    uint32_t row = 0;
+    if (mt < nm) {
+      const int pos = off_e + m0 + mt;
+      row = GU ? (uint32_t)(A.rt.perm[pos] / A.k) * (uint32_t)A.H * 2u : (uint32_t)pos * (uint32_t)A.I * 2u;
+    }
+    arow[tg] = row + 16u * (uint32_t)g;
+  }
+  // sub-step s = 2 k + hh of step k: word 8 (k >> 2) + 4 hh + (k & 3)
+  auto load_a = [&](u32x4v (&Ar)[kPfTG], int s) {
+    const int k = s >> 1, hh = s & 1;
+    const int wd = 8 * (k >> 2) + 4 * hh + (k & 3);
+    const bool in = wd < W;
+    const __amdgpu_buffer_rsrc_t rs = in ? ars : ars0;
+    const int woff = in ? 64 * wd : 0;
+#pragma unroll
+    for (int tg = 0; tg < kPfTG; ++tg)
+      Ar[tg] = __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)arow[tg], woff, 0));
+  };
+
+  float4v acc[kPfTG][kPfRG];
+#pragma unroll
+  for (int i = 0; i < kPfTG; ++i)
+#pragma unroll
+    for (int j = 0; j < kPfRG; ++j) acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  // B fragment of row group rg, sub-step hh, from buffer `buf`: lane (m, g)
+  // holds row 16 rg + m, K slots 8 g .. +8.
+  const uint32_t bbase = lds_addr(btile) + (uint32_t)(m * kPfBStride + 16 * g);
+  auto read_b = [&](int buf, int hh, int rg) -> u32x4v {
+    return *(lds_u4c)(size_t)(bbase + (uint32_t)(buf * kPfBBytes + 16 * rg * kPfBStride + hh * 64));
+  };
+  auto mma = [&](const u32x4v (&Ar)[kPfTG], const u32x4v& b, int rg) {
+#pragma unroll
+    for (int tg = 0; tg < kPfTG; ++tg)
+      acc[tg][rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8v, Ar[tg]),
+                                                           __builtin_bit_cast(half8v, b), acc[tg][rg], 0, 0, 0);
+  };
+  constexpr int kMfma = 0x008, kValu = 0x002;
+
+  // Prologue: planes of quads 0 and 1, activations of sub-step 0; tables in;
+  // decode step 0 into buffer 0; the fields of step 1.
+  uint32_t P0[Q][4], P1[Q][4];
+  u32x4v A0[kPfTG], A1[kPfTG];
+  load_quad(P0, 0);
+  load_quad(P1, 1);
+  load_a(A0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the tables and the first planes have landed
+  __syncthreads();
+  decode_all(P0, std::integral_constant<int, 0>{}, 0);
+  fields_in(P0, std::integral_constant<int, 1>{});
+  fields_level<Q, 1>(R);
+  fields_out();
+  __syncthreads();
+
+  // Step k: products of sub-step 0 (A0) and sub-step 1 (A1) from buffer
+  // k & 1; the decode of step k + 1 into the other buffer from the fields
+  // computed in step k - 1; the fields of step k + 2 (after the last steps
+  // this decodes zero planes into buffers nobody reads; plane and activation
+  // loads past the end read zero).  Sixteen pieces, one per row group and
+  // sub-step.  A piece first issues its memory operations (the next piece's
+  // B fragment, the lookups of one byte, the B-tile stores, the activation
+  // and plane loads), then, in a block of its own, its eight products
+  // interleaved with a part of the decode's vector work (fields, lookup
+  // addresses, packing), which so runs in the shadow of the matrix cores.
+  // The block is a branch on an always-true value the compiler cannot see
+  // through: the compiler keeps the pieces' order and their short register
+  // lifetimes, and since no memory operation sits inside a block, both ways
+  // around it leave the same loads in flight and the memory-counter waits
+  // stay exact.
+  // Word of step s: quad s >> 2, word s & 3 of it; quads alternate between
+  // P0 (even) and P1 (odd).  A quad's registers take the quad two ahead once
+  // the fields of its last word are done.  Unrolled over two quads so every
+  // plane-register index is static.
+  auto step = [&](auto Jf, uint32_t (&Pf)[Q][4], auto Ld, int k) {
+    constexpr int JF = decltype(Jf)::value;   // word of step k + 2 inside its quad (held in Pf)
+    constexpr bool LD = decltype(Ld)::value;  // JF == 3: Pf takes the quad two ahead afterwards
+    const int cur = k & 1;
+    u32x4v b = read_b(cur, 0, 0);
+    auto piece = [&](auto Ic) {
+      constexpr int I = decltype(Ic)::value;   // 0 .. 15: sub-step I / 8, row group I % 8
+      constexpr int HH = I / 8, RG = I % 8;
+      u32x4v bn = b;
+      if constexpr (I < 15) bn = read_b(cur, (I + 1) / 8, (I + 1) % 8);
+      if constexpr (I == 0) load_a(A1, 2 * k + 1);
+      if constexpr (I >= 1 && I <= 4) lookups(I - 1);
+      if constexpr (I == 6) store_b(cur ^ 1);
+      if constexpr (I == 8) load_a(A0, 2 * k + 2);
+      if constexpr (I == 11 && LD) load_quad(Pf, ((k + 2) >> 2) + 2);
+      if (always_true()) {
+        mma(HH == 0 ? A0 : A1, b, RG);
+        if constexpr (I <= 3) lookup_addrs(I);
+        if constexpr (I >= 2 && I <= 5) pack(I - 2);
+        if constexpr (I == 8) fields_in(Pf, Jf);
+        if constexpr (I == 9) fields_level<Q, 1>(R);
+        if constexpr (I == 10) fields_out();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kValu, 3, 0);
+        }
+      }
+      b = bn;
+    };
+    piece(std::integral_constant<int, 0>{});
+    piece(std::integral_constant<int, 1>{});
+    piece(std::integral_constant<int, 2>{});
+    piece(std::integral_constant<int, 3>{});
+    piece(std::integral_constant<int, 4>{});
+    piece(std::integral_constant<int, 5>{});
+    piece(std::integral_constant<int, 6>{});
+    piece(std::integral_constant<int, 7>{});
+    piece(std::integral_constant<int, 8>{});
+    piece(std::integral_constant<int, 9>{});
+    piece(std::integral_constant<int, 10>{});
+    piece(std::integral_constant<int, 11>{});
+    piece(std::integral_constant<int, 12>{});
+    piece(std::integral_constant<int, 13>{});
+    piece(std::integral_constant<int, 14>{});
+    piece(std::integral_constant<int, 15>{});
+    __syncthreads();
+  };
+  using std::integral_constant;
+  using F = integral_constant<bool, false>;
+  using T = integral_constant<bool, true>;
+  for (int k0 = 0; k0 < nsteps; k0 += 8) {
+    step(integral_constant<int, 2>{}, P0, F{}, k0);
+    step(integral_constant<int, 3>{}, P0, T{}, k0 + 1);
+    step(integral_constant<int, 0>{}, P1, F{}, k0 + 2);
+    step(integral_constant<int, 1>{}, P1, F{}, k0 + 3);
+    if (k0 + 4 >= nsteps) break;
+    step(integral_constant<int, 2>{}, P1, F{}, k0 + 4);
+    step(integral_constant<int, 3>{}, P1, T{}, k0 + 5);
+    step(integral_constant<int, 0>{}, P0, F{}, k0 + 6);
+    step(integral_constant<int, 1>{}, P0, F{}, k0 + 7);
+  }
+
+  // Epilogue.  acc[tg][rg] element v: token 128 wave + 16 tg + 4 g + v,
+  // MFMA column m = device row 128 nt + 16 rg + m.
+#pragma unroll
+  for (int tg = 0; tg < kPfTG; ++tg) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int mt = kPfWM * wave + 16 * tg + 4 * g + v;
+      const bool ok = mt < nm;
+      const size_t pos = (size_t)(off_e + m0 + mt);
+#pragma unroll
+      for (int rg = 0; rg < kPfRG; ++rg) {
+        const int dt = 8 * nt + rg;   // device tile
+        if constexpr (GU) {
+          const float gate = acc[tg][rg][v];
+          const float up = __shfl_xor(gate, 8, kWave);   // column m + 8 holds the matching up row
+          if (ok && m < 8 && 8 * dt + m < I) {
+            const _Float16 hh = (_Float16)(silu_f32(gate) * up);
+            A.hout[pos * I + 8 * dt + m] = __builtin_bit_cast(uint16_t, hh);
+          }
+        } else {
+          if (ok && 16 * dt + m < H) A.oout[(size_t)A.rt.perm[pos] * H + 16 * dt + m] = acc[tg][rg][v];
+        }
+      }
+    }
+  }
+}
+
+template <bool GU>
+__device__ __forceinline__ void pf_zero_tile(const MfmaArgs& A, int n_e, int off_e, int m0, int nt) {
+  const int nm = n_e - m0 < kPfTM ? n_e - m0 : kPfTM;
+  for (int i = threadIdx.x; i < nm * kPfTN; i += kPfThreads) {
+    const int mt = i / kPfTN, r = i % kPfTN;
+    const int dr = kPfTN * nt + r;
+    const size_t pos = (size_t)(off_e + m0 + mt);
+    if constexpr (GU) {
+      if ((dr & 15) < 8 && dr < 2 * A.I) A.hout[pos * A.I + 8 * (dr >> 4) + (dr & 7)] = 0;
+    } else {
+      if (dr < A.H) A.oout[(size_t)A.rt.perm[pos] * A.H + dr] = 0.0f;
     }
   }
   if (threadIdx.x == 0 && nt == 0 && m0 == 0) raise_status(A.rt.status, PW_DEV_BAD_BITWIDTH);
 }
 
 template <bool GU>
-__global__ __launch_bounds__(kMfmaThreads) void mfma_kernel(MfmaArgs A) {
-  __shared__ __align__(16) uint8_t lds[kMfmaLds];
+__global__ __launch_bounds__(kPfThreads, 1) void mfma_kernel(MfmaArgs A) {
+  __shared__ __align__(1024) uint8_t lds[kPfLds];
   // deal items so that one XCD works through consecutive items
   const int per_xcd = A.grid / kXcds;
   const int item = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
@@ -506,26 +415,14 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_kernel(MfmaArgs A) {
   const int n_e = uniform(A.rt.counts[e]);
   const int off_e = uniform(A.rt.offsets[e]);
   const int qv = uniform(A.q[2 * e + (GU ? 0 : 1)]);
-  if (qv < kMinBits || qv > kMaxBits) {
-    mfma_zero_tile<GU>(A, n_e, off_e, m0, nt);
-  } else if (n_e - m0 >= kDirectBelow || !A.direct_ok) {
-    switch (qv) {
-      case 3: mfma_tile<3, GU>(A, e, n_e, off_e, m0, nt, lds); break;
-      case 4: mfma_tile<4, GU>(A, e, n_e, off_e, m0, nt, lds); break;
-      case 5: mfma_tile<5, GU>(A, e, n_e, off_e, m0, nt, lds); break;
-      case 6: mfma_tile<6, GU>(A, e, n_e, off_e, m0, nt, lds); break;
-      case 7: mfma_tile<7, GU>(A, e, n_e, off_e, m0, nt, lds); break;
-      default: mfma_tile<8, GU>(A, e, n_e, off_e, m0, nt, lds); break;
-    }
-  } else {
-    switch (qv) {
-      case 3: mfma_tile_direct<3, GU>(A, e, n_e, off_e, m0, nt, lds); break;
-      case 4: mfma_tile_direct<4, GU>(A, e, n_e, off_e, m0, nt, lds); break;
-      case 5: mfma_tile_direct<5, GU>(A, e, n_e, off_e, m0, nt, lds); break;
-      case 6: mfma_tile_direct<6, GU>(A, e, n_e, off_e, m0, nt, lds); break;
-      case 7: mfma_tile_direct<7, GU>(A, e, n_e, off_e, m0, nt, lds); break;
-      default: mfma_tile_direct<8, GU>(A, e, n_e, off_e, m0, nt, lds); break;
-    }
+  switch (qv) {
+    case 3: pf_tile<3, GU>(A, e, n_e, off_e, m0, nt, lds); break;
+    case 4: pf_tile<4, GU>(A, e, n_e, off_e, m0, nt, lds); break;
+    case 5: pf_tile<5, GU>(A, e, n_e, off_e, m0, nt, lds); break;
+    case 6: pf_tile<6, GU>(A, e, n_e, off_e, m0, nt, lds); break;
+    case 7: pf_tile<7, GU>(A, e, n_e, off_e, m0, nt, lds); break;
+    case 8: pf_tile<8, GU>(A, e, n_e, off_e, m0, nt, lds); break;
+    default: pf_zero_tile<GU>(A, n_e, off_e, m0, nt); break;
   }
 }
 
@@ -536,15 +433,16 @@ static hipError_t launch_mfma(const ExpertArgs& a, const uint16_t* act, uint16_t
   A.H = a.H; A.I = a.I; A.E = a.E; A.k = a.k; A.T = a.T;
   A.blocks = a.blocks; A.q = a.q; A.rt = a.rt;
   A.act = act; A.hout = h; A.oout = o;
-  A.ntiles = GU ? (a.I + 63) / 64 : (a.H + kTN - 1) / kTN;
+  A.ntiles = ((GU ? 2 * a.I : a.H) + kPfTN - 1) / kPfTN;
   const long long act_bytes = 2LL * (GU ? (long long)a.T * a.H : (long long)a.T * a.k * a.I);
-  A.direct_ok = act_bytes < 0x80000000LL ? 1 : 0;
+  if (act_bytes >= 0x80000000LL) return hipErrorInvalidValue;   // the A operand is addressed with 32-bit offsets
+  A.act_bytes = (uint32_t)act_bytes;
   const long long items = (long long)mtile_bound(a.E, a.T, a.k) * A.ntiles;
   const long long grid = (items + kXcds - 1) / kXcds * kXcds;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   A.grid = (int)grid;
-  return launch_kernel(mfma_kernel<GU>, dim3((unsigned)grid), dim3(kMfmaThreads), s, ev, A);
+  return launch_kernel(mfma_kernel<GU>, dim3((unsigned)grid), dim3(kPfThreads), s, ev, A);
 }
 
 hipError_t launch_mfma_gate_up(const ExpertArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s,

@@ -406,10 +406,10 @@ def test_forward_mfma_forced(torch, name, T):
 
 
 def test_forward_mfma_ragged_shapes(torch):
-    # the last case gives each expert one full 256-token tile and a partial one,
-    # with both K ranges ending half way through a 64-wide step
+    # the last case gives each expert one full 512-token tile and a partial one,
+    # with both K ranges ending inside a quad of eight plane words
     for (H, I, E, k, T, seed) in [(2080, 96, 5, 3, 70, 41), (96, 1056, 4, 4, 45, 42), (256, 512, 2, 1, 300, 43),
-                                  (160, 96, 2, 2, 260, 44)]:
+                                  (160, 96, 2, 2, 260, 44), (160, 96, 2, 2, 600, 46)]:
         L = custom_layer(H, I, E, k, T, seed)
         say(f"forward mfma ragged H={H} I={I} E={E} k={k} T={T}")
         _, y = run_forward(torch, L, B.PW_PATH_MFMA)
@@ -432,8 +432,8 @@ def test_forward_qwen_batched_auto_mixes_paths(torch):
 
 
 # Full-size prefill (T = 4096, E = 8, top-2, skewed bitwidths).  Every expert
-# gets about 1000 slots, i.e. four or five 256-slot MFMA tiles, the last one
-# partial (fewer than 128 slots takes the direct-activation variant).  Each pair
+# gets about 1000 slots, i.e. two or three 512-slot MFMA tiles, the last one
+# partial (some with fewer tokens than one wave's 128).  Each pair
 # test drops every slot outside two experts (ids -> -1): those experts' slots,
 # their order and hence their MFMA tiles stay exactly as in the full call, and
 # every token routed to them is compared with the oracle over the same ids, so
@@ -495,15 +495,15 @@ def test_forward_mixtral_prefill_expert_pairs_all_tokens(torch, pair):
 
 
 def _c4_strata():
-    """For every expert: 4 tokens from its first 256-slot tile and 4 from its last."""
+    """For every expert: 4 tokens from its first 512-slot tile and 4 from its last."""
     L = _c4_layer()
     flat = L.ids.reshape(-1)
     toks = set()
     for e in range(L.wl.E):
         slots = np.nonzero(flat == e)[0]          # slot order = the expert's sorted order
-        ntile = (len(slots) + 255) // 256
-        first = slots[:256] // L.wl.k
-        last = slots[256 * (ntile - 1):] // L.wl.k
+        ntile = (len(slots) + 511) // 512
+        first = slots[:512] // L.wl.k
+        last = slots[512 * (ntile - 1):] // L.wl.k
         for part in (first, last):
             pick = np.unique(part)
             toks.update(int(t) for t in pick[np.linspace(0, len(pick) - 1, 4).astype(int)])
