@@ -294,7 +294,8 @@ __device__ __forceinline__ uint32_t buf_load_u32(__amdgpu_buffer_rsrc_t r, uint3
 
 constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset that reads as zero
 
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+// z * sigmoid(z) with the hardware reciprocal (1 ulp) in place of a division.
+__device__ __forceinline__ float silu_f32(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // Weighted top-k combine of token t at hidden positions n .. n+3:
 // sum over j < k, ascending, of w[t][j] * o[t k + j][n ..] (each o row the sum

@@ -46,6 +46,24 @@ inline int down_kparts(int H, int I, int E, int k, int T) {
   return kp < 1 ? 1 : kp;
 }
 
+// Parts of the down product's K range for the MFMA kernels when they run
+// alone (prefill): the down product has few row tiles (H / 128), so with
+// few token tiles its workgroups would fill the CUs only two or three times
+// over and the last round would run mostly empty.  Parts double until there
+// are enough (token tile, row tile, part) items for about four rounds, each
+// part keeping at least sixteen quads of eight plane words.
+constexpr int kNumCUs = 256;
+inline int mfma_down_kparts(int H, int I, int E, int k, int T) {
+  (void)E;
+  const long long slots = (long long)T * k;
+  if (slots <= 0) return 1;
+  const long long items = (slots + kMfmaTileM - 1) / kMfmaTileM * ((H + 127) / 128);
+  const int quads = (I / 32 + 7) / 8;
+  int kp = 1;
+  while (kp < 4 && items * kp < 4LL * kNumCUs && quads >= 16 * 2 * kp) kp *= 2;
+  return kp;
+}
+
 // Workspace layout (byte offsets from the workspace base).  The first 256
 // bytes are the header: status word, active-expert count.
 struct WsLayout {
@@ -73,7 +91,8 @@ inline WsLayout ws_layout(int H, int I, int E, int k, int T) {
   WsLayout L;
   size_t off = kAlign;
   const size_t slots = (size_t)T * (size_t)k;
-  const size_t kp = (size_t)down_kparts(H, I, E, k, T);
+  const int kpg = down_kparts(H, I, E, k, T), kpm = mfma_down_kparts(H, I, E, k, T);
+  const size_t kp = (size_t)(kpg > kpm ? kpg : kpm);
   L.counts = off;  off = align_up(off + sizeof(int32_t) * E, kAlign);
   L.offsets = off; off = align_up(off + sizeof(int32_t) * (E + 1), kAlign);
   L.active = off;  off = align_up(off + sizeof(int32_t) * E, kAlign);
@@ -125,6 +144,7 @@ struct ExpertArgs {
   Route rt;
   int min_tokens;   // process experts with min_tokens <= n_e < max_tokens
   int max_tokens;
+  int kparts;       // parts of the down product's K range (MFMA kernels running alone)
 };
 
 // Everything the GEMV kernels need for one call.

@@ -29,9 +29,9 @@
 // device layout's interleave), so SwiGLU pairs MFMA columns n and n + 8.
 //
 // Work items are (token tile, row tile) pairs; token tiles come from the route
-// kernel's list.  Consecutive items on one XCD (workgroups are dealt to the 8
-// XCDs round-robin) sweep the row tiles of one token tile, so its activation
-// rows stay in that XCD's L2.
+// kernel's list.  The items are dealt evenly over the 8 XCDs, a run of
+// consecutive items each, which sweeps the row tiles of one token tile, so its
+// activation rows stay in that XCD's L2.
 #include <type_traits>
 
 #include "pw_device.h"
@@ -79,12 +79,14 @@ struct MfmaArgs {
   uint16_t* hout;        // gate_up output
   float* oout;           // down output
   int ntiles;            // row tiles per block
-  int grid;              // launched workgroups (multiple of 8)
+  int kparts;            // parts of the K range (down product), each its own items and o slice
+  size_t part_stride;    // floats between the o slices of two parts
   uint32_t act_bytes;    // activation bytes (< 2^31): out-of-range offsets read zero
 };
 
 template <int Q, bool GU>
-__device__ __forceinline__ void pf_tile(const MfmaArgs& A, int e, int n_e, int off_e, int m0, int nt, uint8_t* lds) {
+__device__ __forceinline__ void pf_tile(const MfmaArgs& A, int e, int n_e, int off_e, int m0, int nt, int part,
+                                        uint8_t* lds) {
   constexpr int TAB = (1 << Q) * 2;
   constexpr int TSTRIDE = kTabStride<Q>;
   const int tid = threadIdx.x;
@@ -94,7 +96,14 @@ __device__ __forceinline__ void pf_tile(const MfmaArgs& A, int e, int n_e, int o
   const int N = GU ? 2 * I : H;
   const int K = GU ? H : I;
   const int W = K >> 5;
-  const int nq = (W + 7) >> 3;             // quads of four K steps
+  // K part `part` of A.kparts: quads [q0, q0 + nq) of the row's eight-word
+  // quads, words [w0, w1)
+  const int nqa = (W + 7) >> 3;
+  const int nqp = (nqa + A.kparts - 1) / A.kparts;
+  const int q0 = part * nqp;
+  const int nq = nqa - q0 < nqp ? (nqa - q0 > 0 ? nqa - q0 : 0) : nqp;
+  const int w0 = 8 * q0;
+  const int w1 = w0 + 8 * nq < W ? w0 + 8 * nq : W;
   const int nsteps = 4 * nq;
   const int nm = n_e - m0 < kPfTM ? n_e - m0 : kPfTM;
 
@@ -135,8 +144,8 @@ __device__ __forceinline__ void pf_tile(const MfmaArgs& A, int e, int n_e, int o
   const uint32_t skew4 = skew_of(r) * 0x01010101u;
   const bool vec = (W & 3) == 0;
   auto load_quad = [&](uint32_t (&P)[Q][4], int qd) {
-    const int wd = 8 * qd + 4 * h;
-    const bool live = qd < nq && wd < W && drow < N;
+    const int wd = w0 + 8 * qd + 4 * h;
+    const bool live = qd < nq && wd < w1 && drow < N;
     const uint32_t voff = live ? dev_word(drow, wd, W) * 4u : kOutOfRange;
     if (vec) {
 #pragma unroll
@@ -150,7 +159,7 @@ __device__ __forceinline__ void pf_tile(const MfmaArgs& A, int e, int n_e, int o
       for (int p = 0; p < Q; ++p)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          P[p][i] = buf_load_u32(prs, (live && wd + i < W) ? dev_word(drow, wd + i, W) * 4u : kOutOfRange,
+          P[p][i] = buf_load_u32(prs, (live && wd + i < w1) ? dev_word(drow, wd + i, W) * 4u : kOutOfRange,
                                  (uint32_t)p * pstride);
     }
   };
@@ -232,8 +241,8 @@ __device__ __forceinline__ void pf_tile(const MfmaArgs& A, int e, int n_e, int o
   // sub-step s = 2 k + hh of step k: word 8 (k >> 2) + 4 hh + (k & 3)
   auto load_a = [&](u32x4v (&Ar)[kPfTG], int s) {
     const int k = s >> 1, hh = s & 1;
-    const int wd = 8 * (k >> 2) + 4 * hh + (k & 3);
-    const bool in = wd < W;
+    const int wd = w0 + 8 * (k >> 2) + 4 * hh + (k & 3);
+    const bool in = wd < w1;
     const __amdgpu_buffer_rsrc_t rs = in ? ars : ars0;
     const int woff = in ? 64 * wd : 0;
 #pragma unroll
@@ -360,25 +369,48 @@ __device__ __forceinline__ void pf_tile(const MfmaArgs& A, int e, int n_e, int o
 
   // Epilogue.  acc[tg][rg] element v: token 128 wave + 16 tg + 4 g + v,
   // MFMA column m = device row 128 nt + 16 rg + m.
+  if constexpr (GU) {
+    // Column m < 8 holds gate row 8 dt + m, column m + 8 the matching up row.
+    // Per pair of elements (v, v + 1) the lanes of a column pair swap one
+    // value (DPP rotate by 8 within each row of 16 lanes): lane m < 8 then
+    // holds gate and up of token v, lane m + 8 those of token v + 1, and
+    // each computes one SwiGLU output.
+    const bool lo = m < 8;
+    const int col = m & 7;
 #pragma unroll
-  for (int tg = 0; tg < kPfTG; ++tg) {
+    for (int tg = 0; tg < kPfTG; ++tg) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int mt = kPfWM * wave + 16 * tg + 4 * g + v;
-      const bool ok = mt < nm;
-      const size_t pos = (size_t)(off_e + m0 + mt);
+      for (int v = 0; v < 4; v += 2) {
+        const int mt = kPfWM * wave + 16 * tg + 4 * g + v + (lo ? 0 : 1);
+        const bool ok = mt < nm;
+        const size_t pos = (size_t)(off_e + m0 + mt);
 #pragma unroll
-      for (int rg = 0; rg < kPfRG; ++rg) {
-        const int dt = 8 * nt + rg;   // device tile
-        if constexpr (GU) {
-          const float gate = acc[tg][rg][v];
-          const float up = __shfl_xor(gate, 8, kWave);   // column m + 8 holds the matching up row
-          if (ok && m < 8 && 8 * dt + m < I) {
+        for (int rg = 0; rg < kPfRG; ++rg) {
+          const int dt = 8 * nt + rg;   // device tile
+          const float a0 = acc[tg][rg][v], a1 = acc[tg][rg][v + 1];
+          const float recv = __builtin_bit_cast(
+              float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, lo ? a1 : a0), 0x128, 0xF, 0xF, false));
+          const float gate = lo ? a0 : recv;
+          const float up = lo ? recv : a1;
+          if (ok && 8 * dt + col < I) {
             const _Float16 hh = (_Float16)(silu_f32(gate) * up);
-            A.hout[pos * I + 8 * dt + m] = __builtin_bit_cast(uint16_t, hh);
+            A.hout[pos * I + 8 * dt + col] = __builtin_bit_cast(uint16_t, hh);
           }
-        } else {
-          if (ok && 16 * dt + m < H) A.oout[(size_t)A.rt.perm[pos] * H + 16 * dt + m] = acc[tg][rg][v];
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int tg = 0; tg < kPfTG; ++tg) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int mt = kPfWM * wave + 16 * tg + 4 * g + v;
+        if (mt >= nm) continue;
+        const size_t orow = (size_t)part * A.part_stride + (size_t)A.rt.perm[off_e + m0 + mt] * H;
+#pragma unroll
+        for (int rg = 0; rg < kPfRG; ++rg) {
+          const int dt = 8 * nt + rg;   // device tile
+          if (16 * dt + m < H) A.oout[orow + 16 * dt + m] = acc[tg][rg][v];
         }
       }
     }
@@ -386,7 +418,7 @@ __device__ __forceinline__ void pf_tile(const MfmaArgs& A, int e, int n_e, int o
 }
 
 template <bool GU>
-__device__ __forceinline__ void pf_zero_tile(const MfmaArgs& A, int n_e, int off_e, int m0, int nt) {
+__device__ __forceinline__ void pf_zero_tile(const MfmaArgs& A, int n_e, int off_e, int m0, int nt, int part) {
   const int nm = n_e - m0 < kPfTM ? n_e - m0 : kPfTM;
   for (int i = threadIdx.x; i < nm * kPfTN; i += kPfThreads) {
     const int mt = i / kPfTN, r = i % kPfTN;
@@ -395,34 +427,42 @@ __device__ __forceinline__ void pf_zero_tile(const MfmaArgs& A, int n_e, int off
     if constexpr (GU) {
       if ((dr & 15) < 8 && dr < 2 * A.I) A.hout[pos * A.I + 8 * (dr >> 4) + (dr & 7)] = 0;
     } else {
-      if (dr < A.H) A.oout[(size_t)A.rt.perm[pos] * A.H + dr] = 0.0f;
+      if (dr < A.H) A.oout[(size_t)part * A.part_stride + (size_t)A.rt.perm[pos] * A.H + dr] = 0.0f;
     }
   }
-  if (threadIdx.x == 0 && nt == 0 && m0 == 0) raise_status(A.rt.status, PW_DEV_BAD_BITWIDTH);
+  if (threadIdx.x == 0 && nt == 0 && m0 == 0 && part == 0) raise_status(A.rt.status, PW_DEV_BAD_BITWIDTH);
 }
 
 template <bool GU>
 __global__ __launch_bounds__(kPfThreads, 1) void mfma_kernel(MfmaArgs A) {
   __shared__ __align__(1024) uint8_t lds[kPfLds];
-  // deal items so that one XCD works through consecutive items
-  const int per_xcd = A.grid / kXcds;
-  const int item = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  const int mi = item / A.ntiles;
+  // Workgroups go to the eight XCDs round-robin (workgroup i to XCD i mod 8)
+  // and the grid is sized for the most token tiles routing can produce.  The
+  // items that exist (token tiles x row tiles, counted on the device) are
+  // dealt evenly, a run of consecutive items per XCD, so the XCDs finish
+  // together and one XCD sweeps the row tiles of a token tile, whose
+  // activation rows then stay in its L2.
+  const int nitems = uniform(*A.rt.num_mtiles) * A.kparts * A.ntiles;
+  const int per_xcd = (nitems + kXcds - 1) / kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int item = (blockIdx.x % kXcds) * per_xcd + slot;
+  if (slot >= per_xcd || item >= nitems) return;
+  const int mi = item / (A.kparts * A.ntiles);
+  const int part = item / A.ntiles % A.kparts;
   const int nt = item % A.ntiles;
-  if (mi >= uniform(*A.rt.num_mtiles)) return;
   const int e = uniform(A.rt.mtiles[2 * mi]);
   const int m0 = uniform(A.rt.mtiles[2 * mi + 1]);
   const int n_e = uniform(A.rt.counts[e]);
   const int off_e = uniform(A.rt.offsets[e]);
   const int qv = uniform(A.q[2 * e + (GU ? 0 : 1)]);
   switch (qv) {
-    case 3: pf_tile<3, GU>(A, e, n_e, off_e, m0, nt, lds); break;
-    case 4: pf_tile<4, GU>(A, e, n_e, off_e, m0, nt, lds); break;
-    case 5: pf_tile<5, GU>(A, e, n_e, off_e, m0, nt, lds); break;
-    case 6: pf_tile<6, GU>(A, e, n_e, off_e, m0, nt, lds); break;
-    case 7: pf_tile<7, GU>(A, e, n_e, off_e, m0, nt, lds); break;
-    case 8: pf_tile<8, GU>(A, e, n_e, off_e, m0, nt, lds); break;
-    default: pf_zero_tile<GU>(A, n_e, off_e, m0, nt); break;
+    case 3: pf_tile<3, GU>(A, e, n_e, off_e, m0, nt, part, lds); break;
+    case 4: pf_tile<4, GU>(A, e, n_e, off_e, m0, nt, part, lds); break;
+    case 5: pf_tile<5, GU>(A, e, n_e, off_e, m0, nt, part, lds); break;
+    case 6: pf_tile<6, GU>(A, e, n_e, off_e, m0, nt, part, lds); break;
+    case 7: pf_tile<7, GU>(A, e, n_e, off_e, m0, nt, part, lds); break;
+    case 8: pf_tile<8, GU>(A, e, n_e, off_e, m0, nt, part, lds); break;
+    default: pf_zero_tile<GU>(A, n_e, off_e, m0, nt, part); break;
   }
 }
 
@@ -434,14 +474,15 @@ static hipError_t launch_mfma(const ExpertArgs& a, const uint16_t* act, uint16_t
   A.blocks = a.blocks; A.q = a.q; A.rt = a.rt;
   A.act = act; A.hout = h; A.oout = o;
   A.ntiles = ((GU ? 2 * a.I : a.H) + kPfTN - 1) / kPfTN;
+  A.kparts = GU ? 1 : (a.kparts > 0 ? a.kparts : 1);
+  A.part_stride = (size_t)a.T * a.k * a.H;
   const long long act_bytes = 2LL * (GU ? (long long)a.T * a.H : (long long)a.T * a.k * a.I);
   if (act_bytes >= 0x80000000LL) return hipErrorInvalidValue;   // the A operand is addressed with 32-bit offsets
   A.act_bytes = (uint32_t)act_bytes;
-  const long long items = (long long)mtile_bound(a.E, a.T, a.k) * A.ntiles;
+  const long long items = (long long)mtile_bound(a.E, a.T, a.k) * A.kparts * A.ntiles;
   const long long grid = (items + kXcds - 1) / kXcds * kXcds;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-  A.grid = (int)grid;
   return launch_kernel(mfma_kernel<GU>, dim3((unsigned)grid), dim3(kPfThreads), s, ev, A);
 }
 

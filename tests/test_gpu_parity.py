@@ -406,12 +406,16 @@ def test_forward_mfma_forced(torch, name, T):
 
 
 def test_forward_mfma_ragged_shapes(torch):
-    # the last case gives each expert one full 512-token tile and a partial one,
-    # with both K ranges ending inside a quad of eight plane words
+    # (160, 96, .., 600) gives each expert one full 512-token tile and a partial
+    # one, with both K ranges ending inside a quad of eight plane words; the
+    # last case runs the down product in two K parts (33 quads: 17 + 16, the
+    # last one partial)
     for (H, I, E, k, T, seed) in [(2080, 96, 5, 3, 70, 41), (96, 1056, 4, 4, 45, 42), (256, 512, 2, 1, 300, 43),
-                                  (160, 96, 2, 2, 260, 44), (160, 96, 2, 2, 600, 46)]:
+                                  (160, 96, 2, 2, 260, 44), (160, 96, 2, 2, 600, 46), (256, 8224, 2, 1, 300, 47)]:
         L = custom_layer(H, I, E, k, T, seed)
-        say(f"forward mfma ragged H={H} I={I} E={E} k={k} T={T}")
+        info = B.pw_moe_path_info(B.shape(H, I, E, k), T, B.make_options(path=B.PW_PATH_MFMA))
+        say(f"forward mfma ragged H={H} I={I} E={E} k={k} T={T} down K parts={info.down_kparts}")
+        assert info.down_kparts == (2 if I == 8224 else 1)
         _, y = run_forward(torch, L, B.PW_PATH_MFMA)
         compare(y, oracle_y(L), f"mfma ragged H={H} I={I}")
 
