@@ -93,10 +93,13 @@ pw_status make_plan(const pw_moe_shape* shape, int32_t T, const pw_moe_options* 
   pl.b1 = b1;
   pl.b2 = b2;
   pl.inline_route = max_slots <= 64 && !pl.mfma && !pl.mgemv;
-  // the families write one K part of o each, except one family running alone:
-  // the GEMV or the MFMA kernels then split the down product's K range
-  if (pl.mfma) pl.kparts = (pl.mgemv || pl.gemv) ? 1 : mfma_down_kparts(H, I, E, k, T);
-  else pl.kparts = pl.mgemv ? 1 : down_kparts(H, I, E, k, T);
+  // the families write one K part of o each, except one family running alone,
+  // which then splits the down product's K range
+  const int nfam = (int)pl.mfma + (int)pl.mgemv + (int)pl.gemv;
+  if (nfam != 1) pl.kparts = 1;
+  else if (pl.mfma) pl.kparts = mfma_down_kparts(H, I, E, k, T);
+  else if (pl.mgemv) pl.kparts = mgemv_down_kparts(H, I, E, k, T);
+  else pl.kparts = down_kparts(H, I, E, k, T);
   return PW_OK;
 }
 
@@ -151,7 +154,7 @@ pw_status forward_on(const pw_moe_shape* shape, int32_t T, const uint16_t* x, co
 
   const bool inline_route = pl.inline_route;
   ExpertArgs mfma{H, I, E, k, T, blocks, q, rt, thresh == 0 ? 1 : thresh, INT_MAX, pl.mfma ? pl.kparts : 1};
-  ExpertArgs mg{H, I, E, k, T, blocks, q, rt, b1 == 0 ? 1 : b1, b2, 1};
+  ExpertArgs mg{H, I, E, k, T, blocks, q, rt, b1 == 0 ? 1 : b1, b2, pl.mgemv ? pl.kparts : 1};
   GemvLaunch g{};
   g.H = H; g.I = I; g.E = E; g.k = k; g.T = T;
   g.blocks = blocks; g.q = q; g.ids = ids; g.rt = rt;

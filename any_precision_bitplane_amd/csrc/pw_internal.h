@@ -64,6 +64,25 @@ inline int mfma_down_kparts(int H, int I, int E, int k, int T) {
   return kp;
 }
 
+// Parts of the down product's K range for the matrix-core GEMV when it runs
+// alone: a 32-row chunk of the down block walks all of I, and with few token
+// tiles (decode batches: about one per routed expert) there are too few
+// (tile, chunk) items to keep eight waves on every CU.  Parts double until
+// there are about 4096 items, each part keeping at least eight super-chunks
+// of eight plane words.
+inline int mgemv_down_kparts(int H, int I, int E, int k, int T) {
+  const long long slots = (long long)T * k;
+  if (slots <= 0) return 1;
+  const long long tiles = (E < slots ? E : slots) > (slots + kMgTileM - 1) / kMgTileM
+                              ? (E < slots ? E : slots)
+                              : (slots + kMgTileM - 1) / kMgTileM;
+  const long long items = tiles * ((H + 31) / 32);
+  const int supers = (I / 32 + 7) / 8;
+  int kp = 1;
+  while (kp < 8 && items * kp < 4096 && supers >= 8 * 2 * kp) kp *= 2;
+  return kp;
+}
+
 // Workspace layout (byte offsets from the workspace base).  The first 256
 // bytes are the header: status word, active-expert count.
 struct WsLayout {
@@ -92,7 +111,9 @@ inline WsLayout ws_layout(int H, int I, int E, int k, int T) {
   size_t off = kAlign;
   const size_t slots = (size_t)T * (size_t)k;
   const int kpg = down_kparts(H, I, E, k, T), kpm = mfma_down_kparts(H, I, E, k, T);
-  const size_t kp = (size_t)(kpg > kpm ? kpg : kpm);
+  const int kpv = mgemv_down_kparts(H, I, E, k, T);
+  const int kpx = kpg > kpm ? kpg : kpm;
+  const size_t kp = (size_t)(kpx > kpv ? kpx : kpv);
   L.counts = off;  off = align_up(off + sizeof(int32_t) * E, kAlign);
   L.offsets = off; off = align_up(off + sizeof(int32_t) * (E + 1), kAlign);
   L.active = off;  off = align_up(off + sizeof(int32_t) * E, kAlign);

@@ -4,36 +4,35 @@
 // kernel): every block is read at its own committed bitwidth q from the
 // device page table.
 //
-// A workgroup is one wave and owns 16 weight rows of one routed block for the
-// whole K range (gate_up: 8 gate rows and the matching 8 up rows; down: 16
-// rows).  Each weight is decoded exactly once, in registers, straight into the
-// matrix cores' B operand, and multiplies up to 32 tokens (two 16-token
-// groups) with v_mfma_f32_16x16x32_f16 -- no weight tile in LDS, no barrier in
-// the K loop.  For v_mfma_f32_16x16x32_f16 lane l supplies B column l & 15
-// (the weight row) and K slots 8 (l >> 4) .. +8, and A row l & 15 (the token)
-// at the same K slots.  The K order inside one instruction is free as long as
-// A and B agree, so lane group g = l >> 4 takes plane word w of its row (32
-// weights), transposes its q plane words into code fields once, looks the 32
-// weights up in the row's table in LDS, and feeds byte b of the word (weights
-// 8b .. 8b + 7) to sub-step b; the activations of sub-step b are
-// x[token][32 w + 8b .. +8], one 16-byte load.  In a 512-wide super-chunk C,
-// group g reads words 16 C + 4 g .. +4 with one load per plane (the four
-// groups cover a row's 64-byte line) and sub-chunk i uses word 16 C + 4 g + i.
-// Plane words are requested two super-chunks ahead and activations one
-// sub-chunk ahead.  gate_up pairs gate and up rows in columns n and n + 8, so
-// SwiGLU is one lane swap on the accumulators.
+// A workgroup is one wave and owns 32 device rows of one routed block (two
+// 16-row device tiles; gate_up: 16 gate rows and their 16 up rows) for the
+// whole K range and a tile of up to 32 tokens.  Each weight is decoded once,
+// in registers, straight into the B operand of v_mfma_f32_32x32x16_f16, whose
+// 32 x 32 output covers all 32 rows and all 32 tokens: one activation
+// fragment feeds 32 weight rows.  Lane l supplies B column l & 31 (the weight
+// row) and K slots 8 (l >> 5) .. +8, and A row l & 31 (the token) at the same
+// K slots.  The K order inside one instruction is free as long as A and B
+// agree, so lane half h = l >> 5 takes plane word w_h of its row (32
+// weights), transposes its q plane words into code fields, looks the 32
+// weights up in the row's table in LDS, and feeds byte b of the word
+// (weights 8b .. 8b + 7) to product b; the activations of product b are
+// x[token][32 w_h + 8b .. +8], one 16-byte load.  In a 256-wide super-chunk
+// C, half h reads words 8 C + 4 h .. +4 with one load per plane and
+// sub-chunk i uses word 8 C + 4 h + i.  Plane words are requested two
+// super-chunks ahead and activations one sub-chunk ahead.  gate_up pairs
+// gate and up rows in columns c and c + 8, so SwiGLU is one lane swap on the
+// accumulators.
 #include "pw_device.h"
 #include "pw_internal.h"
 
 namespace pw {
 
-constexpr int kMgRows = 16;
+constexpr int kMgRows = 32;
 constexpr long long kMgMaxGrid = 32768;   // workgroups per launch (several per SIMD)
-constexpr int kMgGroups = 2;                 // 16-token groups per wave
-static_assert(16 * kMgGroups == kMgTileM, "a tile fills the token groups");
+static_assert(kMgTileM == 32, "a tile fills the 32 MFMA rows");
 
 typedef _Float16 mg_half8 __attribute__((ext_vector_type(8)));
-typedef float mg_float4 __attribute__((ext_vector_type(4)));
+typedef float mg_float16 __attribute__((ext_vector_type(16)));
 
 struct MgArgs {
   int H, I, E, k, T;
@@ -43,29 +42,18 @@ struct MgArgs {
   const uint16_t* act;   // gate_up: x [T][H]; down: h [slots][I] by sorted position
   uint16_t* hout;
   float* oout;           // o [slots][H] by slot (one K part)
-  int chunks;            // row chunks per block
+  int chunks;            // 32-row chunks per block
+  int kparts;            // parts of the K range (down product), each its own items and o slice
+  size_t part_stride;    // floats between the o slices of two parts
   uint32_t act_bytes;    // < 2^31: out-of-range offsets read zero
 };
 
-// Tile-local row r (0..15) of chunk ch -> block row, and whether it exists.
-template <bool GU>
-__device__ __forceinline__ int mg_row(int ch, int r, int I, int H, bool& ok) {
-  if constexpr (GU) {
-    const int x = 8 * ch + (r & 7);
-    ok = x < I;
-    return (r < 8 ? 0 : I) + x;
-  } else {
-    const int x = 16 * ch + r;
-    ok = x < H;
-    return x;
-  }
-}
-
 template <int Q, bool GU>
-__device__ __forceinline__ void mg_chunk(const MgArgs& A, int e, int n_e, int off_e, int ch, uint8_t* tabs) {
+__device__ __forceinline__ void mg_chunk(const MgArgs& A, int e, int n_e, int off_e, int ch, int part,
+                                         uint8_t* tabs) {
   constexpr int TAB = (1 << Q) * 2;
   const int lane = threadIdx.x;
-  const int n = lane & 15, g = lane >> 4;
+  const int c = lane & 31, hf = lane >> 5;
   const int H = A.H, I = A.I;
   const int N = GU ? 2 * I : H;
   const int K = GU ? H : I;
@@ -76,22 +64,24 @@ __device__ __forceinline__ void mg_chunk(const MgArgs& A, int e, int n_e, int of
   const __amdgpu_buffer_rsrc_t prs = make_rsrc(uniform_ptr(d.planes), pstride * (uint32_t)Q);
   const uint16_t* __restrict__ lut = uniform_ptr(d.lut_all) + lut_offset(N, Q);
 
-  bool row_ok;
-  const int row = mg_row<GU>(ch, n, I, H, row_ok);
+  // the lane's row: device row 32 ch + c
+  const int drow = kMgRows * ch + c;
+  const bool row_ok = drow < N;
 
-  // K is walked in 512-wide super-chunks C: lane group g reads plane words
-  // 16 C + 4 g .. +4 of its row, and word 16 C + 4 g + i feeds sub-chunk i.
-  // The item's 16 rows are device tile ch (gate_up: 8 gate rows and their 8
-  // up rows), so the wave's load of one plane is the tile's contiguous 1 KB
-  // piece (less in a narrower last column tile).  With W % 4 == 0 a lane's
-  // four words are one aligned 16-byte load; otherwise four 4-byte loads.
-  // Words past the row's end are not read and count as zero.
-  const int ns = (W + 15) >> 4;
+  // K is walked in 256-wide super-chunks C: half h reads plane words
+  // 8 C + 4 h .. +4 of its row (the device layout keeps a row's 16-word run
+  // contiguous), and word 8 C + 4 h + i feeds sub-chunk i.  With W % 4 == 0
+  // a lane's four words are one aligned 16-byte load; otherwise four 4-byte
+  // loads.  Words past the row's end are not read and count as zero.
+  // K part `part` of A.kparts: super-chunks [C0, C0 + nsc)
+  const int nsa = (W + 7) >> 3;
+  const int nsp = (nsa + A.kparts - 1) / A.kparts;
+  const int C0 = part * nsp;
+  const int nsc = nsa - C0 < nsp ? (nsa - C0 > 0 ? nsa - C0 : 0) : nsp;
   const bool vec = (W & 3) == 0;
-  const int drow = 16 * ch + n;
   auto load_planes = [&](uint32_t (&P)[Q][4], int C) {
-    const int wd = 16 * C + 4 * g;
-    const bool live = row_ok && C < ns && wd < W;
+    const int wd = 8 * (C0 + C) + 4 * hf;
+    const bool live = row_ok && C < nsc && wd < W;
     const uint32_t voff = live ? dev_word(drow, wd, W) * 4u : kOutOfRange;
     if (vec) {
 #pragma unroll
@@ -113,52 +103,39 @@ __device__ __forceinline__ void mg_chunk(const MgArgs& A, int e, int n_e, int of
   load_planes(P0, 0);
   load_planes(P1, 1);
 
-  // the 16 row tables -> LDS, row r at r * TAB (rows outside the block read as zero)
-  for (int c = lane; c < kMgRows * TAB / 16; c += kWave) {
-    const int r = c / (TAB / 16), cc = c % (TAB / 16);
-    bool ok;
-    const int rr = mg_row<GU>(ch, r, I, H, ok);
+  // the 32 row tables -> LDS, row c at c * TAB (rows outside the block read as zero)
+  for (int i = lane; i < kMgRows * TAB / 16; i += kWave) {
+    const int r = i / (TAB / 16), cc = i % (TAB / 16);
+    const int dr = kMgRows * ch + r;
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (ok) v = *reinterpret_cast<const uint4*>(lut + (size_t)rr * (1 << Q) + cc * 8);
-    *reinterpret_cast<uint4*>(tabs + c * 16) = v;
+    if (dr < N) v = *reinterpret_cast<const uint4*>(lut + (size_t)canon_row(dr, I, GU) * (1 << Q) + cc * 8);
+    *reinterpret_cast<uint4*>(tabs + i * 16) = v;
   }
   __syncthreads();
-  const uint32_t base = lds_addr(tabs) + (uint32_t)(n * TAB);
+  const uint32_t base = lds_addr(tabs) + (uint32_t)(c * TAB);
 
-  // activation rows of the lane's token in each group (A row = lane & 15)
-  const int ntg = (n_e + 15) >> 4;
+  // activation row of the lane's token (A row = lane & 31); tokens past the
+  // tile read zero and their output rows are not stored
   const __amdgpu_buffer_rsrc_t ars = make_rsrc(A.act, A.act_bytes);
-  uint32_t aoff[kMgGroups];
-#pragma unroll
-  for (int tg = 0; tg < kMgGroups; ++tg) {
-    const int m = 16 * tg + n;
-    aoff[tg] = kOutOfRange;
-    if (m < n_e) {
-      const int pos = off_e + m;
-      aoff[tg] = GU ? (uint32_t)(A.rt.perm[pos] / A.k) * (uint32_t)H * 2u : (uint32_t)pos * (uint32_t)I * 2u;
-    }
+  uint32_t aoff = kOutOfRange;
+  if (c < n_e) {
+    const int pos = off_e + c;
+    aoff = GU ? (uint32_t)(A.rt.perm[pos] / A.k) * (uint32_t)H * 2u : (uint32_t)pos * (uint32_t)I * 2u;
   }
 
-  mg_float4 acc[kMgGroups];
-#pragma unroll
-  for (int tg = 0; tg < kMgGroups; ++tg) acc[tg] = mg_float4{0.f, 0.f, 0.f, 0.f};
+  mg_float16 acc = {};
 
-  // sub-chunk: plane word wd (its four plane bytes b = sub-steps)
-  // Software-pipelined sub-chunks (sub-chunk s = word 16 (s >> 2) + 4 g + (s & 3)):
+  // Software-pipelined sub-chunks (sub-chunk s = word 8 (s >> 2) + 4 h + (s & 3)):
   // each step issues its lookups, then requests the next sub-chunk's
   // activations and transposes its plane words while the lookups are in
   // flight, and only then multiplies.  Unrolled over two super-chunks so every
   // register index is static.
-  auto load_a = [&](uint4 (&ar)[kMgGroups][4], int s) {
-    const int wd = 16 * (s >> 2) + 4 * g + (s & 3);
+  auto load_a = [&](uint4 (&ar)[4], int s) {
+    const int wd = 8 * (C0 + (s >> 2)) + 4 * hf + (s & 3);
 #pragma unroll
-    for (int tg = 0; tg < kMgGroups; ++tg) {
-      if (tg >= ntg) continue;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const uint32_t voff = wd < W ? aoff[tg] + (uint32_t)(wd * 32 + 8 * b) * 2u : kOutOfRange;
-        ar[tg][b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ars, (int)voff, 0, 0));
-      }
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t voff = wd < W ? aoff + (uint32_t)(wd * 32 + 8 * b) * 2u : kOutOfRange;
+      ar[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ars, (int)voff, 0, 0));
     }
   };
   auto fields = [&](const uint32_t (&P)[Q][4], int i, uint32_t (&R)[8]) {
@@ -167,22 +144,17 @@ __device__ __forceinline__ void mg_chunk(const MgArgs& A, int e, int n_e, int of
     for (int p = 0; p < Q; ++p) W8[p] = P[p][i];
     planes_to_fields<Q>(W8, R);
   };
-  auto multiply = [&](const uint4 (&ar)[kMgGroups][4], const uint32_t (&packed)[16]) {
+  auto multiply = [&](const uint4 (&ar)[4], const uint32_t (&packed)[16]) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const mg_half8 bop = __builtin_bit_cast(
           mg_half8, make_uint4(packed[4 * b], packed[4 * b + 1], packed[4 * b + 2], packed[4 * b + 3]));
-#pragma unroll
-      for (int tg = 0; tg < kMgGroups; ++tg) {
-        if (tg >= ntg) continue;
-        acc[tg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(mg_half8, ar[tg][b]), bop, acc[tg], 0,
-                                                         0, 0);
-      }
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(mg_half8, ar[b]), bop, acc, 0, 0, 0);
     }
   };
 
-  const int S = 4 * ns;   // sub-chunks (past the last word they read zero activations)
-  uint4 A0[kMgGroups][4], A1[kMgGroups][4];
+  const int S = 4 * nsc;   // sub-chunks (past the last word they read zero activations)
+  uint4 A0[4], A1[4];
   uint32_t R[8];
   load_a(A0, 0);
   fields(P0, 0, R);
@@ -214,44 +186,52 @@ __device__ __forceinline__ void mg_chunk(const MgArgs& A, int e, int n_e, int of
   }
 #undef PW_MG_STEP
 
-  // acc[tg] element v: token 16 tg + 4 g + v, tile column n
+  // acc element i: token 8 (i / 4) + 4 h + i % 4, column c = device row 32 ch + c
+  if constexpr (GU) {
+    // Column c (c & 8 == 0) holds gate row 8 t + (c & 7) of device tile
+    // t = 2 ch + (c >> 4), column c + 8 the matching up row.  Per pair of
+    // elements (i, i + 1) the lanes of a column pair swap one value (DPP
+    // rotate by 8 within each row of 16 lanes): the gate lane then holds gate
+    // and up of token 8 (i / 4) + 4 h + i % 4, the up lane those of the next
+    // token, and each computes one SwiGLU output.
+    const bool lo = (c & 8) == 0;
+    const int col = 8 * (2 * ch + (c >> 4)) + (c & 7);
 #pragma unroll
-  for (int tg = 0; tg < kMgGroups; ++tg) {
-    if (tg >= ntg) continue;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = 16 * tg + 4 * g + v;
-      if constexpr (GU) {
-        const float gate = acc[tg][v];
-        const float up = __shfl_xor(gate, 8, kWave);   // column n + 8 holds the matching up row
-        if (n < 8 && row_ok && m < n_e) {
-          const _Float16 hh = (_Float16)(silu_f32(gate) * up);
-          A.hout[(size_t)(off_e + m) * I + 8 * ch + n] = __builtin_bit_cast(uint16_t, hh);
-        }
-      } else {
-        if (row_ok && m < n_e) {
-          const size_t slot = (size_t)A.rt.perm[off_e + m];
-          A.oout[slot * H + row] = acc[tg][v];
-        }
+    for (int i = 0; i < 16; i += 2) {
+      const float a0 = acc[i], a1 = acc[i + 1];
+      const float recv = __builtin_bit_cast(
+          float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, lo ? a1 : a0), 0x128, 0xF, 0xF, false));
+      const float gate = lo ? a0 : recv;
+      const float up = lo ? recv : a1;
+      const int m = 8 * (i >> 2) + 4 * hf + (i & 3) + (lo ? 0 : 1);
+      if (m < n_e && col < I) {
+        const _Float16 hh = (_Float16)(silu_f32(gate) * up);
+        A.hout[(size_t)(off_e + m) * I + col] = __builtin_bit_cast(uint16_t, hh);
       }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = 8 * (i >> 2) + 4 * hf + (i & 3);
+      if (row_ok && m < n_e) A.oout[(size_t)part * A.part_stride + (size_t)A.rt.perm[off_e + m] * H + drow] = acc[i];
     }
   }
 }
 
 template <bool GU>
-__device__ __forceinline__ void mg_zero(const MgArgs& A, int n_e, int off_e, int ch, bool first_tile) {
+__device__ __forceinline__ void mg_zero(const MgArgs& A, int n_e, int off_e, int ch, int part, bool first_tile) {
+  const int N = GU ? 2 * A.I : A.H;
   for (int i = threadIdx.x; i < n_e * kMgRows; i += kWave) {
     const int m = i / kMgRows, r = i % kMgRows;
-    bool ok;
-    const int row = mg_row<GU>(ch, r, A.I, A.H, ok);
-    if (!ok) continue;
+    const int dr = kMgRows * ch + r;
+    if (dr >= N) continue;
     if constexpr (GU) {
-      if (r < 8) A.hout[(size_t)(off_e + m) * A.I + 8 * ch + r] = 0;
+      if ((dr & 15) < 8) A.hout[(size_t)(off_e + m) * A.I + 8 * (dr >> 4) + (dr & 7)] = 0;
     } else {
-      A.oout[(size_t)A.rt.perm[off_e + m] * A.H + row] = 0.0f;
+      A.oout[(size_t)part * A.part_stride + (size_t)A.rt.perm[off_e + m] * A.H + dr] = 0.0f;
     }
   }
-  if (threadIdx.x == 0 && ch == 0 && first_tile) raise_status(A.rt.status, PW_DEV_BAD_BITWIDTH);
+  if (threadIdx.x == 0 && ch == 0 && part == 0 && first_tile) raise_status(A.rt.status, PW_DEV_BAD_BITWIDTH);
 }
 
 // Work items are (32-token tile, row chunk) pairs; the route kernel lists the
@@ -262,11 +242,12 @@ __device__ __forceinline__ void mg_zero(const MgArgs& A, int n_e, int off_e, int
 template <bool GU>
 __global__ __launch_bounds__(kWave) void mgemv_kernel(MgArgs A) {
   __shared__ __align__(16) uint8_t tabs[kMgRows * (1 << kMaxBits) * 2];
-  const int items = uniform(*A.rt.num_mgtiles) * A.chunks;
+  const int items = uniform(*A.rt.num_mgtiles) * A.kparts * A.chunks;
   for (int item = (int)blockIdx.x; item < items; item += (int)gridDim.x) {
     if (item != (int)blockIdx.x) __syncthreads();   // the previous item's lookups are done before new tables land
-    const int t = item / A.chunks;
-    const int ch = item - t * A.chunks;
+    const int t = item / (A.kparts * A.chunks);
+    const int part = item / A.chunks % A.kparts;
+    const int ch = item % A.chunks;
     const int e = uniform(A.rt.mgtiles[2 * t]);
     const int m0 = uniform(A.rt.mgtiles[2 * t + 1]);
     const int n_e = uniform(A.rt.counts[e]);
@@ -274,13 +255,13 @@ __global__ __launch_bounds__(kWave) void mgemv_kernel(MgArgs A) {
     const int off_e = uniform(A.rt.offsets[e]) + m0;
     const int qv = uniform(A.q[2 * e + (GU ? 0 : 1)]);
     switch (qv) {
-      case 3: mg_chunk<3, GU>(A, e, nm, off_e, ch, tabs); break;
-      case 4: mg_chunk<4, GU>(A, e, nm, off_e, ch, tabs); break;
-      case 5: mg_chunk<5, GU>(A, e, nm, off_e, ch, tabs); break;
-      case 6: mg_chunk<6, GU>(A, e, nm, off_e, ch, tabs); break;
-      case 7: mg_chunk<7, GU>(A, e, nm, off_e, ch, tabs); break;
-      case 8: mg_chunk<8, GU>(A, e, nm, off_e, ch, tabs); break;
-      default: mg_zero<GU>(A, nm, off_e, ch, m0 == 0); break;
+      case 3: mg_chunk<3, GU>(A, e, nm, off_e, ch, part, tabs); break;
+      case 4: mg_chunk<4, GU>(A, e, nm, off_e, ch, part, tabs); break;
+      case 5: mg_chunk<5, GU>(A, e, nm, off_e, ch, part, tabs); break;
+      case 6: mg_chunk<6, GU>(A, e, nm, off_e, ch, part, tabs); break;
+      case 7: mg_chunk<7, GU>(A, e, nm, off_e, ch, part, tabs); break;
+      case 8: mg_chunk<8, GU>(A, e, nm, off_e, ch, part, tabs); break;
+      default: mg_zero<GU>(A, nm, off_e, ch, part, m0 == 0); break;
     }
   }
 }
@@ -292,11 +273,13 @@ static hipError_t launch_mg(const ExpertArgs& a, const uint16_t* act, uint16_t* 
   A.H = a.H; A.I = a.I; A.E = a.E; A.k = a.k; A.T = a.T;
   A.blocks = a.blocks; A.q = a.q; A.rt = a.rt;
   A.act = act; A.hout = h; A.oout = o;
-  A.chunks = GU ? (a.I + 7) / 8 : (a.H + kMgRows - 1) / kMgRows;
+  A.chunks = ((GU ? 2 * a.I : a.H) + kMgRows - 1) / kMgRows;
+  A.kparts = GU ? 1 : (a.kparts > 0 ? a.kparts : 1);
+  A.part_stride = (size_t)a.T * a.k * a.H;
   const long long act_bytes = 2LL * (GU ? (long long)a.T * a.H : (long long)a.T * a.k * a.I);
   if (act_bytes >= 0x80000000LL) return hipErrorInvalidValue;
   A.act_bytes = (uint32_t)act_bytes;
-  long long grid = (long long)mgtile_bound(a.E, a.T, a.k) * A.chunks;
+  long long grid = (long long)mgtile_bound(a.E, a.T, a.k) * A.kparts * A.chunks;
   if (grid > 0x7FFFFFFFLL - kMgMaxGrid) return hipErrorInvalidValue;   // the kernel counts items in int
   const bool timed = ev.start || ev.stop;
   if ((grid == 0 || a.min_tokens >= a.max_tokens) && !timed) return hipSuccess;
