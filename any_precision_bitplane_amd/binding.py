@@ -71,7 +71,8 @@ class PwPageInfo(ctypes.Structure):
 
 class PwPathInfo(ctypes.Structure):
     _fields_ = [("gemv", c_int32), ("mgemv", c_int32), ("mfma", c_int32), ("mgemv_from", c_int32),
-                ("mfma_from", c_int32), ("inline_route", c_int32), ("down_kparts", c_int32), ("launches", c_int32)]
+                ("mfma_from", c_int32), ("inline_route", c_int32), ("down_kparts", c_int32), ("launches", c_int32),
+                ("mfma_tail", c_int32)]
 
 
 class PwPlanProblem(ctypes.Structure):

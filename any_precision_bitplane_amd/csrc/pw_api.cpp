@@ -54,6 +54,8 @@ struct Plan {
   int b1, b2;          // b2 == INT_MAX: no MFMA launch
   bool inline_route;   // <= 64 slots on the GEMV alone: the gate_up kernel routes
   int kparts;          // parts of the GEMV down product's K range
+  int tail;            // MFMA experts' last <= tail tokens past whole tiles take the
+                       // matrix-core GEMV (0: none); only the AUTO rule's prefill sets it
 };
 
 pw_status make_plan(const pw_moe_shape* shape, int32_t T, const pw_moe_options* opts, Plan& pl) {
@@ -93,8 +95,10 @@ pw_status make_plan(const pw_moe_shape* shape, int32_t T, const pw_moe_options* 
   pl.b1 = b1;
   pl.b2 = b2;
   pl.inline_route = max_slots <= 64 && !pl.mfma && !pl.mgemv;
-  // the families write one K part of o each, except one family running alone,
-  // which then splits the down product's K range
+  pl.tail = (path == PW_PATH_AUTO && !explicit_bands && pl.mfma && !pl.mgemv && !pl.gemv && mg_ok) ? kMfmaTailTokens : 0;
+  // the families write one K part of o each, except one family running alone
+  // (MFMA with its tails counts as one: the matrix-core GEMV then splits the
+  // K range as the MFMA kernels do), which then splits the down product's K range
   const int nfam = (int)pl.mfma + (int)pl.mgemv + (int)pl.gemv;
   if (nfam != 1) pl.kparts = 1;
   else if (pl.mfma) pl.kparts = mfma_down_kparts(H, I, E, k, T);
@@ -133,7 +137,8 @@ pw_status forward_on(const pw_moe_shape* shape, int32_t T, const uint16_t* x, co
   Plan pl;
   pw_status st = make_plan(shape, T, opts, pl);
   if (st != PW_OK) return st;
-  const bool use_gemv = pl.gemv, use_mg = pl.mgemv, use_mfma = pl.mfma;
+  const bool use_gemv = pl.gemv, use_mfma = pl.mfma;
+  const bool use_mg = pl.mgemv || pl.tail > 0;   // its band, or only the MFMA experts' tails
   const int b1 = pl.b1, b2 = pl.b2, thresh = pl.b2;
 
   Route rt;
@@ -154,7 +159,8 @@ pw_status forward_on(const pw_moe_shape* shape, int32_t T, const uint16_t* x, co
 
   const bool inline_route = pl.inline_route;
   ExpertArgs mfma{H, I, E, k, T, blocks, q, rt, thresh == 0 ? 1 : thresh, INT_MAX, pl.mfma ? pl.kparts : 1};
-  ExpertArgs mg{H, I, E, k, T, blocks, q, rt, b1 == 0 ? 1 : b1, b2, pl.mgemv ? pl.kparts : 1};
+  ExpertArgs mg{H, I, E, k, T, blocks, q, rt, pl.mgemv ? (b1 == 0 ? 1 : b1) : 1, pl.mgemv ? b2 : INT_MAX,
+                use_mg ? pl.kparts : 1};
   GemvLaunch g{};
   g.H = H; g.I = I; g.E = E; g.k = k; g.T = T;
   g.blocks = blocks; g.q = q; g.ids = ids; g.rt = rt;
@@ -185,8 +191,8 @@ pw_status forward_on(const pw_moe_shape* shape, int32_t T, const uint16_t* x, co
 
   hipError_t e = mark(PW_STAGE_ROUTE);
   if (e == hipSuccess && !inline_route)
-    e = launch_route(ids, T, k, E, use_mfma ? (thresh == 0 ? 1 : thresh) : INT_MAX, use_mg ? (b1 == 0 ? 1 : b1) : INT_MAX,
-                     use_mg ? b2 : INT_MAX, rt, s);
+    e = launch_route(ids, T, k, E, use_mfma ? (thresh == 0 ? 1 : thresh) : INT_MAX,
+                     pl.mgemv ? (b1 == 0 ? 1 : b1) : INT_MAX, pl.mgemv ? b2 : INT_MAX, pl.tail, rt, s);
   for (int product = 0; product < 2 && e == hipSuccess; ++product) {
     e = mark(product == 0 ? PW_STAGE_GATE_UP : PW_STAGE_DOWN);
     int done = 0;
@@ -299,13 +305,14 @@ pw_status pw_moe_path_info(const pw_moe_shape* shape, int32_t T, const pw_moe_op
   st = make_plan(shape, T, opts, pl);
   if (st != PW_OK) return st;
   info->gemv = pl.gemv ? 1 : 0;
-  info->mgemv = pl.mgemv ? 1 : 0;
+  info->mgemv = (pl.mgemv || pl.tail > 0) ? 1 : 0;
   info->mfma = pl.mfma ? 1 : 0;
   info->mgemv_from = pl.mgemv ? (pl.b1 == 0 ? 1 : pl.b1) : 0;
   info->mfma_from = pl.mfma ? (pl.b2 == 0 ? 1 : pl.b2) : 0;
   info->inline_route = pl.inline_route ? 1 : 0;
   info->down_kparts = pl.kparts;
-  const int families = (int)pl.gemv + (int)pl.mgemv + (int)pl.mfma;
+  info->mfma_tail = pl.tail;
+  const int families = (int)pl.gemv + (int)(pl.mgemv || pl.tail > 0) + (int)pl.mfma;
   info->launches = (pl.inline_route ? 0 : 1) + 2 * families + 1;
   return PW_OK;
 }

@@ -28,6 +28,13 @@ inline int mtile_bound(int E, int T, int k) {
 
 constexpr int kMgTileM = 32;      // tokens per matrix-core GEMV pass
 
+// Prefill: the tokens of an MFMA expert past its last whole 512-token tile
+// go to the matrix-core GEMV when there are at most this many.  An MFMA tile
+// costs the same whatever its token count (the weight decode and the products
+// of all its 512 token rows); a 32-token matrix-core GEMV tile of the same
+// expert costs about a quarter of it, so up to three such tiles win.
+constexpr int kMfmaTailTokens = 96;
+
 inline int mgtile_bound(int E, int T, int k) {
   const int slots = T * k;
   return (E < slots ? E : slots) + (slots + kMgTileM - 1) / kMgTileM;
@@ -202,8 +209,10 @@ inline hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, hipStream_t s, 
 }
 
 // Launchers (return hipSuccess or the launch error).
+// mfma_tail: an MFMA expert's tokens past its last whole 512-token tile, when
+// at most this many (0: never), are listed as matrix-core GEMV tiles instead
 hipError_t launch_route(const int32_t* ids, int T, int k, int E, int mfma_min_tokens, int mg_min_tokens,
-                        int mg_max_tokens, const Route& rt, hipStream_t s);
+                        int mg_max_tokens, int mfma_tail, const Route& rt, hipStream_t s);
 hipError_t launch_gemv_gate_up(const GemvLaunch& g, hipStream_t s, const KernelEvents& ev);
 hipError_t launch_gemv_down(const GemvLaunch& g, hipStream_t s, const KernelEvents& ev);
 hipError_t launch_mfma_gate_up(const ExpertArgs& a, const uint16_t* x, uint16_t* h, hipStream_t s,

@@ -22,7 +22,7 @@ constexpr int kRouteWaves = kRouteThreads / kWave;
 
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __restrict__ ids, int T, int k,
                                                               int E, int mfma_min_tokens, int mg_min_tokens,
-                                                              int mg_max_tokens, Route rt) {
+                                                              int mg_max_tokens, int mfma_tail, Route rt) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int off[kMaxExperts + 1];
   __shared__ int base[kMaxExperts];
@@ -51,17 +51,26 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
   if (wave == 0) {
     // Lane l owns experts 4l .. 4l+3 (E <= 256).  Four exclusive scans over the
     // wave give each expert its offset, its index in the active list and the
-    // first entries of its MFMA (256-token) and matrix-core GEMV (32-token)
-    // tiles, so every list is written in parallel, in expert order.
-    int c[4], na[4], nm[4], ng[4];
+    // first entries of its MFMA (512-token) and matrix-core GEMV (32-token)
+    // tiles, so every list is written in parallel, in expert order.  An MFMA
+    // expert whose tokens past its last whole 512-token tile number at most
+    // mfma_tail hands them to the matrix-core GEMV (tiles from token g0 on):
+    // a nearly empty MFMA tile costs as much as a full one.
+    int c[4], na[4], nm[4], ng[4], g0[4];
     int sc = 0, sa = 0, sm = 0, sg = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * lane + i;
       c[i] = e < E ? cnt[e] : 0;
       na[i] = c[i] > 0 ? 1 : 0;
-      nm[i] = (c[i] > 0 && c[i] >= mfma_min_tokens) ? (c[i] + kMfmaTileM - 1) / kMfmaTileM : 0;
-      ng[i] = (c[i] > 0 && c[i] >= mg_min_tokens && c[i] < mg_max_tokens) ? (c[i] + kMgTileM - 1) / kMgTileM : 0;
+      const bool mf = c[i] > 0 && c[i] >= mfma_min_tokens;
+      const int rem = c[i] % kMfmaTileM;
+      const bool tail = mf && rem > 0 && rem <= mfma_tail;
+      nm[i] = mf ? (tail ? c[i] / kMfmaTileM : (c[i] + kMfmaTileM - 1) / kMfmaTileM) : 0;
+      g0[i] = tail ? c[i] - rem : 0;
+      ng[i] = tail ? (rem + kMgTileM - 1) / kMgTileM
+                   : ((c[i] > 0 && c[i] >= mg_min_tokens && c[i] < mg_max_tokens) ? (c[i] + kMgTileM - 1) / kMgTileM
+                                                                                  : 0);
       sc += c[i]; sa += na[i]; sm += nm[i]; sg += ng[i];
     }
     int xc = sc, xa = sa, xm = sm, xg = sg;   // inclusive scans
@@ -84,7 +93,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
         }
         for (int t = 0; t < ng[i]; ++t) {
           rt.mgtiles[2 * (pg + t)] = e;
-          rt.mgtiles[2 * (pg + t) + 1] = t * kMgTileM;
+          rt.mgtiles[2 * (pg + t) + 1] = g0[i] + t * kMgTileM;
         }
       }
       pc += c[i]; pa += na[i]; pm += nm[i]; pg += ng[i];
@@ -152,9 +161,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
 }
 
 hipError_t launch_route(const int32_t* ids, int T, int k, int E, int mfma_min_tokens, int mg_min_tokens,
-                        int mg_max_tokens, const Route& rt, hipStream_t s) {
+                        int mg_max_tokens, int mfma_tail, const Route& rt, hipStream_t s) {
   hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, s, ids, T, k, E, mfma_min_tokens, mg_min_tokens,
-                     mg_max_tokens, rt);
+                     mg_max_tokens, mfma_tail, rt);
   return hipGetLastError();
 }
 

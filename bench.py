@@ -372,8 +372,11 @@ def measure(name, layer, dev, copies, args, evs, stream, opts_kw):
 
     kms = kern.mean(axis=0)
     m = 0 if kms[0] >= kms[1] else 1
-    fam = family[-1] if family else "gemv"
-    kname = KERNEL_NAMES[(fam, m)]
+    # the product's kernels, one per family that runs (the start / stop events
+    # bracket all of them: e.g. prefill's MFMA tiles and its tails on the
+    # matrix-core GEMV)
+    knames = [KERNEL_NAMES[(f, m)] for f in (family or ["gemv"])]
+    kname = " + ".join(knames)
     dom_bytes = RL.module_bytes(layer.q, layer.ids, H, I, E, T, k, m)
     dom_flops = RL.module_flops(T, k, H, I, m)
     bound = RL.bound(dom_flops, dom_bytes)
@@ -400,12 +403,13 @@ def measure(name, layer, dev, copies, args, evs, stream, opts_kw):
         "event_span": {"avg_ms": span_ms, "frac": rate(span_ms) / peak,
                        "what": "events on the stream before and after the product (includes the launch gap)"},
     }
-    tr = profile_fields(name, "traffic", kname)
-    if tr is not None:
-        roof["traffic"] = tr["traffic_bytes_per_launch"]
-    kt = profile_fields(name, "kernels", kname)
-    if kt is not None:
-        roof["kernel_trace"] = {"avg_ms": kt["avg_ns"] * 1e-6, "frac": rate(kt["avg_ns"] * 1e-6) / peak,
+    tr = [profile_fields(name, "traffic", kn) for kn in knames]
+    if all(t is not None for t in tr):
+        roof["traffic"] = sum(t["traffic_bytes_per_launch"] for t in tr)
+    kt = [profile_fields(name, "kernels", kn) for kn in knames]
+    if all(t is not None for t in kt):
+        kt_ms = sum(t["avg_ns"] for t in kt) * 1e-6
+        roof["kernel_trace"] = {"avg_ms": kt_ms, "frac": rate(kt_ms) / peak,
                                 "profile": f"profiles/kernels_{name}.txt"}
 
     status = dev.status()

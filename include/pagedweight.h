@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define PW_ABI_VERSION 3
+#define PW_ABI_VERSION 4
 
 typedef int32_t pw_status;
 #define PW_OK                     0
@@ -210,17 +210,22 @@ pw_status pw_moe_forward_noalloc(const pw_moe_shape* shape, int32_t T, const uin
  * the result does not depend on the routing itself. */
 typedef struct {
   int32_t gemv;          /* 1: the bit-plane GEMV kernels run                 */
-  int32_t mgemv;         /* 1: the matrix-core GEMV kernels run               */
+  int32_t mgemv;         /* 1: the matrix-core GEMV kernels run (for their
+                            band, or only for the MFMA experts' tails)        */
   int32_t mfma;          /* 1: the dequant-to-LDS MFMA kernels run            */
   int32_t mgemv_from;    /* experts with at least this many tokens (and below
                             mfma_from, if MFMA runs) take the matrix-core GEMV;
-                            0 if it does not run                               */
+                            0 if it has no band                                */
   int32_t mfma_from;     /* experts with at least this many tokens take MFMA;
                             0 if it does not run                               */
   int32_t inline_route;  /* 1: no separate routing kernel (GEMV alone, at most
                             64 slots: the gate_up kernel routes)               */
   int32_t down_kparts;   /* parts of the K range of the GEMV down product    */
   int32_t launches;      /* kernels the call enqueues (T > 0)                 */
+  int32_t mfma_tail;     /* an MFMA expert's tokens past its last whole
+                            512-token tile, when at most this many, take the
+                            matrix-core GEMV instead (the AUTO rule's prefill
+                            form; the kernels of both families run); 0: never */
 } pw_path_info;
 
 /*   shape, opts  host, as for pw_moe_forward (opts may be NULL)

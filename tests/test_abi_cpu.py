@@ -39,7 +39,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert B.pw_abi_version() == 3
+    assert B.pw_abi_version() == 4
     for s in (B.PW_OK, B.PW_ERR_INVALID_ARG, B.PW_ERR_UNSUPPORTED_SHAPE, B.PW_ERR_BITWIDTH,
               B.PW_ERR_WORKSPACE, B.PW_ERR_ALIGNMENT, B.PW_ERR_HIP, B.PW_ERR_UNSUPPORTED, 12345):
         assert isinstance(B.pw_status_str(s), str) and B.pw_status_str(s)
@@ -171,13 +171,15 @@ def _families(info):
     return tuple(n for n in ("gemv", "mgemv", "mfma") if getattr(info, n))
 
 
+# fams: the families whose kernels run; ("mgemv", "mfma") on the AUTO rule's
+# prefill side means MFMA with the matrix-core GEMV taking the experts' tails
 @pytest.mark.parametrize("shp,T,fams,inline,launches,kparts", [
     # E = 8, k = 2: the mean routed slots per routed expert m = T*k / min(E, T*k) crosses 2 at T = 8 and 64 at T = 256
     ((1024, 1024, 8, 2), 1, ("gemv",), 1, 3, None),
     ((1024, 1024, 8, 2), 7, ("gemv",), 1, 3, None),
     ((1024, 1024, 8, 2), 8, ("mgemv",), 0, 4, 1),
     ((1024, 1024, 8, 2), 256, ("mgemv",), 0, 4, 1),
-    ((1024, 1024, 8, 2), 257, ("mfma",), 0, 4, 1),
+    ((1024, 1024, 8, 2), 257, ("mgemv", "mfma"), 0, 6, 1),
     # Qwen-shaped layer: decode, 16 tokens (64 slots, still routed inline), 17 tokens (a route kernel), batched
     ((2048, 1408, 60, 4), 4, ("gemv",), 1, 3, 1),
     ((2048, 1408, 60, 4), 16, ("gemv",), 1, 3, None),
@@ -188,8 +190,8 @@ def _families(info):
     ((4096, 14336, 8, 2), 1, ("gemv",), 1, 3, 4),
     # 64 tokens: matrix-core GEMV alone, its down product in four K parts (8 tiles x 128 chunks)
     ((4096, 14336, 8, 2), 64, ("mgemv",), 0, 4, 4),
-    ((4096, 14336, 8, 2), 4096, ("mfma",), 0, 4, 2),
-    ((4096, 14336, 8, 2), 16384, ("mfma",), 0, 4, 1),
+    ((4096, 14336, 8, 2), 4096, ("mgemv", "mfma"), 0, 6, 2),
+    ((4096, 14336, 8, 2), 16384, ("mgemv", "mfma"), 0, 6, 1),
 ])
 def test_path_info_auto_rule(lib, shp, T, fams, inline, launches, kparts):
     info = B.pw_moe_path_info(B.shape(*shp), T)
@@ -197,8 +199,10 @@ def test_path_info_auto_rule(lib, shp, T, fams, inline, launches, kparts):
     assert info.inline_route == inline and info.launches == launches
     if kparts is not None:
         assert info.down_kparts == kparts
-    assert info.mgemv_from == (1 if "mgemv" in fams else 0)
-    assert info.mfma_from == (1 if "mfma" in fams else 0)
+    prefill = "mfma" in fams
+    assert info.mgemv_from == (1 if "mgemv" in fams and not prefill else 0)
+    assert info.mfma_from == (1 if prefill else 0)
+    assert info.mfma_tail == (96 if prefill else 0)
 
 
 def test_path_info_forced_paths_and_bands(lib):
@@ -206,13 +210,16 @@ def test_path_info_forced_paths_and_bands(lib):
     i = B.pw_moe_path_info(s, 4096, B.make_options(path=B.PW_PATH_GEMV))
     assert _families(i) == ("gemv",) and i.launches == 4 and i.down_kparts == 1
     i = B.pw_moe_path_info(s, 1, B.make_options(path=B.PW_PATH_MFMA))
-    assert _families(i) == ("mfma",) and i.mfma_from == 1 and i.inline_route == 0
+    assert _families(i) == ("mfma",) and i.mfma_from == 1 and i.inline_route == 0 and i.mfma_tail == 0
     i = B.pw_moe_path_info(s, 1, B.make_options(path=B.PW_PATH_MGEMV))
     assert _families(i) == ("mgemv",) and i.mgemv_from == 1
     # explicit bands on a batch averaging 17 slots per expert: all three families, in one call
     i = B.pw_moe_path_info(s, 256, B.make_options(mgemv_min_tokens=4, mfma_min_tokens=64))
     assert _families(i) == ("gemv", "mgemv", "mfma") and (i.mgemv_from, i.mfma_from) == (4, 64)
-    assert i.launches == 1 + 2 * 3 + 1
+    assert i.launches == 1 + 2 * 3 + 1 and i.mfma_tail == 0
+    # explicit bands keep every MFMA expert whole on the MFMA kernels
+    i = B.pw_moe_path_info(B.shape(4096, 14336, 8, 2), 4096, B.make_options(mfma_min_tokens=1))
+    assert _families(i) == ("mfma",) and i.mfma_tail == 0 and i.launches == 4
     # an MFMA band no expert can reach is not launched; below a mean of 2 the GEMV keeps every expert
     i = B.pw_moe_path_info(s, 4, B.make_options(mfma_min_tokens=256))
     assert _families(i) == ("gemv",) and i.inline_route == 1

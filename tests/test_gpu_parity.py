@@ -614,18 +614,28 @@ def test_forward_auto_edge_layers(torch, H, I, E, k, T, seed):
 _FAMILIES = {B.PW_PATH_GEMV: "gemv", B.PW_PATH_MGEMV: "mgemv", B.PW_PATH_MFMA: "mfma"}
 
 
-@pytest.mark.parametrize("T,family", [(7, B.PW_PATH_GEMV), (8, B.PW_PATH_MGEMV), (256, B.PW_PATH_MGEMV),
-                                      (257, B.PW_PATH_MFMA)])
-def test_auto_family_at_the_mean_edges(torch, T, family):
+@pytest.mark.parametrize("T,family,launched", [(7, B.PW_PATH_GEMV, ("gemv",)), (8, B.PW_PATH_MGEMV, ("mgemv",)),
+                                               (256, B.PW_PATH_MGEMV, ("mgemv",)),
+                                               (257, B.PW_PATH_MGEMV, ("mgemv", "mfma"))])
+def test_auto_family_at_the_mean_edges(torch, T, family, launched):
     """AUTO runs one kernel family per call, chosen from the mean routed slots
     per routed expert m = T*k / min(E, T*k): GEMV for m < 2, matrix-core GEMV
-    for 2 <= m <= 64, MFMA above.  With E = 8, k = 2 the batches T = 7 / 8 /
-    256 / 257 sit on either side of both edges.  Every family is deterministic
-    and sums in its own order, so AUTO's output equals the chosen family's
-    forced output bit for bit and differs from the other two."""
+    for 2 <= m <= 64, MFMA above, where an expert's tokens past its last whole
+    512-token tile take the matrix-core GEMV when there are at most 96 of them.
+    With E = 8, k = 2 the batches T = 7 / 8 / 256 / 257 sit on either side of
+    both edges; at T = 257 every expert holds at most 96 tokens, so all of
+    them are such tails and the MFMA kernels find no tile.  Every family is
+    deterministic and sums in its own order (here with the down product's K
+    range in one part on both GEMV forms), so AUTO's output equals the
+    computing family's forced output bit for bit and differs from the others."""
     L = custom_layer(1024, 1024, 8, 2, T, 700 + T)
     info = B.pw_moe_path_info(B.shape(1024, 1024, 8, 2), T)
-    assert [n for n in ("gemv", "mgemv", "mfma") if getattr(info, n)] == [_FAMILIES[family]]
+    assert _families(info) == launched
+    forced = B.pw_moe_path_info(B.shape(1024, 1024, 8, 2), T, B.make_options(path=family))
+    assert forced.down_kparts == info.down_kparts == 1
+    if "mfma" in launched:
+        assert info.mfma_tail == 96
+        assert np.bincount(L.ids.reshape(-1), minlength=8).max() <= 96
     say(f"forward AUTO family edge T={T} (expect {_FAMILIES[family]})")
     dev, y_auto = run_forward(torch, L, B.PW_PATH_AUTO)
     assert dev.status() == 0
@@ -637,6 +647,42 @@ def test_auto_family_at_the_mean_edges(torch, T, family):
             same.append(f)
     assert same == [family], [_FAMILIES[f] for f in same]
     compare(y_auto, oracle_y(L), f"auto family edge T={T}")
+
+
+def _families(info):
+    return tuple(n for n in ("gemv", "mgemv", "mfma") if getattr(info, n))
+
+
+def _designed_ids(counts, seed):
+    """k = 1 routing with the given per-expert slot counts, in seeded token order."""
+    ids = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
+    np.random.default_rng(seed).shuffle(ids)
+    return ids.reshape(-1, 1)
+
+
+@pytest.mark.parametrize("H,I,counts,kparts", [
+    # tails of exactly 96 (matrix-core GEMV) and 97 (a partial MFMA tile), an
+    # expert of 80 tokens (all of it a tail), a whole tile, an unrouted expert
+    # and a one-token expert; I = 8224 splits the down product's K range in two
+    # (33 quads of eight plane words), which both families then share
+    (256, 8224, [608, 609, 80, 512, 0, 1], 2),
+    # K range in one part; tails of 1, 31, 32, 33 and 95 tokens behind one or two whole tiles
+    (512, 1024, [513, 543, 544, 1057, 607, 700], 1),
+])
+def test_forward_auto_prefill_tails(torch, H, I, counts, kparts):
+    """AUTO's prefill form: MFMA tiles for whole 512-token runs, the
+    matrix-core GEMV for short tails, both writing the same K parts of the
+    expert outputs, against the oracle on every token."""
+    E, T = len(counts), int(sum(counts))
+    L = custom_layer(H, I, E, 1, T, 800 + T)
+    L.ids = _designed_ids(counts, 810 + T)
+    L.w = np.ones((T, 1), np.float32)
+    info = B.pw_moe_path_info(B.shape(H, I, E, 1), T)
+    assert _families(info) == ("mgemv", "mfma") and info.mfma_tail == 96 and info.down_kparts == kparts
+    say(f"forward AUTO prefill tails H={H} I={I} counts={counts} down K parts={kparts}")
+    dev, y = run_forward(torch, L, B.PW_PATH_AUTO)
+    assert dev.status() == 0
+    compare(y, oracle_y(L), f"auto prefill tails H={H} I={I}")
 
 
 def _random_case(seed):
