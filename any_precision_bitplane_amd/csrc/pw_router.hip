@@ -7,15 +7,15 @@
 // logits in descending order (lower expert id first on equal logits), weights
 // = softmax over the selected logits.
 //
-// One launch: a workgroup of four waves takes TT tokens (1 for batches of up
-// to 256 tokens, 4 above, so larger batches share each router row read), the
-// waves split the experts, each wave's lanes stride over H in 8-element chunks
-// (fp16 pairs multiplied into fp32 with v_dot2, one butterfly sum per token
-// and expert), and the logits meet in LDS; then wave t selects the top-k of
-// token t: k rounds of a wave-wide (value desc, id asc) butterfly arg-max, lane
-// j keeping slot j, softmax with the device exp, lane j writing slot j and its
-// statistics (count exact, mass an fp32 atomic sum whose order varies between
-// runs).  An earlier form used two launches (logits, then top-k through global
+// One launch: a workgroup of sixteen waves takes TT tokens (1 for batches of
+// up to 256 tokens, 4 above, so larger batches share each router row read),
+// the waves split the experts, each wave's lanes stride over H in 8-element
+// chunks (fp16 pairs multiplied into fp32 with v_dot2, one wave-wide DPP sum
+// per token and expert), and the logits meet in LDS; then wave t selects the
+// top-k of token t: k rounds of a wave-wide DPP max and a ballot for the
+// lowest id holding it, lane j keeping slot j, softmax with the device exp,
+// lane j writing slot j and its statistics (count exact, mass an fp32 atomic
+// sum whose order varies between runs).  An earlier form used two launches (logits, then top-k through global
 // memory); on the Qwen-shaped decode layer the second launch and its gap cost
 // about as much as the work.
 #include <limits.h>
@@ -28,15 +28,46 @@ namespace pw {
 constexpr int kRouterTokens = 4;     // tokens per workgroup for batches above 256 tokens
 constexpr int kRouterWaves = 16;     // waves per workgroup
 
+// Wave-wide sum and max in DPP: inside each 16-lane row, partners lane ^ 1,
+// lane ^ 2, then the mirror inside 8 lanes and inside 16 lanes (each pairing
+// is symmetric, so every lane of a row ends with the same bits); then the four
+// rows' values read out of lanes 0, 16, 32, 48 and combined the same way in
+// every lane.  All 64 lanes must be active.  A shuffle-based butterfly (one
+// LDS permute per step) made the router's top-k rounds a chain of permutes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kHalfRowMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+__device__ __forceinline__ float row_lane(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  v += dpp_row<kQuadXor1>(v);
+  v += dpp_row<kQuadXor2>(v);
+  v += dpp_row<kHalfRowMirror>(v);
+  v += dpp_row<kRowMirror>(v);
+  return (row_lane(v, 0) + row_lane(v, 16)) + (row_lane(v, 32) + row_lane(v, 48));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_row<kQuadXor1>(v));
+  v = fmaxf(v, dpp_row<kQuadXor2>(v));
+  v = fmaxf(v, dpp_row<kHalfRowMirror>(v));
+  v = fmaxf(v, dpp_row<kRowMirror>(v));
+  return fmaxf(fmaxf(row_lane(v, 0), row_lane(v, 16)), fmaxf(row_lane(v, 32), row_lane(v, 48)));
 }
 
 // Selection and softmax of token t from its logits l[e] (e < E; lane owns
-// e = lane + 64 i, E <= 256): k rounds of a (value desc, id asc) butterfly
-// arg-max, slot j kept in lane j; lane j writes slot j and its statistics.
+// e = lane + 64 i, E <= 256): k rounds of a wave-wide max over the live
+// logits, the lowest expert id holding it found by ballot (so equal logits
+// go to the lower id), slot j kept in lane j; lane j writes slot j and its
+// statistics.  NaN logits count as -inf.
 __device__ __forceinline__ void select_topk(const float* l, int E, int k, int t, int32_t* ids, float* w,
                                             uint32_t* count, float* mass) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -46,39 +77,32 @@ __device__ __forceinline__ void select_topk(const float* l, int E, int k, int t,
   for (int i = 0; i < 4; ++i) {
     const int e = lane + kWave * i;
     live[i] = e < E;
-    v[i] = live[i] ? l[e] : 0.f;
+    const float x = live[i] ? l[e] : -INFINITY;
+    v[i] = x == x ? x : -INFINITY;
   }
-  float my_l = 0.f;
+  float my_l = 0.f, top = 0.f;
   int my_e = -1;
   for (int j = 0; j < k; ++j) {
-    float bv = 0.f;
-    int bi = INT_MAX;
+    float lm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (live[i]) lm = fmaxf(lm, v[i]);
+    const float m = wave_max(lm);
+    int bi = -1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int e = lane + kWave * i;
-      if (live[i] && (bi == INT_MAX || v[i] > bv)) {
-        bv = v[i];
-        bi = e;
-      }
+      const unsigned long long b = __ballot(live[i] && v[i] == m);
+      if (bi < 0 && b) bi = kWave * i + __ffsll((long long)b) - 1;
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, kWave);
-      const int oi = __shfl_xor(bi, off, kWave);
-      if (oi != INT_MAX && (bi == INT_MAX || ov > bv || (ov == bv && oi < bi))) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    if (j == 0) top = m;
     if (lane == j) {
-      my_l = bv;
+      my_l = m;
       my_e = bi;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (lane + kWave * i == bi) live[i] = false;
   }
-  const float top = __shfl(my_l, 0, kWave);
   const float z = lane < k ? __expf(my_l - top) : 0.f;
   const float s = wave_sum(z);
   if (lane < k) {
@@ -144,11 +168,9 @@ __device__ __forceinline__ void router_logits(const uint16_t* x, size_t x_stride
       }
     }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
+    for (int g = 0; g < kRtGroup; ++g)
 #pragma unroll
-      for (int g = 0; g < kRtGroup; ++g)
-#pragma unroll
-        for (int t = 0; t < TT; ++t) acc[g][t] += __shfl_xor(acc[g][t], off, kWave);
+      for (int t = 0; t < TT; ++t) acc[g][t] = wave_sum(acc[g][t]);
     if (lane == 0) {
 #pragma unroll
       for (int g = 0; g < kRtGroup; ++g) {

@@ -50,6 +50,7 @@ def run_router(torch, x, wr, E, k, stats=None, repeat=1):
     cnt = torch.zeros(E, dtype=torch.int32, device=dev) if stats else None
     mass = torch.zeros(E, dtype=torch.float32, device=dev) if stats else None
     ws = torch.empty(max(B.pw_workspace_bytes(shp, T), 256), dtype=torch.uint8, device=dev)
+    B.pw_workspace_init(ws)
     for _ in range(repeat):
         B.pw_router_topk(shp, T, xd, wd, ids, w, cnt, mass, ws)
     torch.cuda.synchronize()
@@ -101,6 +102,22 @@ def test_router_matches_oracle(torch, name, T, H, E, k, seed):
     wr = synth.draw_router_weights(seed, E, H)
     gids, gw = run_router(torch, x, wr, E, k)
     check_route(gids, gw, x, wr, k)
+
+
+def test_router_forms_agree_bit_for_bit(torch):
+    """Batches of up to 256 tokens take one workgroup per token, larger ones
+    four tokens per workgroup; both sum every logit in the same order, so 256
+    tokens routed alone and as the first rows of a 257-token batch get the
+    same ids and the same weight bits."""
+    for (H, E, k, seed) in [(2048, 60, 4, 21), (96, 5, 1, 23), (128, 256, 64, 24)]:
+        say(f"router forms: H={H} E={E} k={k}, T=256 alone and inside T=257")
+        x = synth.draw_x(seed, 257, H)
+        wr = synth.draw_router_weights(seed, E, H)
+        ids256, w256 = run_router(torch, x[:256], wr, E, k)
+        ids257, w257 = run_router(torch, x, wr, E, k)
+        assert np.array_equal(ids256, ids257[:256])
+        assert np.array_equal(w256.view(np.uint32), w257[:256].view(np.uint32))
+        check_route(ids256, w256, x[:256], wr, k)
 
 
 def test_router_ties_pick_lower_ids(torch):
