@@ -45,6 +45,7 @@ constexpr int kPfTM = kMfmaTileM;        // tokens per tile
 constexpr int kPfWM = kPfTM / kPfWaves;  // tokens per wave
 static_assert(kPfWM == 128, "eight 16-token groups per wave");
 constexpr int kPfTN = 128;               // device rows per tile
+constexpr int kPfTileGroup = 2;          // token tiles whose items of one row tile run together
 constexpr int kPfTG = kPfWM / 16;        // token groups per wave
 constexpr int kPfRG = kPfTN / 16;        // row groups
 constexpr int kPfBStride = 2 * 64 + 16;  // bytes per B-tile row: 64 fp16 of one step + pad (conflict-free reads)
@@ -438,18 +439,30 @@ __global__ __launch_bounds__(kPfThreads, 1) void mfma_kernel(MfmaArgs A) {
   __shared__ __align__(1024) uint8_t lds[kPfLds];
   // Workgroups go to the eight XCDs round-robin (workgroup i to XCD i mod 8)
   // and the grid is sized for the most token tiles routing can produce.  The
-  // items that exist (token tiles x row tiles, counted on the device) are
-  // dealt evenly, a run of consecutive items per XCD, so the XCDs finish
-  // together and one XCD sweeps the row tiles of a token tile, whose
-  // activation rows then stay in its L2.
-  const int nitems = uniform(*A.rt.num_mtiles) * A.kparts * A.ntiles;
+  // items that exist (token tiles x K parts x row tiles, counted on the
+  // device) are dealt evenly, a run of consecutive items per XCD, so the XCDs
+  // finish together and one XCD sweeps the row tiles of a few token tiles,
+  // whose activation rows then stay near it.  Items run in groups of
+  // kPfTileGroup consecutive token tiles (an expert's tiles are adjacent in
+  // the list): inside a group the tiles of one (K part, row tile) are
+  // adjacent, so they read that row tile's planes at about the same time and
+  // the second read finds them in L2 (Mixtral prefill, two tiles per expert:
+  // gate_up 2.31 -> 2.25 ms, down 1.21 -> 1.17 ms against tile-major items).
+  const int ntl = uniform(*A.rt.num_mtiles);
+  const int nitems = ntl * A.kparts * A.ntiles;
   const int per_xcd = (nitems + kXcds - 1) / kXcds;
   const int slot = blockIdx.x / kXcds;
   const int item = (blockIdx.x % kXcds) * per_xcd + slot;
   if (slot >= per_xcd || item >= nitems) return;
-  const int mi = item / (A.kparts * A.ntiles);
-  const int part = item / A.ntiles % A.kparts;
-  const int nt = item % A.ntiles;
+  const int per_group = kPfTileGroup * A.kparts * A.ntiles;
+  const int full = ntl / kPfTileGroup;   // whole groups; the last one may hold fewer tiles
+  const bool whole = item < full * per_group;
+  const int g0 = whole ? item / per_group * kPfTileGroup : full * kPfTileGroup;
+  const int gn = whole ? kPfTileGroup : ntl - full * kPfTileGroup;
+  const int r = whole ? item % per_group : item - full * per_group;
+  const int mi = g0 + r % gn;
+  const int part = r / (gn * A.ntiles);
+  const int nt = (r / gn) % A.ntiles;
   const int e = uniform(A.rt.mtiles[2 * mi]);
   const int m0 = uniform(A.rt.mtiles[2 * mi + 1]);
   const int n_e = uniform(A.rt.counts[e]);
