@@ -278,7 +278,8 @@ __device__ __forceinline__ void build_pair_tables3(uint32_t tab_base) {
 // ---------------------------------------------------------------------------
 struct Slots {
   int e, n_e, off_e, num_active;
-  int qd;                    // down bitwidth from the work descriptor (desc_mode)
+  int qd;                    // bitwidth of the block when `pre` (down: from the work descriptor)
+  bool pre;                  // qd and d already hold the block's page-table entry
   unsigned long long mask;   // inline routing: slots routed to e (bit = slot)
   pw_block_desc d;           // page-table entry of this product's block of e
 };
@@ -384,6 +385,18 @@ __device__ __forceinline__ int wave_segment(const GemvArgs& A, int n_act) {
 __device__ __forceinline__ bool find_expert_inline(const GemvArgs& A, int& a, Slots& sl, RouteLds& L) {
   const int lane = threadIdx.x;
   const int S = A.T * A.k;
+  // With at most 64 experts, lane i requests expert i's gate_up page-table
+  // entry together with the ids, so the routed expert's entry is a readlane
+  // away instead of a load that waits for the routing.
+  const bool pre = A.E <= kWave;
+  int pq = 0;
+  uint64_t pp = 0, pt = 0;
+  if (pre && lane < A.E) {
+    pq = A.q[2 * lane];
+    const pw_block_desc bd = A.blocks[2 * lane];
+    pp = reinterpret_cast<uint64_t>(bd.planes);
+    pt = reinterpret_cast<uint64_t>(bd.lut_all);
+  }
   const int id = lane < S ? A.ids[lane] : -1;
   const bool valid = id >= 0 && id < A.E;
   if (blockIdx.x == 0 && __ballot(lane < S && !valid) != 0ull && lane == 0)
@@ -428,6 +441,17 @@ __device__ __forceinline__ bool find_expert_inline(const GemvArgs& A, int& a, Sl
   sl.n_e = __builtin_amdgcn_readfirstlane(L.cnt[e]);
   sl.off_e = __builtin_amdgcn_readfirstlane(L.off[e]);
   sl.mask = __ballot(id == e);
+  sl.pre = pre;
+  if (pre) {
+    auto pick = [e](uint64_t v) {
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, e);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), e);
+      return ((uint64_t)hi << 32) | lo;
+    };
+    sl.qd = __builtin_amdgcn_readlane(pq, e);
+    sl.d.planes = reinterpret_cast<const uint32_t*>(pick(pp));
+    sl.d.lut_all = reinterpret_cast<const uint16_t*>(pick(pt));
+  }
   return true;
 }
 
@@ -435,6 +459,7 @@ template <bool GU>
 __device__ __forceinline__ bool find_expert_routed(const GemvArgs& A, int& a, Slots& sl) {
   const int n_act = uniform(*A.rt.num_active);
   sl.num_active = n_act;
+  sl.pre = false;
   a = n_act > 0 ? wave_segment<GU>(A, n_act) / A.kparts : 0;
   if (a >= n_act) return false;
   const int e = uniform(A.rt.active[a]);
@@ -453,6 +478,7 @@ __device__ __forceinline__ bool find_expert_desc(const GemvArgs& A, int& a, Slot
   const int n_act = uniform(*A.rt.num_active);
   sl.num_active = n_act;
   sl.mask = 0ull;
+  sl.pre = false;
   if (n_act <= 0) return false;
   per = waves_per_segment<false>(A, n_act);
   a = ((int)blockIdx.x / per) / A.kparts;
@@ -745,8 +771,8 @@ __global__ __launch_bounds__(kWave) void gemv_kernel(GemvArgs A) {
   if (ch.n <= 0) return;
   // bitwidth and page-table entry of the block, requested together
   int qv;
-  if (!GU && A.desc_mode) {
-    qv = sl.qd;   // the work descriptor carried the entry
+  if ((!GU && A.desc_mode) || sl.pre) {
+    qv = sl.qd;   // the work descriptor, or the routing step, carried the entry
   } else {
     qv = uniform(A.q[2 * sl.e + (GU ? 0 : 1)]);
     sl.d = A.blocks[2 * sl.e + (GU ? 0 : 1)];
