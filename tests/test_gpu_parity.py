@@ -685,6 +685,25 @@ def test_forward_auto_prefill_tails(torch, H, I, counts, kparts):
     compare(y, oracle_y(L), f"auto prefill tails H={H} I={I}")
 
 
+@pytest.mark.parametrize("H,I,E,k,T,seed", [(128, 96, 256, 64, 1, 71), (256, 128, 256, 8, 40, 72),
+                                            (64, 64, 256, 256, 2, 73)])
+def test_forward_largest_expert_counts_every_path(torch, H, I, E, k, T, seed):
+    """The largest expert count the layer takes (E = 256): 64 slots routed
+    inside the gate_up kernel (k = 64, one token), 320 slots over 179 experts
+    through the route kernel, and k = E (every expert takes both tokens); AUTO
+    and each family forced.  Routing weights are 1 (the layer uses them as
+    given), which keeps the outputs well inside fp16's normal range."""
+    L = custom_layer(H, I, E, k, T, seed)
+    L.w[:] = 1.0
+    ref = oracle_y(L)
+    dev = None
+    for path in (B.PW_PATH_AUTO, B.PW_PATH_GEMV, B.PW_PATH_MGEMV, B.PW_PATH_MFMA):
+        say(f"forward E={E} k={k} T={T} H={H} I={I} path={path}")
+        dev, y = run_forward(torch, L, path, dev=dev)
+        assert dev.status() == 0
+        compare(y, ref, f"E={E} k={k} T={T} path={path}")
+
+
 def _random_case(seed):
     rng = np.random.default_rng(9000 + seed)
     H = 32 * int(rng.integers(1, 40))
