@@ -74,9 +74,12 @@ inline int mfma_down_kparts(int H, int I, int E, int k, int T) {
 // Parts of the down product's K range for the matrix-core GEMV when it runs
 // alone: a 32-row chunk of the down block walks all of I, and with few token
 // tiles (decode batches: about one per routed expert) there are too few
-// (tile, chunk) items to keep eight waves on every CU.  Parts double until
-// there are about 4096 items, each part keeping at least eight super-chunks
-// of eight plane words.
+// (tile, chunk) items to keep the CUs busy.  Parts double until there are
+// about 2048 items, each part keeping at least eight super-chunks of eight
+// plane words; every part stages the chunk's row tables again and writes its
+// own o slice, so more parts cost more than they spread (Mixtral-shaped down
+// product at T = 64, 1024 (tile, chunk) items: 177 / 136 / 141 / 156 us with
+// 1 / 2 / 4 / 8 parts).
 inline int mgemv_down_kparts(int H, int I, int E, int k, int T) {
   const long long slots = (long long)T * k;
   if (slots <= 0) return 1;
@@ -86,7 +89,7 @@ inline int mgemv_down_kparts(int H, int I, int E, int k, int T) {
   const long long items = tiles * ((H + 31) / 32);
   const int supers = (I / 32 + 7) / 8;
   int kp = 1;
-  while (kp < 8 && items * kp < 4096 && supers >= 8 * 2 * kp) kp *= 2;
+  while (kp < 8 && items * kp < 2048 && supers >= 8 * 2 * kp) kp *= 2;
   return kp;
 }
 
