@@ -704,6 +704,90 @@ def test_forward_largest_expert_counts_every_path(torch, H, I, E, k, T, seed):
         compare(y, ref, f"E={E} k={k} T={T} path={path}")
 
 
+# ---------------------------------------------------------------------------
+# The forward kernels' own decode, read back exactly
+# ---------------------------------------------------------------------------
+# Tables chosen so that the layer's output is one column of a dequantized
+# block: every gate weight 32 (with a one-hot token x, gate = 32 exactly and
+# SiLU(32) = 32 exactly in fp32, since exp(-32) vanishes next to 1), so
+#   readout "down": up row i_e's weights all 1/32 and the other up rows 0, so
+#     h is exactly one-hot at i_e and y[t] = W_down[:, i_e] of the token's expert;
+#   readout "up":   the down block the identity scaled by 1/32 (code 2^(q-1)
+#     at (n, n), table entries 0 except that code's 1/32), so
+#     h = 32 W_up[:, k0] and y[t][n] = W_up[n, k0] for n < min(H, I).
+# Every product and sum on the way is exact in fp32 and the results are fp16
+# values, so the kernels must reproduce the oracle's dequantized weights
+# exactly (values compared, -0 equal to +0: a weight of -0 comes out as +0
+# after the combine's add).
+_F16_32, _F16_1_32 = 0x5000, 0x2800
+
+
+def _table(L, e, m, N):
+    q = int(L.q[e][m])
+    off = orc.lut_offset(N, q)
+    return L.luts[e][m][off: off + N * 2 ** q].reshape(N, 2 ** q)
+
+
+def _readout_layer(H, I, E, T, seed, mode):
+    L = custom_layer(H, I, E, 1, T, seed)
+    L.q[:, 0] = [3 + (e % 6) for e in range(E)]
+    L.q[:, 1] = [3 + ((e + 1) % 6) for e in range(E)]
+    L.ids = (np.arange(T, dtype=np.int32) % E).reshape(T, 1)
+    L.w = np.ones((T, 1), np.float32)
+    k0 = [(7 * t + 3) % H for t in range(T)]
+    L.x = np.zeros((T, H), np.float16)
+    L.x[np.arange(T), k0] = 1.0
+    col = [(37 * e + 5) % I for e in range(E)]
+    for e in range(E):
+        L.luts[e][0] = L.luts[e][0].copy()
+        tab = _table(L, e, 0, 2 * I)
+        tab[:I] = _F16_32                       # every gate weight 32
+        if mode == "down":
+            tab[I:] = 0
+            tab[I + col[e]] = _F16_1_32
+        else:
+            pl = np.zeros_like(L.planes[e][1])
+            n = np.arange(min(H, I))
+            pl[0, n, n // 32] = (np.uint32(1) << (n % 32).astype(np.uint32))
+            L.planes[e][1] = pl
+            L.luts[e][1] = np.zeros_like(L.luts[e][1])
+            tab_d = _table(L, e, 1, H)
+            tab_d[n, 2 ** (int(L.q[e][1]) - 1)] = _F16_1_32
+    if mode == "down":
+        want = np.stack([orc.fp16_bits_to_f64(orc.dequant_block(L.planes[t % E][1], L.luts[t % E][1],
+                                                                int(L.q[t % E][1])))[:, col[t % E]]
+                         for t in range(T)])
+    else:
+        want = np.zeros((T, H))
+        m = min(H, I)
+        for t in range(T):
+            e = t % E
+            wgu = orc.fp16_bits_to_f64(orc.dequant_block(L.planes[e][0], L.luts[e][0], int(L.q[e][0])))
+            want[t, :m] = wgu[I: I + m, k0[t]]
+    return L, want
+
+
+@pytest.mark.parametrize("mode", ["down", "up"])
+@pytest.mark.parametrize("H,I", [(256, 192), (128, 2112)])
+def test_forward_kernels_decode_weights_exactly(torch, mode, H, I):
+    """Each kernel family's decode of the up and down blocks, through the
+    forward itself, equals the oracle's dequantized weights exactly, at every
+    bitwidth 3..8 (six experts, two tokens each); I = 2112 splits the GEMV's
+    down product into two K parts."""
+    E, T = 6, 12
+    L, want = _readout_layer(H, I, E, T, 900 + H + (I if mode == "up" else 0), mode)
+    # the oracle's own forward on the same layer gives the same columns (its
+    # fp64 SiLU(32) is 32 (1 - 1.3e-14), not 32)
+    np.testing.assert_allclose(oracle_y(L), want, rtol=1e-12, atol=0)
+    dev = None
+    for path in (B.PW_PATH_GEMV, B.PW_PATH_MGEMV, B.PW_PATH_MFMA, B.PW_PATH_AUTO):
+        say(f"decode readout {mode} H={H} I={I} path={path}")
+        dev, y = run_forward(torch, L, path, dev=dev)
+        assert dev.status() == 0
+        bad = np.argwhere(y.astype(np.float64) != want)
+        assert bad.size == 0, (mode, path, bad[:5], y[tuple(bad[0])], want[tuple(bad[0])])
+
+
 def _random_case(seed):
     rng = np.random.default_rng(9000 + seed)
     H = 32 * int(rng.integers(1, 40))
