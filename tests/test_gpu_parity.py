@@ -788,6 +788,23 @@ def test_forward_kernels_decode_weights_exactly(torch, mode, H, I):
         assert bad.size == 0, (mode, path, bad[:5], y[tuple(bad[0])], want[tuple(bad[0])])
 
 
+@pytest.mark.parametrize("H,I,E,k,T,seed", [(256, 8224, 2, 1, 1100, 81), (512, 384, 5, 2, 2660, 82),
+                                            (384, 512, 3, 3, 1580, 83), (160, 352, 7, 2, 1890, 84),
+                                            (1056, 224, 4, 4, 560, 85)])
+def test_forward_auto_prefill_seeded_layers(torch, H, I, E, k, T, seed):
+    """AUTO's prefill form on seeded layers whose experts end in short tails
+    (11 to 66 tokens past whole 512-token tiles) next to a nearly full last
+    tile, with odd numbers of MFMA tiles (grouped item order) and, at
+    I = 8224, a two-part K split of the down product shared by both families."""
+    L = custom_layer(H, I, E, k, T, seed)
+    info = B.pw_moe_path_info(B.shape(H, I, E, k), T)
+    assert _families(info) == ("mgemv", "mfma") and info.mfma_tail == 96
+    say(f"forward AUTO prefill seeded H={H} I={I} E={E} k={k} T={T} down K parts={info.down_kparts}")
+    dev, y = run_forward(torch, L, B.PW_PATH_AUTO)
+    assert dev.status() == 0
+    compare(y, oracle_y(L), f"auto prefill seeded H={H} I={I} E={E} k={k} T={T}")
+
+
 def _random_case(seed):
     rng = np.random.default_rng(9000 + seed)
     H = 32 * int(rng.integers(1, 40))
