@@ -805,6 +805,26 @@ def test_forward_auto_prefill_seeded_layers(torch, H, I, E, k, T, seed):
     compare(y, oracle_y(L), f"auto prefill seeded H={H} I={I} E={E} k={k} T={T}")
 
 
+@pytest.mark.parametrize("H,I,E,k,T,seed", [(16384, 32, 2, 2, 5, 91), (32, 16384, 2, 2, 5, 92),
+                                            (8192, 96, 3, 1, 300, 93)])
+def test_forward_extreme_aspect_ratios_every_path(torch, H, I, E, k, T, seed):
+    """The widest hidden size over a one-word inner size (a 64-row gate_up
+    block: one partial 128-row MFMA tile), the reverse (the down product's K
+    range in eight parts on both GEMV forms and four on MFMA), and an
+    8192-wide layer on AUTO's prefill form with its tails; each family forced
+    and AUTO."""
+    L = custom_layer(H, I, E, k, T, seed)
+    L.w[:] = 1.0
+    ref = oracle_y(L)
+    dev = None
+    for path in (B.PW_PATH_AUTO, B.PW_PATH_GEMV, B.PW_PATH_MGEMV, B.PW_PATH_MFMA):
+        info = B.pw_moe_path_info(B.shape(H, I, E, k), T, B.make_options(path=path))
+        say(f"forward H={H} I={I} E={E} k={k} T={T} path={path} down K parts={info.down_kparts}")
+        dev, y = run_forward(torch, L, path, dev=dev)
+        assert dev.status() == 0
+        compare(y, ref, f"H={H} I={I} path={path}")
+
+
 def _random_case(seed):
     rng = np.random.default_rng(9000 + seed)
     H = 32 * int(rng.integers(1, 40))
