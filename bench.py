@@ -530,7 +530,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--only", default=None, choices=[c[0] for c in CONFIGS],
                     help="run one configuration and report it as the line")
     ap.add_argument("--copies", type=int, default=0, help="storage copies to rotate (0: auto, >= 1 GB)")
