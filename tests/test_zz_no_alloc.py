@@ -91,3 +91,29 @@ def test_noalloc_rejects_calls_beyond_its_scratch(torch):
     say(f"noalloc forward asked for {need} scratch bytes (host-side rejection, nothing launched)")
     st = B.pw_moe_forward_noalloc(shp, wl.T, dummy, dummy, dummy, dummy, dummy, dummy, check=False)
     assert st == B.PW_ERR_WORKSPACE
+
+
+def test_noalloc_largest_call_its_scratch_holds(torch):
+    # the largest Qwen-shaped call whose workspace fits the static scratch
+    # (found from pw_workspace_bytes, one token more does not fit); AUTO then
+    # runs the prefill form (MFMA tiles, matrix-core GEMV tails)
+    shp = B.shape(2048, 1408, 60, 4)
+    lim = B.PW_NOALLOC_SCRATCH_BYTES
+    lo, hi = 1, 1 << 16
+    while lo < hi:
+        mid = (lo + hi + 1) // 2
+        if B.pw_workspace_bytes(shp, mid) <= lim:
+            lo = mid
+        else:
+            hi = mid - 1
+    T = lo
+    assert B.pw_workspace_bytes(shp, T + 1) > lim
+    info = B.pw_moe_path_info(shp, T)
+    assert info.mfma == 1 and info.mgemv == 1 and info.mfma_tail > 0
+    wl = synth.WORKLOADS["qwen_decode"].with_T(T)
+    L = synth.make_routed_layer(wl)
+    say(f"noalloc forward qwen_decode T={T} (workspace {B.pw_workspace_bytes(shp, T)} of {lim} bytes)")
+    y_ws, y_na, st, _ = _both(torch, L)
+    assert st == 0
+    assert np.array_equal(y_ws, y_na), f"T={T}: {np.count_nonzero(y_ws != y_na)} elements differ"
+    _check_oracle(y_na, L)
