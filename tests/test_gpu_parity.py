@@ -533,6 +533,36 @@ def test_forward_mixtral_prefill_full_call_stratified(torch):
     _C4.clear()
 
 
+def test_forward_qwen_largest_prefill_stratified(torch):
+    """A Qwen-shaped prefill of 32768 tokens (131072 routed slots, about 2200
+    per expert: four or five 512-slot MFMA tiles each, the remainders of at most
+    96 on the matrix-core GEMV; a 1 GB o buffer), the largest call in the
+    suite.  The oracle takes tokens from every expert's first and last tile."""
+    T = 32768
+    L = layer_for("qwen_decode", T=T)
+    wl = L.wl
+    info = B.pw_moe_path_info(B.shape(wl.H, wl.I, wl.E, wl.k), T)
+    assert info.mfma == 1 and info.mfma_tail > 0
+    say(f"forward qwen_decode T={T} AUTO (prefill form)")
+    dev, y = run_forward(torch, L)
+    assert dev.status() == 0
+    assert np.all(np.isfinite(y))
+    flat = L.ids.reshape(-1)
+    toks = set()
+    for e in range(wl.E):
+        slots = np.nonzero(flat == e)[0]
+        if len(slots) == 0:
+            continue
+        ntile = (len(slots) + 511) // 512
+        for part in (slots[:512] // wl.k, slots[512 * (ntile - 1):] // wl.k):
+            pick = np.unique(part)
+            toks.update(int(t) for t in pick[np.linspace(0, len(pick) - 1, 2).astype(int)])
+    toks = sorted(toks)
+    ref = orc.moe_forward_layer(L, tokens=toks)
+    compare(y[toks], ref, f"qwen T={T}, {len(toks)} tokens from every expert's first and last tile")
+    _LAYERS.clear()
+
+
 # ---------------------------------------------------------------------------
 # matrix-core GEMV (weights decoded in registers into the MFMA B operand)
 # ---------------------------------------------------------------------------
