@@ -247,6 +247,21 @@ def test_forward_many_tokens_per_expert_gemv(torch):
     compare(y, oracle_y(L), "gemv many tokens")
 
 
+@pytest.mark.parametrize("T,inline", [(16, 1), (17, 0)])
+def test_forward_gemv_routing_edge(torch, T, inline):
+    """The bit-plane GEMV's two routing forms at their edge: 16 tokens of the
+    Qwen-shaped layer fill all 64 slots the gate_up kernel routes by itself
+    (one slot per lane), 17 tokens (68 slots) take the route kernel."""
+    L = layer_for("qwen_decode", T=T)
+    wl = L.wl
+    info = B.pw_moe_path_info(B.shape(wl.H, wl.I, wl.E, wl.k), T)
+    assert info.gemv == 1 and info.mgemv == 0 and info.mfma == 0 and info.inline_route == inline
+    say(f"forward qwen_decode T={T} AUTO (GEMV, inline routing {inline})")
+    dev, y = run_forward(torch, L)
+    assert dev.status() == 0
+    compare(y, oracle_y(L), f"qwen gemv T={T}, inline routing {inline}")
+
+
 def test_forward_zero_tokens_is_noop(torch):
     from any_precision_bitplane_amd.device import DeviceLayer
     L = layer_for("tiny")
