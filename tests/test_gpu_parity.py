@@ -262,6 +262,18 @@ def test_forward_gemv_routing_edge(torch, T, inline):
     compare(y, oracle_y(L), f"qwen gemv T={T}, inline routing {inline}")
 
 
+@pytest.mark.parametrize("k", [1, 2])
+@pytest.mark.parametrize("path", [B.PW_PATH_GEMV, B.PW_PATH_MGEMV, B.PW_PATH_MFMA, B.PW_PATH_AUTO])
+def test_forward_single_token_every_family(torch, path, k):
+    """One token (one or two routed slots) on every kernel family: one 32-token
+    matrix-core GEMV tile or one 512-token MFMA tile holding a single token."""
+    L = custom_layer(256, 512, 8, k, 1, seed=70 + k)
+    say(f"forward single token k={k} path={path}")
+    dev, y = run_forward(torch, L, path)
+    assert dev.status() == 0
+    compare(y, oracle_y(L), f"single token k={k} path={path}")
+
+
 def test_forward_zero_tokens_is_noop(torch):
     from any_precision_bitplane_amd.device import DeviceLayer
     L = layer_for("tiny")
