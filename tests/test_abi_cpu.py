@@ -186,11 +186,11 @@ def _families(info):
     ((2048, 1408, 60, 4), 17, ("gemv",), 0, 4, 1),
     ((2048, 1408, 60, 4), 256, ("mgemv",), 0, 4, 1),
     # Mixtral-shaped layer: one token splits the down product's K range over 4 waves; prefill is MFMA,
-    # its down product in two K parts (16 token tiles x 32 row tiles would fill 256 CUs only twice)
+    # its down product in one K part (16 token tiles x 32 row tiles fill 256 CUs twice)
     ((4096, 14336, 8, 2), 1, ("gemv",), 1, 3, 4),
     # 64 tokens: matrix-core GEMV alone, its down product in two K parts (8 tiles x 128 chunks)
     ((4096, 14336, 8, 2), 64, ("mgemv",), 0, 4, 2),
-    ((4096, 14336, 8, 2), 4096, ("mgemv", "mfma"), 0, 6, 2),
+    ((4096, 14336, 8, 2), 4096, ("mgemv", "mfma"), 0, 6, 1),
     ((4096, 14336, 8, 2), 16384, ("mgemv", "mfma"), 0, 6, 1),
 ])
 def test_path_info_auto_rule(lib, shp, T, fams, inline, launches, kparts):
