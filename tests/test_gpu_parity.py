@@ -307,6 +307,35 @@ def test_deterministic_and_relocation_invariant(torch):
     assert torch.equal(y0, y1) and torch.equal(y0, y2)
 
 
+def test_concurrent_calls_on_two_streams(torch):
+    """Two layers, each with its own workspace, enqueued alternately on two
+    streams with nothing ordering one stream against the other: every output
+    equals the serial result bit for bit (calls share no state beyond their
+    arguments).  One layer runs the GEMV family with inline routing, the other
+    the matrix-core GEMV after the route kernel."""
+    from any_precision_bitplane_amd.device import DeviceLayer
+    da = DeviceLayer(layer_for("qwen_decode"))
+    db = DeviceLayer(layer_for("mixtral_decode", T=64))
+    da.forward()
+    db.forward()
+    torch.cuda.synchronize()
+    ya, yb = da.y.clone(), db.y.clone()
+    outs_a = [torch.empty_like(ya) for _ in range(8)]
+    outs_b = [torch.empty_like(yb) for _ in range(8)]
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    sa.wait_stream(torch.cuda.current_stream())
+    sb.wait_stream(torch.cuda.current_stream())
+    say("8 + 8 forwards alternating on two streams")
+    for i in range(8):
+        da.forward(stream=sa, y=outs_a[i])
+        db.forward(stream=sb, y=outs_b[i])
+    torch.cuda.synchronize()
+    assert da.status() == 0 and db.status() == 0
+    for i in range(8):
+        assert torch.equal(outs_a[i], ya), f"stream A call {i}"
+        assert torch.equal(outs_b[i], yb), f"stream B call {i}"
+
+
 def test_commit_is_ordered_on_the_stream(torch):
     """A q write enqueued after a forward does not affect it; the next forward
     sees it (the page table is read on the device)."""
