@@ -18,11 +18,13 @@ namespace {
 // AUTO picks one kernel family per call from the mean number of routed slots
 // per routed expert (measured on the Qwen- and Mixtral-shaped layers: the
 // families run one after another, so a call that mixes them pays each one's
-// fill and drain): GEMV below a mean of 2, the matrix-core GEMV up to 64, MFMA
-// above.  The MFMA/matrix-core crossover lies at a mean of about 60-68 on the
-// Qwen shape and 80-96 on the Mixtral shape.
+// fill and drain): GEMV below a mean of 2, the matrix-core GEMV up to 96, the
+// MFMA form (with its short tails on the matrix-core GEMV) above.  Against the
+// MFMA form the matrix-core GEMV is 10-17% faster on the Qwen shape at means of
+// 77 to 107 and ties at 128; on the Mixtral shape the two tie from 72 to 104
+// except at 96 (MFMA form 4% faster), and the MFMA form is 18% faster at 112.
 constexpr int kGemvBelowMean = 2;
-constexpr int kMgemvUpToMean = 64;
+constexpr int kMgemvUpToMean = 96;
 // With explicit thresholds in the options (either one > 0) AUTO splits the
 // experts into token-count bands instead; these fill the one not given.
 constexpr int kDefaultMgemvMinTokens = 1;

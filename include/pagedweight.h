@@ -100,12 +100,13 @@ typedef struct {
 /* Kernel family for the expert products. */
 #define PW_PATH_AUTO  0  /* one family per call by the mean routed slots per
                             routed expert m = T*top_k / min(E, T*top_k): GEMV for
-                            m < 2, matrix-core GEMV for 2 <= m <= 64, MFMA above,
+                            m < 2, matrix-core GEMV for 2 <= m <= 96, MFMA above,
                             where an expert's tokens past its last whole
                             512-token tile take the matrix-core GEMV when
                             there are at most 96 of them (pw_path_info's
-                            mfma_tail).  If either *_min_tokens option is > 0 and m >= 2, per
-                            expert by its token count n instead: GEMV below
+                            mfma_tail).  If either *_min_tokens option is
+                            > 0 and m >= 2, per expert by its token count n
+                            instead: GEMV below
                             mgemv_min_tokens (default 1), matrix-core GEMV below
                             mfma_min_tokens (default 256), MFMA from there; with
                             m < 2 the GEMV still takes every expert below

@@ -40,18 +40,19 @@ def _check_oracle(y, L, ids=None):
     assert np.all(np.isfinite(y)) and rel <= REL_L2 and mx <= MAX_ABS, (rel, mx)
 
 
-def _both(torch, L, ids=None):
+def _both(torch, L, ids=None, opts=None, dev=None):
     """y from pw_moe_forward (workspace) and from pw_moe_forward_noalloc, and
     the status word the latter raised."""
     from any_precision_bitplane_amd.device import DeviceLayer
-    dev = DeviceLayer(L)
+    dev = dev or DeviceLayer(L)
     if ids is not None:
         dev.ids.copy_(torch.from_numpy(ids))
-    dev.forward()
+    dev.forward(opts)
     y_ws = dev.y.clone()
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     y_na = torch.full_like(dev.y, 7.0)
-    B.pw_moe_forward_noalloc(dev.shape, L.wl.T, dev.x, dev.ids, dev.w, dev.blocks[0], dev.q, y_na, status)
+    B.pw_moe_forward_noalloc(dev.shape, L.wl.T, dev.x, dev.ids, dev.w, dev.blocks[0], dev.q, y_na, status,
+                             opts=opts)
     torch.cuda.synchronize()
     return y_ws.float().cpu().numpy(), y_na.float().cpu().numpy(), int(status.item()), dev
 
@@ -95,8 +96,8 @@ def test_noalloc_rejects_calls_beyond_its_scratch(torch):
 
 def test_noalloc_largest_call_its_scratch_holds(torch):
     # the largest Qwen-shaped call whose workspace fits the static scratch
-    # (found from pw_workspace_bytes, one token more does not fit); AUTO then
-    # runs the prefill form (MFMA tiles, matrix-core GEMV tails)
+    # (found from pw_workspace_bytes, one token more does not fit), on the
+    # family AUTO picks and on the MFMA kernels forced through the options
     shp = B.shape(2048, 1408, 60, 4)
     lim = B.PW_NOALLOC_SCRATCH_BYTES
     lo, hi = 1, 1 << 16
@@ -108,12 +109,19 @@ def test_noalloc_largest_call_its_scratch_holds(torch):
             hi = mid - 1
     T = lo
     assert B.pw_workspace_bytes(shp, T + 1) > lim
-    info = B.pw_moe_path_info(shp, T)
-    assert info.mfma == 1 and info.mgemv == 1 and info.mfma_tail > 0
     wl = synth.WORKLOADS["qwen_decode"].with_T(T)
     L = synth.make_routed_layer(wl)
-    say(f"noalloc forward qwen_decode T={T} (workspace {B.pw_workspace_bytes(shp, T)} of {lim} bytes)")
-    y_ws, y_na, st, _ = _both(torch, L)
-    assert st == 0
-    assert np.array_equal(y_ws, y_na), f"T={T}: {np.count_nonzero(y_ws != y_na)} elements differ"
-    _check_oracle(y_na, L)
+    ref = orc.moe_forward_layer(L)
+    dev = None
+    for path in (B.PW_PATH_AUTO, B.PW_PATH_MFMA):
+        opts = B.make_options(path=path)
+        info = B.pw_moe_path_info(shp, T, opts)
+        say(f"noalloc forward qwen_decode T={T} path={path} mgemv={info.mgemv} mfma={info.mfma} "
+            f"(workspace {B.pw_workspace_bytes(shp, T)} of {lim} bytes)")
+        y_ws, y_na, st, dev = _both(torch, L, opts=opts, dev=dev)
+        assert st == 0
+        assert np.array_equal(y_ws, y_na), f"T={T} path={path}: {np.count_nonzero(y_ws != y_na)} elements differ"
+        err = y_na.astype(np.float64) - ref
+        rel = np.linalg.norm(err) / np.linalg.norm(ref)
+        say(f"  vs oracle: rel_l2={rel:.3e} max_abs={np.max(np.abs(err)):.3e}")
+        assert rel <= REL_L2 and np.max(np.abs(err)) <= MAX_ABS
