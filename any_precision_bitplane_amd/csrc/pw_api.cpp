@@ -18,12 +18,16 @@ namespace {
 // AUTO picks one kernel family per call from the mean number of routed slots
 // per routed expert (measured on the Qwen- and Mixtral-shaped layers: the
 // families run one after another, so a call that mixes them pays each one's
-// fill and drain): GEMV below a mean of 2, the matrix-core GEMV up to 96, the
+// fill and drain): GEMV below a mean of 1.6, the matrix-core GEMV up to 96, the
 // MFMA form (with its short tails on the matrix-core GEMV) above.  Against the
 // MFMA form the matrix-core GEMV is 10-17% faster on the Qwen shape at means of
 // 77 to 107 and ties at 128; on the Mixtral shape the two tie from 72 to 104
 // except at 96 (MFMA form 4% faster), and the MFMA form is 18% faster at 112.
-constexpr int kGemvBelowMean = 2;
+// Against the GEMV the matrix-core GEMV wins from a mean of about 1.6: the
+// GEMV is 5% faster at 1.33 on the Qwen shape and 7% at 1.5 on the Mixtral
+// shape, within 2% at 1.6, and 11% (Qwen, 1.87) and 18% (Mixtral, 1.75) slower
+// above.  The GEMV takes calls with m < kGemvBelowNum / kGemvBelowDen.
+constexpr int kGemvBelowNum = 8, kGemvBelowDen = 5;
 constexpr int kMgemvUpToMean = 96;
 // With explicit thresholds in the options (either one > 0) AUTO splits the
 // experts into token-count bands instead; these fill the one not given.
@@ -79,7 +83,7 @@ pw_status make_plan(const pw_moe_shape* shape, int32_t T, const pw_moe_options* 
     b2 = opts->mfma_min_tokens > 0 ? opts->mfma_min_tokens : kDefaultMfmaMinTokens;
     b1 = opts->mgemv_min_tokens > 0 ? opts->mgemv_min_tokens : kDefaultMgemvMinTokens;
     if (b1 > b2) b1 = b2;
-  } else if ((long long)max_slots < (long long)kGemvBelowMean * routed_bound) {
+  } else if ((long long)kGemvBelowDen * max_slots < (long long)kGemvBelowNum * routed_bound) {
     b1 = b2 = INT_MAX;                        // decode: GEMV alone
   } else if ((long long)max_slots <= (long long)kMgemvUpToMean * routed_bound && mg_ok) {
     b1 = 0; b2 = INT_MAX;                     // moderate batches: matrix-core GEMV alone
@@ -88,9 +92,10 @@ pw_status make_plan(const pw_moe_shape* shape, int32_t T, const pw_moe_options* 
   }
   pl.mfma = b2 <= T;
   if (!pl.mfma) b2 = INT_MAX;
-  // with explicit bands, calls averaging fewer than kGemvBelowMean slots per
+  // with explicit bands, calls averaging fewer than 1.6 slots per
   // routed expert still stay on the GEMV kernels alone
-  const bool mg_worth = !explicit_bands || (long long)max_slots >= (long long)kGemvBelowMean * routed_bound;
+  const bool mg_worth =
+      !explicit_bands || (long long)kGemvBelowDen * max_slots >= (long long)kGemvBelowNum * routed_bound;
   pl.mgemv = b1 < b2 && b1 <= T && mg_ok && (path == PW_PATH_MGEMV || mg_worth);
   if (!pl.mgemv) b1 = b2;
   pl.gemv = b1 > 1;     // a routed expert has at least one token

@@ -99,18 +99,17 @@ typedef struct {
 
 /* Kernel family for the expert products. */
 #define PW_PATH_AUTO  0  /* one family per call by the mean routed slots per
-                            routed expert m = T*top_k / min(E, T*top_k): GEMV for
-                            m < 2, matrix-core GEMV for 2 <= m <= 96, MFMA above,
-                            where an expert's tokens past its last whole
-                            512-token tile take the matrix-core GEMV when
+                            routed expert m = T*top_k / min(E, T*top_k): GEMV
+                            for m < 1.6, matrix-core GEMV for 1.6 <= m <= 96,
+                            MFMA above, where an expert's tokens past its last
+                            whole 512-token tile take the matrix-core GEMV when
                             there are at most 96 of them (pw_path_info's
-                            mfma_tail).  If either *_min_tokens option is
-                            > 0 and m >= 2, per expert by its token count n
-                            instead: GEMV below
-                            mgemv_min_tokens (default 1), matrix-core GEMV below
-                            mfma_min_tokens (default 256), MFMA from there; with
-                            m < 2 the GEMV still takes every expert below
-                            mfma_min_tokens */
+                            mfma_tail).  If either *_min_tokens option is > 0
+                            and m >= 1.6, per expert by its token count n
+                            instead: GEMV below mgemv_min_tokens (default 1),
+                            matrix-core GEMV below mfma_min_tokens (default
+                            256), MFMA from there; with m < 1.6 the GEMV still
+                            takes every expert below mfma_min_tokens */
 #define PW_PATH_GEMV  1  /* every expert on the bit-plane GEMV kernels            */
 #define PW_PATH_MFMA  2  /* every expert on the dequant-to-LDS MFMA kernels       */
 #define PW_PATH_MGEMV 3  /* every expert on the matrix-core GEMV kernels          */

@@ -700,15 +700,15 @@ def test_forward_auto_edge_layers(torch, H, I, E, k, T, seed):
 _FAMILIES = {B.PW_PATH_GEMV: "gemv", B.PW_PATH_MGEMV: "mgemv", B.PW_PATH_MFMA: "mfma"}
 
 
-@pytest.mark.parametrize("T,family,launched", [(7, B.PW_PATH_GEMV, ("gemv",)), (8, B.PW_PATH_MGEMV, ("mgemv",)),
+@pytest.mark.parametrize("T,family,launched", [(6, B.PW_PATH_GEMV, ("gemv",)), (7, B.PW_PATH_MGEMV, ("mgemv",)),
                                                (384, B.PW_PATH_MGEMV, ("mgemv",)),
                                                (385, None, ("mgemv", "mfma"))])
 def test_auto_family_at_the_mean_edges(torch, T, family, launched):
     """AUTO runs one kernel family per call, chosen from the mean routed slots
-    per routed expert m = T*k / min(E, T*k): GEMV for m < 2, matrix-core GEMV
-    for 2 <= m <= 96, MFMA above, where an expert's tokens past its last whole
+    per routed expert m = T*k / min(E, T*k): GEMV for m < 1.6, matrix-core GEMV
+    for 1.6 <= m <= 96, MFMA above, where an expert's tokens past its last whole
     512-token tile take the matrix-core GEMV when there are at most 96 of them.
-    With E = 8, k = 2 the batches T = 7 / 8 / 384 / 385 sit on either side of
+    With E = 8, k = 2 the batches T = 6 / 7 / 384 / 385 sit on either side of
     both edges.  Every family is deterministic and sums in its own order (here
     with the down product's K range in one part on both GEMV forms), so where
     AUTO runs one family its output equals that family's forced output bit for
