@@ -18,17 +18,20 @@ namespace {
 // AUTO picks one kernel family per call from the mean number of routed slots
 // per routed expert (measured on the Qwen- and Mixtral-shaped layers: the
 // families run one after another, so a call that mixes them pays each one's
-// fill and drain): GEMV below a mean of 1.6, the matrix-core GEMV up to 96, the
-// MFMA form (with its short tails on the matrix-core GEMV) above.  Against the
-// MFMA form the matrix-core GEMV is 10-17% faster on the Qwen shape at means of
-// 77 to 107 and ties at 128; on the Mixtral shape the two tie from 72 to 104
-// except at 96 (MFMA form 4% faster), and the MFMA form is 18% faster at 112.
-// Against the GEMV the matrix-core GEMV wins from a mean of about 1.6: the
-// GEMV is 5% faster at 1.33 on the Qwen shape and 7% at 1.5 on the Mixtral
-// shape, within 2% at 1.6, and 11% (Qwen, 1.87) and 18% (Mixtral, 1.75) slower
-// above.  The GEMV takes calls with m < kGemvBelowNum / kGemvBelowDen.
+// fill and drain): GEMV below a mean of 1.6, the matrix-core GEMV up to 64, the
+// MFMA form (with its short tails on the matrix-core GEMV) above.  The upper
+// edge depends on how evenly the tokens spread: with evenly routed tokens the
+// matrix-core GEMV stays 10-17% faster up to a mean of about 100 (Qwen shape;
+// Mixtral ties to 104), but with Zipf-routed tokens the hot experts fill MFMA
+// tiles and the MFMA form wins from about 48 (Qwen shape at 68 / 85 / 96: 0.384
+// / 0.479 / 0.472 ms against 0.479 / 0.563 / 0.619 with the edge at 96).
+// Against the GEMV the matrix-core GEMV wins from a mean of about 1.6 with even
+// routing: the GEMV is 5% faster at 1.33 on the Qwen shape and 7% at 1.5 on
+// the Mixtral shape, within 2% at 1.6, and 11% (Qwen, 1.87) and 18% (Mixtral,
+// 1.75) slower above; with Zipf routing the matrix-core GEMV wins throughout.
+// The GEMV takes calls with m < kGemvBelowNum / kGemvBelowDen.
 constexpr int kGemvBelowNum = 8, kGemvBelowDen = 5;
-constexpr int kMgemvUpToMean = 96;
+constexpr int kMgemvUpToMean = 64;
 // With explicit thresholds in the options (either one > 0) AUTO splits the
 // experts into token-count bands instead; these fill the one not given.
 constexpr int kDefaultMgemvMinTokens = 1;

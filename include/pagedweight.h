@@ -100,7 +100,7 @@ typedef struct {
 /* Kernel family for the expert products. */
 #define PW_PATH_AUTO  0  /* one family per call by the mean routed slots per
                             routed expert m = T*top_k / min(E, T*top_k): GEMV
-                            for m < 1.6, matrix-core GEMV for 1.6 <= m <= 96,
+                            for m < 1.6, matrix-core GEMV for 1.6 <= m <= 64,
                             MFMA above, where an expert's tokens past its last
                             whole 512-token tile take the matrix-core GEMV when
                             there are at most 96 of them (pw_path_info's

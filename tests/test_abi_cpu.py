@@ -174,13 +174,13 @@ def _families(info):
 # fams: the families whose kernels run; ("mgemv", "mfma") on the AUTO rule's
 # prefill side means MFMA with the matrix-core GEMV taking the experts' tails
 @pytest.mark.parametrize("shp,T,fams,inline,launches,kparts", [
-    # E = 8, k = 2: the mean routed slots per routed expert m = T*k / min(E, T*k) crosses 1.6 at T = 7 and 96 at
-    # T = 385
+    # E = 8, k = 2: the mean routed slots per routed expert m = T*k / min(E, T*k) crosses 1.6 at T = 7 and 64 at
+    # T = 257
     ((1024, 1024, 8, 2), 1, ("gemv",), 1, 3, None),
     ((1024, 1024, 8, 2), 6, ("gemv",), 1, 3, None),
     ((1024, 1024, 8, 2), 7, ("mgemv",), 0, 4, 1),
-    ((1024, 1024, 8, 2), 384, ("mgemv",), 0, 4, 1),
-    ((1024, 1024, 8, 2), 385, ("mgemv", "mfma"), 0, 6, 1),
+    ((1024, 1024, 8, 2), 256, ("mgemv",), 0, 4, 1),
+    ((1024, 1024, 8, 2), 257, ("mgemv", "mfma"), 0, 6, 1),
     # Qwen-shaped layer: decode, 16 tokens (64 slots, still routed inline), 17 tokens (a route kernel), batched
     ((2048, 1408, 60, 4), 4, ("gemv",), 1, 3, 1),
     ((2048, 1408, 60, 4), 16, ("gemv",), 1, 3, None),
